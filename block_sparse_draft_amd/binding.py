@@ -1,0 +1,270 @@
+"""ctypes binding of libsplitkv (include/splitkv.h).
+
+Argument marshalling only: every step of the attention path runs in the HIP
+library; this module turns numpy arrays and torch tensors into the pointers,
+sizes and structs the C ABI takes.  PyTorch is used for device memory and the
+current HIP stream, nothing else.  The library must be built
+(``python -m block_sparse_draft_amd.build``); importing this module without it
+raises.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Optional
+
+import numpy as np
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsplitkv.so")
+
+SKV_OK, SKV_EINVAL, SKV_EDTYPE, SKV_ESHAPE, SKV_EHIP, SKV_EWORKSPACE, SKV_EPLAN = 0, -1, -2, -3, -4, -5, -6
+SKV_F32, SKV_BF16 = 0, 1
+SKV_ITEM_FWD, SKV_ITEM_BWD = 0, 1
+SKV_TILE = 64
+_STATUS = {0: "SKV_OK", -1: "SKV_EINVAL", -2: "SKV_EDTYPE", -3: "SKV_ESHAPE", -4: "SKV_EHIP",
+           -5: "SKV_EWORKSPACE", -6: "SKV_EPLAN"}
+
+
+class SkvError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{_STATUS.get(code, code)}: {msg}")
+        self.code = code
+
+
+class skv_problem(C.Structure):
+    _fields_ = [("n_seq", C.c_int32), ("block", C.c_int32), ("hq", C.c_int32), ("hkv", C.c_int32),
+                ("d", C.c_int32), ("chunk", C.c_int32), ("dtype", C.c_int32), ("sm_scale", C.c_float),
+                ("h_q_off", C.c_void_p), ("d_q_off", C.c_void_p), ("h_kv_off", C.c_void_p), ("d_kv_off", C.c_void_p),
+                ("h_anchor", C.c_void_p), ("d_anchor", C.c_void_p),
+                ("q_stride_tok", C.c_int64), ("q_stride_head", C.c_int64),
+                ("kv_stride_tok", C.c_int64), ("kv_stride_head", C.c_int64)]
+
+
+class skv_item(C.Structure):
+    _fields_ = [("seq", C.c_int32), ("kv_head", C.c_int32), ("chunk", C.c_int32), ("range", C.c_int32),
+                ("part_base", C.c_int64), ("lo", C.c_int32), ("hi", C.c_int32)]
+
+
+ITEM_DTYPE = np.dtype([("seq", "<i4"), ("kv_head", "<i4"), ("chunk", "<i4"), ("range", "<i4"),
+                       ("part_base", "<i8"), ("lo", "<i4"), ("hi", "<i4")])
+assert ITEM_DTYPE.itemsize == C.sizeof(skv_item) == 32
+
+
+class skv_plan(C.Structure):
+    _fields_ = [("kind", C.c_int32), ("n_workers", C.c_int32), ("n_items", C.c_int64),
+                ("d_items", C.c_void_p), ("d_worker_off", C.c_void_p)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m block_sparse_draft_amd.build`")
+    # torch ships its own HIP runtime.  Load it first so that libsplitkv binds
+    # to that same runtime (its libamdhip64 dependency resolves to the copy
+    # already in the process); two runtimes in one process do not share
+    # devices, streams or allocations.
+    import torch  # noqa: F401
+    lib = C.CDLL(LIB_PATH)
+    P, VP, I32, I64, F = C.POINTER, C.c_void_p, C.c_int32, C.c_int64, C.c_float
+    sig = {
+        "skv_last_error": (C.c_char_p, []),
+        "skv_check_problem": (C.c_int, [P(skv_problem)]),
+        "skv_partial_layout": (C.c_int, [P(skv_problem), VP, VP]),
+        "skv_item_table": (C.c_int, [P(skv_problem), I32, I32, VP, VP, VP, P(I64), P(I64)]),
+        "lpt_plan": (C.c_int, [VP, I64, I32, VP, VP, VP, VP]),
+        "skv_static_plan": (C.c_int, [VP, I64, I64, I32, VP, VP, VP]),
+        "skv_gather_items": (C.c_int, [VP, VP, I64, VP]),
+        "sparse_attn_partial_fwd": (C.c_int, [P(skv_problem), P(skv_plan), VP, VP, VP, VP, VP, VP, VP]),
+        "lse_merge": (C.c_int, [I32, I32, I64, I32, VP, VP, VP, VP, I64, I64, I32, VP, I64, VP]),
+        "skv_bwd_workspace_bytes": (C.c_size_t, [P(skv_problem)]),
+        "sparse_attn_bwd": (C.c_int, [P(skv_problem), P(skv_plan)] + [VP] * 10 + [C.c_size_t, VP]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype, fn.argtypes = res, args
+    return lib
+
+
+lib = _load()
+EXPORTED = ("skv_last_error", "skv_check_problem", "skv_partial_layout", "skv_item_table", "lpt_plan",
+            "skv_static_plan", "skv_gather_items", "sparse_attn_partial_fwd", "lse_merge",
+            "skv_bwd_workspace_bytes", "sparse_attn_bwd")
+
+
+def last_error() -> str:
+    return lib.skv_last_error().decode()
+
+
+def _check(rc: int):
+    if rc != SKV_OK:
+        raise SkvError(rc, last_error())
+
+
+def _ptr(a) -> Optional[int]:
+    """Address of a numpy array or torch tensor (None stays NULL)."""
+    if a is None:
+        return None
+    if isinstance(a, np.ndarray):
+        if not a.flags.c_contiguous:
+            raise ValueError("numpy arrays passed to libsplitkv must be C-contiguous")
+        return a.ctypes.data
+    return a.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+# ---------------------------------------------------------------------------
+# Host calls
+# ---------------------------------------------------------------------------
+
+def lpt_plan(cost, n_workers: int):
+    """LPT planning (host).  Returns (assign int32, order int64, worker_off int64, load int64)."""
+    cost = np.ascontiguousarray(cost, dtype=np.int64)
+    n = len(cost)
+    assign = np.empty(n, np.int32)
+    order = np.empty(n, np.int64)
+    off = np.empty(n_workers + 1 if n_workers > 0 else 1, np.int64)
+    load = np.empty(max(n_workers, 1), np.int64)
+    _check(lib.lpt_plan(_ptr(cost), n, n_workers, _ptr(assign), _ptr(order), _ptr(off), _ptr(load)))
+    return assign, order, off, load
+
+
+def skv_static_plan(tok_start, total_tok: int, n_workers: int):
+    """Static token-count plan (host).  Returns (assign, order, worker_off)."""
+    t = np.ascontiguousarray(tok_start, dtype=np.int64)
+    n = len(t)
+    assign = np.empty(n, np.int32)
+    order = np.empty(n, np.int64)
+    off = np.empty(n_workers + 1 if n_workers > 0 else 1, np.int64)
+    _check(lib.skv_static_plan(_ptr(t), n, int(total_tok), n_workers, _ptr(assign), _ptr(order), _ptr(off)))
+    return assign, order, off
+
+
+def skv_gather_items(items: np.ndarray, order: np.ndarray) -> np.ndarray:
+    items = np.ascontiguousarray(items, dtype=ITEM_DTYPE)
+    order = np.ascontiguousarray(order, dtype=np.int64)
+    out = np.empty(len(order), ITEM_DTYPE)
+    _check(lib.skv_gather_items(_ptr(items), _ptr(order), len(order), _ptr(out)))
+    return out
+
+
+class Problem:
+    """A skv_problem plus the host and device arrays it points to.
+
+    q_off, kv_off (int64 [n_seq+1]) and anchors (int32, sorted per sequence)
+    are host numpy arrays; their device copies are made with torch when a
+    device is given (``device=None`` gives a host-only problem for planning).
+    """
+
+    def __init__(self, q_off, kv_off, anchors, block: int, hq: int, hkv: int, d: int, chunk: int,
+                 dtype: int, sm_scale: float, q_strides=None, kv_strides=None, device=None):
+        self.h_q_off = np.ascontiguousarray(q_off, dtype=np.int64)
+        self.h_kv_off = np.ascontiguousarray(kv_off, dtype=np.int64)
+        self.h_anchor = np.ascontiguousarray(anchors, dtype=np.int32)
+        self.n_seq = len(self.h_q_off) - 1
+        self.block, self.hq, self.hkv, self.d, self.chunk = block, hq, hkv, d, chunk
+        self.dtype, self.sm_scale = dtype, sm_scale
+        self.q_strides = q_strides or (hq * d, d)
+        self.kv_strides = kv_strides or (hkv * d, d)
+        self.device = device
+        self.d_q_off = self.d_kv_off = self.d_anchor = None
+        if device is not None:
+            import torch
+            self.d_q_off = torch.from_numpy(self.h_q_off).to(device)
+            self.d_kv_off = torch.from_numpy(self.h_kv_off).to(device)
+            self.d_anchor = torch.from_numpy(self.h_anchor).to(device)
+        self.c = skv_problem(self.n_seq, block, hq, hkv, d, chunk, dtype, sm_scale,
+                             _ptr(self.h_q_off), _ptr(self.d_q_off), _ptr(self.h_kv_off), _ptr(self.d_kv_off),
+                             _ptr(self.h_anchor), _ptr(self.d_anchor),
+                             self.q_strides[0], self.q_strides[1], self.kv_strides[0], self.kv_strides[1])
+
+    @property
+    def total_q(self) -> int:
+        return int(self.h_q_off[-1])
+
+    @property
+    def total_kv(self) -> int:
+        return int(self.h_kv_off[-1])
+
+    def check(self):
+        _check(lib.skv_check_problem(C.byref(self.c)))
+
+    def partial_layout(self):
+        base = np.empty(self.n_seq + 1, np.int64)
+        nchunk = np.empty(max(self.n_seq, 1), np.int32)
+        _check(lib.skv_partial_layout(C.byref(self.c), _ptr(base), _ptr(nchunk)))
+        return base, nchunk[:self.n_seq]
+
+    def item_table(self, kind: int, granule: int):
+        """(items structured array, cost int64, tok_start int64, total_tok)."""
+        n = C.c_int64(0)
+        tot = C.c_int64(0)
+        _check(lib.skv_item_table(C.byref(self.c), kind, granule, None, None, None, C.byref(n), C.byref(tot)))
+        items = np.empty(n.value, ITEM_DTYPE)
+        cost = np.empty(n.value, np.int64)
+        tok = np.empty(n.value, np.int64)
+        _check(lib.skv_item_table(C.byref(self.c), kind, granule, _ptr(items), _ptr(cost), _ptr(tok),
+                                  C.byref(n), C.byref(tot)))
+        return items, cost, tok, tot.value
+
+    def bwd_workspace_bytes(self) -> int:
+        return int(lib.skv_bwd_workspace_bytes(C.byref(self.c)))
+
+
+class Plan:
+    """A device plan (items in worker order + worker offsets) and its host record."""
+
+    def __init__(self, problem: Problem, kind: int, granule: int, n_workers: int, policy: str = "lpt"):
+        import torch
+        items, cost, tok, total = problem.item_table(kind, granule)
+        if policy == "lpt":
+            assign, order, off, load = lpt_plan(cost, n_workers)
+        elif policy == "static":
+            assign, order, off = skv_static_plan(tok, total, n_workers)
+            load = np.bincount(assign, weights=cost, minlength=n_workers).astype(np.int64)
+        else:
+            raise ValueError(policy)
+        self.kind, self.granule, self.n_workers, self.policy = kind, granule, n_workers, policy
+        self.items, self.cost, self.assign, self.order, self.worker_off, self.load = items, cost, assign, order, off, load
+        self.h_items = skv_gather_items(items, order)
+        self.d_items = torch.from_numpy(self.h_items.view(np.uint8).copy()).to(problem.device)
+        self.d_worker_off = torch.from_numpy(off).to(problem.device)
+        self.c = skv_plan(kind, n_workers, len(items), self.d_items.data_ptr(), self.d_worker_off.data_ptr())
+
+    @property
+    def imbalance(self) -> float:
+        mean = self.load.mean()
+        return float(self.load.max() / mean - 1.0) if mean > 0 else 0.0
+
+
+# ---------------------------------------------------------------------------
+# Device calls (asynchronous on the given / current stream)
+# ---------------------------------------------------------------------------
+
+def sparse_attn_partial_fwd(problem: Problem, plan: Plan, q, k, v, o_part, m_part, lse_part, stream=None):
+    _check(lib.sparse_attn_partial_fwd(C.byref(problem.c), C.byref(plan.c), _ptr(q), _ptr(k), _ptr(v),
+                                       _ptr(o_part), _ptr(m_part), _ptr(lse_part), _stream(stream)))
+
+
+def lse_merge(n_part: int, hq: int, mq: int, d: int, o_part, m_part, lse_part, o_out, o_stride_tok: int,
+              o_stride_head: int, out_dtype: int, lse_out, lse_stride_tok: int, stream=None,
+              part_offset: int = 0, out_offset: int = 0, lse_offset: int = 0):
+    """Merge n_part partials of one sequence.  ``*_offset`` are element offsets
+    added to the given tensors' base addresses (partial rows start at
+    ``part_offset`` rows; the output at token ``out_offset``)."""
+    ob = o_out.element_size()
+    _check(lib.lse_merge(n_part, hq, mq, d,
+                         _ptr(o_part) + part_offset * d * 4, _ptr(m_part) + part_offset * 4,
+                         _ptr(lse_part) + part_offset * 4,
+                         _ptr(o_out) + out_offset * o_stride_tok * ob, o_stride_tok, o_stride_head, out_dtype,
+                         _ptr(lse_out) + lse_offset * 4, lse_stride_tok, _stream(stream)))
+
+
+def sparse_attn_bwd(problem: Problem, plan: Plan, q, k, v, o, lse, dout, dq, dk, dv, workspace, stream=None):
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(lib.sparse_attn_bwd(C.byref(problem.c), C.byref(plan.c), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                               _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), nbytes, _stream(stream)))

@@ -1,0 +1,121 @@
+// Device entry points of libsplitkv: argument checks (host copies only, before
+// any HIP call), then kernel launches on the caller's stream.
+#include <cmath>
+
+#include "internal.h"
+#include "launch.h"
+
+using namespace skv;
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_plan(const skv_plan* plan, int32_t kind) {
+  if (!plan) return fail(SKV_EINVAL, "plan is NULL");
+  if (plan->kind != kind) return fail(SKV_EPLAN, "plan kind %d does not match this call (%d)", plan->kind, kind);
+  if (plan->n_workers < 1) return fail(SKV_EPLAN, "plan has %d workers", plan->n_workers);
+  if (plan->n_items < 0) return fail(SKV_EPLAN, "plan has a negative item count");
+  if (!plan->d_worker_off || (plan->n_items > 0 && !plan->d_items)) return fail(SKV_EPLAN, "plan arrays are NULL");
+  return SKV_OK;
+}
+
+int check_device_problem(const skv_problem* p) {
+  if (!p->d_q_off || !p->d_kv_off || !p->d_anchor) return fail(SKV_EINVAL, "device offset/anchor arrays are NULL");
+  return SKV_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(SKV_EHIP, "%s: %s", what, hipGetErrorString(e));
+  clear_error();
+  return SKV_OK;
+}
+
+}  // namespace
+
+extern "C" int sparse_attn_partial_fwd(const skv_problem* p, const skv_plan* plan, const void* q, const void* k,
+                                       const void* v, float* o_part, float* m_part, float* lse_part, void* stream) {
+  int rc = skv_check_problem(p);
+  if (rc) return rc;
+  if ((rc = check_device_problem(p))) return rc;
+  if ((rc = check_plan(plan, SKV_ITEM_FWD))) return rc;
+  if (!q || !k || !v || !o_part || !m_part || !lse_part) return fail(SKV_EINVAL, "tensor pointer is NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o_part))
+    return fail(SKV_ESHAPE, "q, k, v and o_part must be 16-byte aligned");
+  FwdArgs a{};
+  a.q = q; a.k = k; a.v = v;
+  a.q_st = p->q_stride_tok; a.q_sh = p->q_stride_head;
+  a.kv_st = p->kv_stride_tok; a.kv_sh = p->kv_stride_head;
+  a.q_off = p->d_q_off; a.kv_off = p->d_kv_off; a.anchor = p->d_anchor;
+  a.items = plan->d_items; a.worker_off = plan->d_worker_off;
+  a.o_part = o_part; a.m_part = m_part; a.lse_part = lse_part;
+  a.block = p->block; a.group = p->hq / p->hkv; a.hq = p->hq; a.chunk = p->chunk;
+  a.scale_log2 = p->sm_scale * kLog2e_host;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = p->dtype == SKV_BF16 ? launch_fwd_bf16(a, plan->n_workers, st)
+                                      : launch_fwd_f32(a, p->d, plan->n_workers, st);
+  return hip_status(e, "sparse_attn_partial_fwd launch");
+}
+
+extern "C" int lse_merge(int32_t n_part, int32_t hq, int64_t mq, int32_t d, const float* o_part, const float* m_part,
+                         const float* lse_part, void* o_out, int64_t o_stride_tok, int64_t o_stride_head,
+                         int32_t out_dtype, float* lse_out, int64_t lse_stride_tok, void* stream) {
+  if (n_part < 0 || hq < 1 || mq < 0) return fail(SKV_EINVAL, "bad counts n_part=%d hq=%d mq=%lld", n_part, hq,
+                                                  (long long)mq);
+  if (d != 64 && d != 128) return fail(SKV_ESHAPE, "lse_merge supports head_dim 64 or 128, got %d", d);
+  if (out_dtype != SKV_F32 && out_dtype != SKV_BF16) return fail(SKV_EDTYPE, "unknown out_dtype %d", out_dtype);
+  if (mq == 0) { clear_error(); return SKV_OK; }
+  if (!o_out || !lse_out || (n_part > 0 && (!o_part || !m_part || !lse_part)))
+    return fail(SKV_EINVAL, "tensor pointer is NULL");
+  const int64_t vec = out_dtype == SKV_BF16 ? 4 : 4;  // 4 elements per lane store
+  if (o_stride_tok < 1 || o_stride_head < d || lse_stride_tok < hq) return fail(SKV_ESHAPE, "bad output strides");
+  if (o_stride_tok % vec || o_stride_head % vec) return fail(SKV_ESHAPE, "output strides must be multiples of 4");
+  if (!aligned16(o_part) || (reinterpret_cast<uintptr_t>(o_out) & 7u))
+    return fail(SKV_ESHAPE, "o_part must be 16-byte and o_out 8-byte aligned");
+  if (mq > (int64_t)INT32_MAX * 32) return fail(SKV_ESHAPE, "mq too large");
+  MergeArgs a{};
+  a.o_part = o_part; a.m_part = m_part; a.lse_part = lse_part;
+  a.o_out = o_out; a.lse_out = lse_out;
+  a.mq = mq; a.o_st = o_stride_tok; a.o_sh = o_stride_head; a.lse_st = lse_stride_tok;
+  a.n_part = n_part; a.hq = hq; a.out_bf16 = out_dtype == SKV_BF16;
+  return hip_status(launch_merge(a, d, static_cast<hipStream_t>(stream)), "lse_merge launch");
+}
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+extern "C" size_t skv_bwd_workspace_bytes(const skv_problem* p) {
+  if (skv_check_problem(p)) return 0;
+  const size_t rows = (size_t)p->h_q_off[p->n_seq] * (size_t)p->hq;
+  return align256(rows * (size_t)p->d * sizeof(float)) + align256(rows * sizeof(float));
+}
+
+extern "C" int sparse_attn_bwd(const skv_problem* p, const skv_plan* plan, const void* q, const void* k, const void* v,
+                               const void* o, const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = skv_check_problem(p);
+  if (rc) return rc;
+  if (p->dtype != SKV_BF16) return fail(SKV_EDTYPE, "sparse_attn_bwd supports bf16 only");
+  if ((rc = check_device_problem(p))) return rc;
+  if ((rc = check_plan(plan, SKV_ITEM_BWD))) return rc;
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return fail(SKV_EINVAL, "tensor pointer is NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) || !aligned16(dq))
+    return fail(SKV_ESHAPE, "q, k, v, o, dout and dq must be 16-byte aligned");
+  const size_t need = skv_bwd_workspace_bytes(p);
+  if (!workspace || workspace_bytes < need)
+    return fail(SKV_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
+  if (reinterpret_cast<uintptr_t>(workspace) & 255u) return fail(SKV_EWORKSPACE, "workspace must be 256-byte aligned");
+  const int64_t total_q = p->h_q_off[p->n_seq];
+  const size_t rows = (size_t)total_q * (size_t)p->hq;
+  BwdArgs a{};
+  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.dout = dout; a.dq = dq; a.dk = dk; a.dv = dv;
+  a.dq_acc = static_cast<float*>(workspace);
+  a.delta = reinterpret_cast<float*>(static_cast<char*>(workspace) + align256(rows * (size_t)p->d * sizeof(float)));
+  a.q_st = p->q_stride_tok; a.q_sh = p->q_stride_head;
+  a.kv_st = p->kv_stride_tok; a.kv_sh = p->kv_stride_head;
+  a.q_off = p->d_q_off; a.kv_off = p->d_kv_off; a.anchor = p->d_anchor;
+  a.items = plan->d_items; a.worker_off = plan->d_worker_off;
+  a.total_q = total_q;
+  a.block = p->block; a.group = p->hq / p->hkv; a.hq = p->hq; a.hkv = p->hkv;
+  a.sm_scale = p->sm_scale; a.scale_log2 = p->sm_scale * kLog2e_host;
+  return hip_status(launch_bwd_bf16(a, plan->n_workers, static_cast<hipStream_t>(stream)), "sparse_attn_bwd launch");
+}

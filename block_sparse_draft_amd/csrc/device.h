@@ -1,0 +1,82 @@
+// Device-side building blocks for the gfx950 (CDNA4) kernels of libsplitkv:
+// vector types, bf16 conversion, the bf16 MFMA and the LDS transpose read.
+//
+// Operand layouts of v_mfma_f32_32x32x16_bf16 on a 64-lane wave (lane l,
+// h = l / 32):  A (32 x 16, M x K): row l % 32, k = 8h .. 8h+7;
+// B (16 x 32, K x N): column l % 32, k = 8h .. 8h+7;
+// C/D (32 x 32): column l % 32, element 4i + j holds row 8i + 4h + j.
+//
+// ds_read_b64_tr_b16 (gfx950): within each group of 16 lanes, lane i receives,
+// for j = 0..3, the 16-bit element i % 4 of the 8-byte chunk addressed by lane
+// 4j + i / 4.  If lane 4j + q of the group addresses row r0 + j, column
+// c0 + 4q of a row-major bf16 tile, lane i receives column c0 + i of rows
+// r0 .. r0+3: a 4 x 16 tile read transposed.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace skv {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// 2^x on the transcendental unit (v_exp_f32); exact 0 for -inf.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t* p) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p));
+}
+
+__device__ __forceinline__ bf16x8 lds_load_bf16x8(const uint16_t* p) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p));
+}
+
+// Two transposed 4 x 16 reads (see the header comment) joined into one MFMA operand.
+__device__ __forceinline__ bf16x8 lds_tr_pair(const uint16_t* p0, const uint16_t* p1) {
+  i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p0));
+  i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p1));
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  i16x8 c = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  return __builtin_bit_cast(bf16x8, c);
+}
+
+// Round-to-nearest-even fp32 -> bf16 of 8 consecutive values.
+__device__ __forceinline__ bf16x8 to_bf16x8(float a0, float a1, float a2, float a3, float a4, float a5, float a6,
+                                            float a7) {
+  bf16x8 r;
+  r[0] = (__bf16)a0; r[1] = (__bf16)a1; r[2] = (__bf16)a2; r[3] = (__bf16)a3;
+  r[4] = (__bf16)a4; r[5] = (__bf16)a5; r[6] = (__bf16)a6; r[7] = (__bf16)a7;
+  return r;
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
+  return __builtin_bit_cast(uint16_t, (__bf16)x);
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+__device__ __forceinline__ int wave_max_i(int x) {
+  for (int o = 32; o > 0; o >>= 1) x = max(x, __shfl_xor(x, o));
+  return x;
+}
+__device__ __forceinline__ int wave_min_i(int x) {
+  for (int o = 32; o > 0; o >>= 1) x = min(x, __shfl_xor(x, o));
+  return x;
+}
+
+}  // namespace skv

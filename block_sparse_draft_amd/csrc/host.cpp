@@ -1,0 +1,231 @@
+// Host side of libsplitkv: argument validation, the error channel, the
+// partial layout, the realized-cost work-item table, and the LPT and static
+// planners.  Nothing here touches a GPU.
+//
+// Planning follows the LPT description on the Split-KV article page
+// ("LPT Scheduling": sort by processing time, longest first, each task to the
+// least-loaded machine) with the processing time replaced by the realized
+// attention cost of each item, which the global query view makes observable
+// ("Split-KV's Core Mechanism"; arXiv:2611.05926, Abstract).
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <queue>
+#include <string>
+#include <vector>
+
+#include "internal.h"
+
+namespace skv {
+
+static thread_local std::string g_last_error = "no error";
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+void clear_error() { g_last_error = "no error"; }
+
+const char* last_error_cstr() { return g_last_error.c_str(); }
+
+}  // namespace skv
+
+using namespace skv;
+
+extern "C" const char* skv_last_error(void) { return last_error_cstr(); }
+
+extern "C" int skv_check_problem(const skv_problem* p) {
+  if (!p) return fail(SKV_EINVAL, "problem is NULL");
+  if (p->n_seq < 0) return fail(SKV_EINVAL, "n_seq = %d < 0", p->n_seq);
+  if (p->block < 1) return fail(SKV_EINVAL, "block = %d < 1", p->block);
+  if (p->hq < 1 || p->hkv < 1) return fail(SKV_ESHAPE, "hq = %d, hkv = %d must be >= 1", p->hq, p->hkv);
+  if (p->hq % p->hkv) return fail(SKV_ESHAPE, "hq = %d is not a multiple of hkv = %d", p->hq, p->hkv);
+  if (p->dtype != SKV_F32 && p->dtype != SKV_BF16) return fail(SKV_EDTYPE, "unknown dtype %d", p->dtype);
+  if (p->dtype == SKV_BF16 && p->d != 128) return fail(SKV_ESHAPE, "bf16 supports head_dim 128, got %d", p->d);
+  if (p->dtype == SKV_F32 && p->d != 64 && p->d != 128)
+    return fail(SKV_ESHAPE, "f32 supports head_dim 64 or 128, got %d", p->d);
+  if (p->chunk < SKV_TILE || p->chunk % SKV_TILE)
+    return fail(SKV_ESHAPE, "chunk = %d must be a positive multiple of %d", p->chunk, SKV_TILE);
+  if (!(std::isfinite(p->sm_scale) && p->sm_scale > 0.f))
+    return fail(SKV_EINVAL, "sm_scale must be finite and > 0");
+  if (!p->h_q_off || !p->h_kv_off || !p->h_anchor) return fail(SKV_EINVAL, "host offset/anchor arrays are NULL");
+  // Vector loads move 16 bytes: strides must keep every head row 16-byte aligned.
+  const int64_t vec = p->dtype == SKV_BF16 ? 8 : 4;
+  if (p->q_stride_head < p->d || p->kv_stride_head < p->d || p->q_stride_tok < 1 || p->kv_stride_tok < 1)
+    return fail(SKV_ESHAPE, "strides must be positive and head strides >= d");
+  if (p->q_stride_tok % vec || p->q_stride_head % vec || p->kv_stride_tok % vec || p->kv_stride_head % vec)
+    return fail(SKV_ESHAPE, "strides must be multiples of %lld elements (16 bytes)", (long long)vec);
+  if (p->h_q_off[0] < 0 || p->h_kv_off[0] < 0) return fail(SKV_EINVAL, "offsets must be >= 0");
+  for (int s = 0; s < p->n_seq; ++s) {
+    const int64_t q0 = p->h_q_off[s], q1 = p->h_q_off[s + 1];
+    const int64_t k0 = p->h_kv_off[s], k1 = p->h_kv_off[s + 1];
+    if (q1 < q0 || k1 < k0) return fail(SKV_EINVAL, "offsets of sequence %d decrease", s);
+    if (q0 % p->block || q1 % p->block)
+      return fail(SKV_EINVAL, "query offsets of sequence %d are not multiples of block %d", s, p->block);
+    if (k1 - k0 > (int64_t)INT32_MAX - p->block) return fail(SKV_ESHAPE, "sequence %d is too long", s);
+    const SeqView v = seq_view(p, s);
+    for (int64_t b = 0; b < v.n_blk; ++b) {
+      const int32_t a = p->h_anchor[v.blk0 + b];
+      if (a < 0) return fail(SKV_EINVAL, "anchor %lld of sequence %d is negative", (long long)b, s);
+      if (b > 0 && a < p->h_anchor[v.blk0 + b - 1])
+        return fail(SKV_EINVAL, "anchors of sequence %d are not sorted ascending", s);
+    }
+  }
+  return SKV_OK;
+}
+
+extern "C" int skv_partial_layout(const skv_problem* p, int64_t* part_base, int32_t* n_chunk) {
+  int rc = skv_check_problem(p);
+  if (rc) return rc;
+  int64_t base = 0;
+  for (int s = 0; s < p->n_seq; ++s) {
+    const SeqView v = seq_view(p, s);
+    const int64_t c = ceil_div(v.n, p->chunk);
+    if (part_base) part_base[s] = base;
+    if (n_chunk) n_chunk[s] = (int32_t)c;
+    base += c * p->hq * v.mq;
+  }
+  if (part_base) part_base[p->n_seq] = base;
+  return SKV_OK;
+}
+
+// Number of 64-key tiles t in [t0, t1) with t*64 < e: the tiles of that span in
+// which a block with prefix end e sees at least one key.
+static inline int64_t tiles_seen(int64_t e, int64_t t0, int64_t t1) {
+  const int64_t last = ceil_div(e, SKV_TILE);  // tiles 0 .. last-1 start below e
+  return std::max<int64_t>(0, std::min(last, t1) - t0);
+}
+
+extern "C" int skv_item_table(const skv_problem* p, int32_t kind, int32_t granule, skv_item* items, int64_t* cost,
+                              int64_t* tok_start, int64_t* n_items, int64_t* total_tok) {
+  int rc = skv_check_problem(p);
+  if (rc) return rc;
+  if (kind != SKV_ITEM_FWD && kind != SKV_ITEM_BWD) return fail(SKV_EINVAL, "unknown item kind %d", kind);
+  if (granule < 1) return fail(SKV_EINVAL, "granule = %d < 1", granule);
+  if (kind == SKV_ITEM_BWD && granule % SKV_TILE)
+    return fail(SKV_EINVAL, "bwd granule = %d is not a multiple of %d", granule, SKV_TILE);
+  const int64_t G = p->hq / p->hkv;
+  int64_t n = 0, tok = 0, base = 0;
+  std::vector<int64_t> ends;
+  for (int s = 0; s < p->n_seq; ++s) {
+    const SeqView v = seq_view(p, s);
+    const int64_t C = ceil_div(v.n, p->chunk);
+    ends.resize(v.n_blk);
+    for (int64_t b = 0; b < v.n_blk; ++b) ends[b] = std::min<int64_t>((int64_t)p->h_anchor[v.blk0 + b] + p->block, v.n);
+    for (int g = 0; g < p->hkv; ++g) {
+      for (int64_t c = 0; c < C; ++c) {
+        const int64_t lo = c * p->chunk, hi = std::min<int64_t>(lo + p->chunk, v.n);
+        if (kind == SKV_ITEM_FWD) {
+          const int64_t t0 = lo / SKV_TILE, t1 = ceil_div(hi, SKV_TILE);
+          const int64_t nr = ceil_div(v.n_blk, granule);
+          for (int64_t r = 0; r < nr; ++r) {
+            const int64_t b0 = r * granule, b1 = std::min<int64_t>(b0 + granule, v.n_blk);
+            if (cost) {
+              int64_t sum = 0;
+              for (int64_t b = b0; b < b1; ++b) sum += tiles_seen(ends[b], t0, t1);
+              cost[n] = G * sum;
+            }
+            if (tok_start) tok_start[n] = tok;
+            if (items) items[n] = skv_item{s, g, (int32_t)c, (int32_t)r, base + c * p->hq * v.mq, (int32_t)b0, (int32_t)b1};
+            ++n;
+          }
+        } else {
+          const int64_t nr = ceil_div(hi - lo, granule);
+          for (int64_t r = 0; r < nr; ++r) {
+            const int64_t klo = lo + r * granule, khi = std::min<int64_t>(klo + granule, hi);
+            if (cost) {
+              const int64_t t0 = klo / SKV_TILE, t1 = ceil_div(khi, SKV_TILE);
+              int64_t sum = 0;
+              for (int64_t b = 0; b < v.n_blk; ++b) sum += tiles_seen(ends[b], t0, t1);
+              cost[n] = G * sum;
+            }
+            if (tok_start) tok_start[n] = tok + (klo - lo);
+            if (items) items[n] = skv_item{s, g, (int32_t)c, (int32_t)r, 0, (int32_t)klo, (int32_t)khi};
+            ++n;
+          }
+        }
+        tok += hi - lo;
+      }
+    }
+    base += C * p->hq * v.mq;
+  }
+  if (n_items) *n_items = n;
+  if (total_tok) *total_tok = tok;
+  return SKV_OK;
+}
+
+static int write_csr(const std::vector<std::vector<int64_t>>& lists, int64_t* order, int64_t* worker_off) {
+  int64_t pos = 0;
+  if (worker_off) worker_off[0] = 0;
+  for (size_t w = 0; w < lists.size(); ++w) {
+    for (int64_t i : lists[w]) {
+      if (order) order[pos] = i;
+      ++pos;
+    }
+    if (worker_off) worker_off[w + 1] = pos;
+  }
+  return SKV_OK;
+}
+
+extern "C" int lpt_plan(const int64_t* cost, int64_t n, int32_t n_workers, int32_t* assign, int64_t* order,
+                        int64_t* worker_off, int64_t* load) {
+  if (n < 0) return fail(SKV_EINVAL, "n = %lld < 0", (long long)n);
+  if (n_workers < 1) return fail(SKV_EINVAL, "n_workers = %d < 1", n_workers);
+  if (n > 0 && !cost) return fail(SKV_EINVAL, "cost is NULL");
+  for (int64_t i = 0; i < n; ++i)
+    if (cost[i] < 0) return fail(SKV_EINVAL, "cost[%lld] < 0", (long long)i);
+  // Longest first; equal costs keep ascending item id.
+  std::vector<int64_t> seq(n);
+  for (int64_t i = 0; i < n; ++i) seq[i] = i;
+  std::stable_sort(seq.begin(), seq.end(), [&](int64_t a, int64_t b) { return cost[a] > cost[b]; });
+  // Min-heap of (load, worker): the top is the least-loaded worker, lowest id on ties.
+  using Slot = std::pair<int64_t, int32_t>;
+  std::priority_queue<Slot, std::vector<Slot>, std::greater<Slot>> heap;
+  for (int32_t w = 0; w < n_workers; ++w) heap.push({0, w});
+  std::vector<std::vector<int64_t>> lists(n_workers);
+  std::vector<int64_t> ld(n_workers, 0);
+  for (int64_t i : seq) {
+    Slot top = heap.top();
+    heap.pop();
+    const int32_t w = top.second;
+    if (assign) assign[i] = w;
+    lists[w].push_back(i);
+    ld[w] = top.first + cost[i];
+    heap.push({ld[w], w});
+  }
+  if (load) std::copy(ld.begin(), ld.end(), load);
+  return write_csr(lists, order, worker_off);
+}
+
+extern "C" int skv_static_plan(const int64_t* tok_start, int64_t n, int64_t total_tok, int32_t n_workers,
+                               int32_t* assign, int64_t* order, int64_t* worker_off) {
+  if (n < 0) return fail(SKV_EINVAL, "n = %lld < 0", (long long)n);
+  if (n_workers < 1) return fail(SKV_EINVAL, "n_workers = %d < 1", n_workers);
+  if (n > 0 && !tok_start) return fail(SKV_EINVAL, "tok_start is NULL");
+  std::vector<std::vector<int64_t>> lists(n_workers);
+  for (int64_t i = 0; i < n; ++i) {
+    if (tok_start[i] < 0 || (total_tok > 0 && tok_start[i] >= total_tok))
+      return fail(SKV_EINVAL, "tok_start[%lld] outside [0, total_tok)", (long long)i);
+    // 128-bit product: tok_start * n_workers may exceed 2^63 for huge streams.
+    const int32_t w = total_tok > 0 ? (int32_t)((__int128)tok_start[i] * n_workers / total_tok) : 0;
+    if (assign) assign[i] = w;
+    lists[w].push_back(i);
+  }
+  return write_csr(lists, order, worker_off);
+}
+
+extern "C" int skv_gather_items(const skv_item* items, const int64_t* order, int64_t n, skv_item* items_out) {
+  if (n < 0) return fail(SKV_EINVAL, "n < 0");
+  if (n > 0 && (!items || !order || !items_out)) return fail(SKV_EINVAL, "NULL argument");
+  for (int64_t i = 0; i < n; ++i) {
+    if (order[i] < 0 || order[i] >= n) return fail(SKV_EINVAL, "order[%lld] out of range", (long long)i);
+    items_out[i] = items[order[i]];
+  }
+  return SKV_OK;
+}

@@ -1,0 +1,66 @@
+// Kernel argument blocks and launchers of libsplitkv (host <-> device glue).
+// Launchers enqueue on `stream` and return hipGetLastError().
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "splitkv.h"
+
+namespace skv {
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  int64_t q_st, q_sh, kv_st, kv_sh;  // element strides
+  const int64_t* q_off;
+  const int64_t* kv_off;
+  const int32_t* anchor;
+  const skv_item* items;
+  const int64_t* worker_off;
+  float* o_part;
+  float* m_part;
+  float* lse_part;
+  int32_t block, group, hq, chunk;
+  float scale_log2;  // sm_scale * log2(e)
+};
+
+struct MergeArgs {
+  const float* o_part;
+  const float* m_part;
+  const float* lse_part;
+  void* o_out;
+  float* lse_out;
+  int64_t mq, o_st, o_sh, lse_st;
+  int32_t n_part, hq, out_bf16;
+};
+
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const float* lse;
+  const void* dout;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dq_acc;  // [sum Mq][hq][d] fp32
+  float* delta;   // [sum Mq][hq] fp32
+  int64_t q_st, q_sh, kv_st, kv_sh;
+  const int64_t* q_off;
+  const int64_t* kv_off;
+  const int32_t* anchor;
+  const skv_item* items;
+  const int64_t* worker_off;
+  int64_t total_q;  // sum Mq
+  int32_t block, group, hq, hkv;
+  float sm_scale, scale_log2;
+};
+
+hipError_t launch_fwd_bf16(const FwdArgs& a, int n_workers, hipStream_t stream);
+hipError_t launch_fwd_f32(const FwdArgs& a, int d, int n_workers, hipStream_t stream);
+hipError_t launch_merge(const MergeArgs& a, int d, hipStream_t stream);
+hipError_t launch_bwd_bf16(const BwdArgs& a, int n_workers, hipStream_t stream);
+
+}  // namespace skv

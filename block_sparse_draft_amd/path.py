@@ -1,0 +1,109 @@
+"""The Split-KV hot path on one GPU: plan, partial forward, merge, backward.
+
+A thin driver over the C ABI (binding.py).  It owns the device buffers (torch
+allocations) and the two plans; every arithmetic step runs in libsplitkv's
+kernels.  On one GPU the pages' context-parallel shards become KV chunks and
+the ranks become persistent workgroups (Split-KV article, "Split-KV's Core
+Mechanism" and "LPT Scheduling").
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import numpy as np
+
+from . import binding as B
+
+
+def default_workers(device) -> int:
+    import torch
+    return torch.cuda.get_device_properties(device).multi_processor_count
+
+
+class SplitKVAttention:
+    """Block-sparse draft attention of a packed batch, Split-KV style.
+
+    Host metadata: q_off, kv_off (int64 [n_seq+1]) and anchors (int32, sorted
+    per sequence).  Device tensors q [sum Mq, hq, d], k, v [sum N, hkv, d] in
+    ``dtype`` (torch.bfloat16 or torch.float32).
+    """
+
+    def __init__(self, q_off, kv_off, anchors, block: int, hq: int, hkv: int, d: int, chunk: int,
+                 sm_scale: float, dtype, device, n_workers: Optional[int] = None,
+                 fwd_granule: Optional[int] = None, bwd_granule: int = 256, policy: str = "lpt",
+                 with_bwd: bool = True):
+        import torch
+        self.device = torch.device(device)
+        self.dtype = dtype
+        self.skv_dtype = B.SKV_BF16 if dtype == torch.bfloat16 else B.SKV_F32
+        self.problem = B.Problem(q_off, kv_off, anchors, block, hq, hkv, d, chunk, self.skv_dtype, sm_scale,
+                                 device=self.device)
+        self.problem.check()
+        self.n_workers = n_workers or default_workers(self.device)
+        G = hq // hkv
+        self.fwd_granule = fwd_granule or max(1, 256 // (G * block))
+        self.bwd_granule = bwd_granule
+        self.fwd_plan = B.Plan(self.problem, B.SKV_ITEM_FWD, self.fwd_granule, self.n_workers, policy)
+        self.bwd_plan = (B.Plan(self.problem, B.SKV_ITEM_BWD, self.bwd_granule, self.n_workers, policy)
+                         if with_bwd else None)
+        self.part_base, self.n_chunk = self.problem.partial_layout()
+        rows = int(self.part_base[-1])
+        tq = self.problem.total_q
+        self.o_part = torch.empty((max(rows, 1), d), dtype=torch.float32, device=self.device)
+        self.m_part = torch.empty(max(rows, 1), dtype=torch.float32, device=self.device)
+        self.lse_part = torch.empty(max(rows, 1), dtype=torch.float32, device=self.device)
+        self.o = torch.empty((tq, hq, d), dtype=dtype, device=self.device)
+        self.lse = torch.empty((tq, hq), dtype=torch.float32, device=self.device)
+        self.workspace = None
+        if with_bwd:
+            nbytes = self.problem.bwd_workspace_bytes()
+            self.workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=self.device)
+
+    # -- steps -------------------------------------------------------------
+    def partial_fwd(self, q, k, v, stream=None):
+        B.sparse_attn_partial_fwd(self.problem, self.fwd_plan, q, k, v, self.o_part, self.m_part, self.lse_part,
+                                  stream)
+
+    def merge(self, stream=None):
+        p = self.problem
+        out_dtype = self.skv_dtype
+        for s in range(p.n_seq):
+            q0 = int(p.h_q_off[s])
+            mq = int(p.h_q_off[s + 1]) - q0
+            B.lse_merge(int(self.n_chunk[s]), p.hq, mq, p.d, self.o_part, self.m_part, self.lse_part, self.o,
+                        p.hq * p.d, p.d, out_dtype, self.lse, p.hq, stream,
+                        part_offset=int(self.part_base[s]), out_offset=q0, lse_offset=q0 * p.hq)
+
+    def forward(self, q, k, v, stream=None):
+        """Partials of every KV chunk, then their exact merge.  Returns (O, LSE)."""
+        self.partial_fwd(q, k, v, stream)
+        self.merge(stream)
+        return self.o, self.lse
+
+    def backward(self, q, k, v, dout, dq, dk, dv, stream=None):
+        """dQ, dK, dV from the merged O and LSE of the last forward."""
+        B.sparse_attn_bwd(self.problem, self.bwd_plan, q, k, v, self.o, self.lse, dout, dq, dk, dv, self.workspace,
+                          stream)
+        return dq, dk, dv
+
+    # -- views ---------------------------------------------------------------
+    def partial_view(self, s: int):
+        """(o_part [C, hq, Mq, d], m_part [C, hq, Mq], lse_part [C, hq, Mq]) of sequence s."""
+        p = self.problem
+        mq = int(p.h_q_off[s + 1] - p.h_q_off[s])
+        c = int(self.n_chunk[s])
+        b = int(self.part_base[s])
+        n = c * p.hq * mq
+        return (self.o_part[b:b + n].view(c, p.hq, mq, p.d), self.m_part[b:b + n].view(c, p.hq, mq),
+                self.lse_part[b:b + n].view(c, p.hq, mq))
+
+
+def unmasked_pairs(q_off, kv_off, anchors, block: int, hq: int) -> int:
+    """Token-exact number of visible (query head, query row, key) triples."""
+    total = 0
+    for s in range(len(q_off) - 1):
+        n = int(kv_off[s + 1] - kv_off[s])
+        b0, b1 = int(q_off[s]) // block, int(q_off[s + 1]) // block
+        e = np.minimum(np.asarray(anchors[b0:b1], dtype=np.int64) + block, n)
+        total += int(e.sum()) * block
+    return total * hq

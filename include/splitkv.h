@@ -1,0 +1,203 @@
+/*
+ * splitkv.h — C ABI of libsplitkv: Split-KV block-sparse draft attention on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * What it computes (pages: "Split-KV: Breaking the Context Parallelism
+ * Bottleneck in Diffusion Drafter Training", lede and "Split-KV's Core
+ * Mechanism"; arXiv:2611.05926, Abstract):  a short set of draft queries,
+ * built by anchor sampling, attends with a block-sparse mask over a much longer
+ * context.  The context K/V stays resident in chunks; every chunk yields a
+ * query-sized partial result and the partials are merged exactly, so the
+ * result equals unsharded attention.  The backward reuses the merged
+ * log-sum-exp.  Work items are placed on persistent workgroups by a
+ * cost-aware longest-processing-time-first (LPT) planner ("LPT Scheduling").
+ *
+ * Mask reading: draft block b of a sequence is anchored at context position
+ * a_b and its `block` query rows see the context prefix [0, e_b) with
+ * e_b = min(a_b + block, N_s).  Anchors are sorted ascending per sequence.
+ *
+ * Conventions shared by every call:
+ *  - All device pointers are caller-owned; the library never allocates,
+ *    frees or synchronizes.  Device calls are asynchronous on `stream`
+ *    (a hipStream_t; NULL = the default stream).  Host calls (planning,
+ *    sizing) are synchronous, pure, and touch no GPU.
+ *  - Return value: SKV_OK or a negative skv_status; the reason is available
+ *    from skv_last_error() on the calling thread.  Arguments are validated
+ *    before any HIP call, so validation errors leave the stream untouched.
+ *    A HIP launch failure returns SKV_EHIP.  Faults inside kernels surface
+ *    at the caller's next synchronization.
+ *  - Q, dO, O, dQ:   [sum_s Mq_s, hq, d]   element (t, h, x) at
+ *                    t*q_stride_tok + h*q_stride_head + x
+ *    K, V, dK, dV:   [sum_s N_s, hkv, d]   element (j, g, x) at
+ *                    j*kv_stride_tok + g*kv_stride_head + x
+ *    LSE:            float [sum_s Mq_s, hq], row-major (t*hq + h).
+ *  - Query head h uses KV head h / (hq / hkv).
+ *  - Logits are sm_scale * q.k; LSE is in natural-log units.
+ */
+#ifndef SPLITKV_H_
+#define SPLITKV_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SKV_OK = 0,
+  SKV_EINVAL = -1,     /* null pointer, bad count, unsorted anchors, ... */
+  SKV_EDTYPE = -2,     /* dtype not supported by this call */
+  SKV_ESHAPE = -3,     /* head_dim, head counts, chunk, strides or alignment */
+  SKV_EHIP = -4,       /* a HIP runtime call failed */
+  SKV_EWORKSPACE = -5, /* workspace missing or too small */
+  SKV_EPLAN = -6       /* plan does not match the call */
+} skv_status;
+
+typedef enum { SKV_F32 = 0, SKV_BF16 = 1 } skv_dtype;
+typedef enum { SKV_ITEM_FWD = 0, SKV_ITEM_BWD = 1 } skv_item_kind;
+typedef enum { SKV_POLICY_LPT = 0, SKV_POLICY_STATIC = 1 } skv_policy;
+
+enum { SKV_TILE = 64 }; /* key-tile granularity of mask skipping and of the cost model */
+
+/* One attention problem: a batch of n_seq sequences packed along the token
+ * axis.  Sequence s owns query rows [q_off[s], q_off[s+1]) (a whole number of
+ * draft blocks) and context tokens [kv_off[s], kv_off[s+1]).  Its draft block
+ * b (0-based within s) is anchor[q_off[s]/block + b].  Every pointer pair holds
+ * the same values in host memory (h_*) and device memory (d_*). */
+typedef struct skv_problem {
+  int32_t n_seq;
+  int32_t block;          /* B: draft tokens per anchor, >= 1 */
+  int32_t hq;             /* query heads */
+  int32_t hkv;            /* KV heads; hq % hkv == 0 */
+  int32_t d;              /* head dim: 128 for bf16; 64 or 128 for f32 */
+  int32_t chunk;          /* L: KV chunk length, positive multiple of SKV_TILE */
+  int32_t dtype;          /* skv_dtype of Q, K, V, O, dO, dQ, dK, dV */
+  float sm_scale;         /* logit scale, finite and > 0 (usually 1/sqrt(d)) */
+  const int64_t *h_q_off, *d_q_off;    /* [n_seq+1], multiples of block, non-decreasing */
+  const int64_t *h_kv_off, *d_kv_off;  /* [n_seq+1], non-decreasing */
+  const int32_t *h_anchor, *d_anchor;  /* [q_off[n_seq]/block], >= 0, sorted per sequence */
+  int64_t q_stride_tok, q_stride_head;   /* elements; head_dim is contiguous */
+  int64_t kv_stride_tok, kv_stride_head; /* elements; head_dim is contiguous */
+} skv_problem;
+
+/* One work item, 32 bytes.  Built on the host by skv_item_table.
+ * FWD: (seq, kv_head, chunk, range) covers draft blocks [lo, hi) of the
+ *      sequence, all hq/hkv query heads of kv_head, against chunk `chunk`;
+ *      part_base is the first partial row of (seq, chunk).
+ * BWD: covers context keys [lo, hi) of the sequence (inside chunk `chunk`)
+ *      for kv_head; part_base is unused (0). */
+typedef struct skv_item {
+  int32_t seq, kv_head, chunk, range;
+  int64_t part_base;
+  int32_t lo, hi;
+} skv_item;
+
+/* A plan as the kernels read it: items grouped by persistent workgroup.
+ * Workgroup w runs d_items[d_worker_off[w] .. d_worker_off[w+1]) in order.
+ * n_workers is the launched grid size. */
+typedef struct skv_plan {
+  int32_t kind;       /* skv_item_kind */
+  int32_t n_workers;  /* >= 1 */
+  int64_t n_items;
+  const skv_item* d_items;      /* device, [n_items] */
+  const int64_t* d_worker_off;  /* device, [n_workers+1], d_worker_off[0] = 0 */
+} skv_plan;
+
+/* Thread-local description of the last error (never NULL). */
+const char* skv_last_error(void);
+
+/* Validate a problem (host copies only).  SKV_OK if usable by the device calls. */
+int skv_check_problem(const skv_problem* p);
+
+/* Partial layout of sparse_attn_partial_fwd.  Sequence s has
+ * n_chunk[s] = ceil(N_s / chunk) partials; partial (s, c) owns rows
+ * part_base[s] + c*hq*Mq_s + h*Mq_s + r  (h = query head, r = query row in s).
+ * part_base has n_seq+1 entries; part_base[n_seq] is the total number of
+ * partial rows.  Either output may be NULL. */
+int skv_partial_layout(const skv_problem* p, int64_t* part_base, int32_t* n_chunk);
+
+/* Work items of a problem, in enumeration order (seq, kv_head, chunk, range),
+ * row-major.  FWD: granule = draft blocks per item.  BWD: granule = keys per
+ * item, a positive multiple of SKV_TILE; ranges restart at every chunk.
+ * Cost = (hq/hkv) x number of (draft block, 64-key tile) pairs of the item in
+ * which the block sees at least one key of the tile (block b sees tile t iff
+ * t*64 < e_b) — the item's realized attention cost.  tok_start = token offset
+ * of the item in the stream of (seq, kv_head, chunk) units laid end to end
+ * (all FWD ranges of one unit share its start); *total_tok = length of that
+ * stream.  Call with items == cost == tok_start == NULL to get *n_items only.
+ * Output arrays, when given, hold *n_items entries. */
+int skv_item_table(const skv_problem* p, int32_t kind, int32_t granule, skv_item* items, int64_t* cost,
+                   int64_t* tok_start, int64_t* n_items, int64_t* total_tok);
+
+/* Cost-aware longest-processing-time-first planning ("LPT Scheduling": sort
+ * by cost, largest first, give each to the least-loaded worker).  Tie-break:
+ * items in order of (cost descending, item id ascending); the chosen worker is
+ * the one with the smallest (load, worker id).  Zero costs are planned too.
+ * cost[n] >= 0.  Outputs (any may be NULL): assign[n] worker of each item;
+ * order[n] item ids grouped by worker, each worker's items in assignment
+ * order; worker_off[n_workers+1]; load[n_workers].  Host only. */
+int lpt_plan(const int64_t* cost, int64_t n, int32_t n_workers, int32_t* assign, int64_t* order,
+             int64_t* worker_off, int64_t* load);
+
+/* Static token-count plan (the baseline LPT is compared with): worker of item
+ * i = floor(tok_start[i] * n_workers / total_tok).  order/worker_off group the
+ * items by worker in ascending id order.  Outputs may be NULL.  Host only. */
+int skv_static_plan(const int64_t* tok_start, int64_t n, int64_t total_tok, int32_t n_workers,
+                    int32_t* assign, int64_t* order, int64_t* worker_off);
+
+/* items_out[i] = items[order[i]] for i < n (host gather into plan order). */
+int skv_gather_items(const skv_item* items, const int64_t* order, int64_t n, skv_item* items_out);
+
+/* Forward partials, one per (sequence, KV chunk).  For every query row r of
+ * sequence s, query head h and chunk c with visible keys
+ * J = {j in [c*L, min((c+1)*L, N_s)) : j < e_b}:
+ *   m_part   = max_{j in J} s_j                        (s_j = sm_scale*q.k_j)
+ *   o_part   = sum_{j in J} exp(s_j - m_part) * v_j    (unnormalised, fp32)
+ *   lse_part = m_part + ln sum_{j in J} exp(s_j - m_part)
+ * at row part_base[s] + c*hq*Mq_s + h*Mq_s + r (see skv_partial_layout);
+ * o_part rows are d floats.  Rows with J empty get m_part = lse_part = -inf
+ * and their o_part row is not written.  Fully masked 64-key tiles are never
+ * read.  `plan` must be a FWD plan over skv_item_table items of this problem
+ * covering every (seq, kv_head, chunk, range) exactly once; it is launched
+ * with plan->n_workers workgroups.  Results are bitwise deterministic. */
+int sparse_attn_partial_fwd(const skv_problem* p, const skv_plan* plan, const void* q, const void* k,
+                            const void* v, float* o_part, float* m_part, float* lse_part, void* stream);
+
+/* Exact log-sum-exp merge of n_part partials of one sequence.
+ * Inputs: o_part [n_part][hq][mq][d], m_part and lse_part [n_part][hq][mq]
+ * (fp32, the layout sparse_attn_partial_fwd writes for one sequence: pass
+ * pointers offset to part_base[s]).  Per row (h, r):
+ *   M = max_c lse_c,  LSE = M + ln sum_c exp(lse_c - M),
+ *   O = sum_{c : lse_c > -inf} exp(m_c - LSE) * o_c
+ * (o_c rows of partials with lse_c = -inf are never read).  A row with every
+ * lse_c = -inf gets O = 0 and LSE = -inf.  O is written in out_dtype at
+ * o_out + r*o_stride_tok + h*o_stride_head (+ x); LSE at lse_out[r*lse_stride_tok + h].
+ * n_part may be 0.  Bitwise deterministic. */
+int lse_merge(int32_t n_part, int32_t hq, int64_t mq, int32_t d, const float* o_part, const float* m_part,
+              const float* lse_part, void* o_out, int64_t o_stride_tok, int64_t o_stride_head, int32_t out_dtype,
+              float* lse_out, int64_t lse_stride_tok, void* stream);
+
+/* Bytes of device workspace sparse_attn_bwd needs: an fp32 dQ accumulator
+ * [sum Mq][hq][d] and fp32 Delta [sum Mq][hq], each 256-byte aligned. */
+size_t skv_bwd_workspace_bytes(const skv_problem* p);
+
+/* Backward of O with respect to Q, K, V, reusing the merged LSE.
+ * With P = exp(s - LSE) on visible entries (0 elsewhere), Delta = sum_x dO*O,
+ * dS = P*(dO.v - Delta):  dV_j = sum P dO,  dQ = sm_scale * dS K,
+ * dK_j = sm_scale * sum dS q, summed over the query heads of each KV head.
+ * o = merged output (problem dtype, Q layout), lse = merged LSE (float
+ * [sum Mq][hq]), dout = dO.  Outputs dq (Q layout), dk and dv (K/V layout)
+ * are fully written, dk = dv = 0 for keys no query sees.  `plan` must be a
+ * BWD plan over skv_item_table items covering every key range once.  dQ is
+ * accumulated with fp32 atomics, so it is not bitwise reproducible.
+ * Only SKV_BF16 with d = 128 is supported. */
+int sparse_attn_bwd(const skv_problem* p, const skv_plan* plan, const void* q, const void* k, const void* v,
+                    const void* o, const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPLITKV_H_ */

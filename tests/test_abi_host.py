@@ -1,0 +1,191 @@
+"""CPU tests of the C ABI: the library loads and exports every declared call,
+host planning matches the oracle bit for bit, and invalid arguments are
+rejected (before any HIP call, so no GPU is needed)."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from block_sparse_draft_amd import binding as B
+from synthetic import make
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_library_exports_every_declared_call():
+    hdr = open(os.path.join(ROOT, "include", "splitkv.h")).read()
+    hdr = re.sub(r"/\*.*?\*/", "", hdr, flags=re.S)
+    names = set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(\w+)\s*\(", hdr, flags=re.M))
+    assert {"sparse_attn_partial_fwd", "lse_merge", "sparse_attn_bwd", "lpt_plan"} <= names
+    lib = C.CDLL(B.LIB_PATH)
+    missing = [n for n in sorted(names) if not hasattr(lib, n)]
+    assert not missing, missing
+    assert set(B.EXPORTED) == names
+
+
+def _problem_from(w, device=None):
+    dt = B.SKV_BF16 if w.is_bf16 else B.SKV_F32
+    return B.Problem(w.q_off, w.kv_off, w.anchors, w.cfg.block, w.cfg.hq, w.cfg.hkv, w.cfg.d, w.cfg.chunk, dt,
+                     w.sm_scale, device=device)
+
+
+def _oracle_table(w, kind, granule):
+    anchors = [w.seq_anchors(s) for s in range(w.cfg.n_seq)]
+    return oracle.item_table(list(w.n_ctx), anchors, w.cfg.block, w.cfg.hq, w.cfg.hkv, w.cfg.chunk, kind, granule)
+
+
+@pytest.mark.parametrize("cfg,over", [
+    ("c1", {}), ("c2", {}), ("c3", {}), ("c5", {}),
+    ("c3", {"n_ctx_range": (100, 2000), "chunk": 128}),
+])
+@pytest.mark.parametrize("kind,granule", [("fwd", 1), ("fwd", 4), ("bwd", 64), ("bwd", 256)])
+def test_item_table_matches_oracle(cfg, over, kind, granule):
+    w = make(cfg, seed=1, with_do=False, **over) if cfg in ("c1", "c2") else _meta_only(cfg, over)
+    p = _problem_from(w)
+    items, cost, tok, total = p.item_table(B.SKV_ITEM_FWD if kind == "fwd" else B.SKV_ITEM_BWD, granule)
+    desc, ocost, otok, ototal = _oracle_table(w, kind, granule)
+    assert np.array_equal(cost, ocost)
+    assert np.array_equal(tok, otok) and total == ototal
+    assert np.array_equal(np.stack([items["seq"], items["kv_head"], items["chunk"], items["range"]], 1), desc)
+
+
+def _meta_only(cfg, over):
+    """Full-size metadata without drawing the big tensors."""
+    from synthetic import workloads as W
+    c = W.CONFIGS[cfg]
+    import dataclasses
+    c = dataclasses.replace(c, **over)
+    rl = W._rng(1, c.cid, W.STREAM_LEN)
+    if c.n_ctx_range is not None:
+        n_ctx = rl.integers(c.n_ctx_range[0], c.n_ctx_range[1], size=c.n_seq, endpoint=True).astype(np.int64)
+    else:
+        n_ctx = np.full(c.n_seq, c.n_ctx, dtype=np.int64)
+    ra = W._rng(1, c.cid, W.STREAM_ANCHOR)
+    anchors = np.concatenate([W._draw_anchors(ra, c, int(n)) for n in n_ctx]).astype(np.int32)
+    mq = c.n_anchor * c.block
+    e = np.empty((0,), np.uint16)
+    return W.Workload(c, n_ctx, anchors, np.arange(c.n_seq + 1, dtype=np.int64) * mq,
+                      np.concatenate([[0], np.cumsum(n_ctx)]).astype(np.int64), e, e, e, None, c.d ** -0.5, 1)
+
+
+@pytest.mark.parametrize("seed", range(25))
+def test_lpt_bit_exact_with_oracle_under_ties(seed):
+    rng = np.random.default_rng(seed)
+    n = int(rng.integers(0, 300))
+    W = int(rng.integers(1, 40))
+    cost = rng.integers(0, 6, size=n) * int(rng.integers(1, 4))   # many ties, zeros
+    a1, o1, f1, l1 = B.lpt_plan(cost, W)
+    a2, o2, f2, l2 = oracle.lpt(cost, W)
+    assert np.array_equal(a1, a2) and np.array_equal(o1, o2) and np.array_equal(f1, f2) and np.array_equal(l1, l2)
+
+
+def test_lpt_worked_example_and_degenerate_inputs():
+    a, o, f, l = B.lpt_plan([3, 3, 2, 2, 2], 2)
+    assert list(a) == [0, 1, 0, 1, 0] and list(l) == [7, 5]
+    a, o, f, l = B.lpt_plan(np.zeros(0, np.int64), 3)
+    assert len(a) == 0 and list(f) == [0, 0, 0, 0] and list(l) == [0, 0, 0]
+    a, o, f, l = B.lpt_plan([5, 5], 7)
+    assert list(a) == [0, 1] and list(l) == [5, 5, 0, 0, 0, 0, 0]
+    with pytest.raises(B.SkvError) as e:
+        B.lpt_plan([1, 2], 0)
+    assert e.value.code == B.SKV_EINVAL
+    with pytest.raises(B.SkvError):
+        B.lpt_plan([1, -2], 2)
+
+
+@pytest.mark.parametrize("cfg", ["c3", "c5"])
+def test_lpt_and_static_on_full_size_items_match_oracle(cfg):
+    w = _meta_only(cfg, {})
+    p = _problem_from(w)
+    G = w.cfg.hq // w.cfg.hkv
+    items, cost, tok, total = p.item_table(B.SKV_ITEM_FWD, max(1, 256 // (G * w.cfg.block)))
+    a1, o1, f1, l1 = B.lpt_plan(cost, 256)
+    a2, o2, f2, l2 = oracle.lpt(cost, 256)
+    assert np.array_equal(a1, a2) and np.array_equal(o1, o2) and np.array_equal(l1, l2)
+    s1, so1, sf1 = B.skv_static_plan(tok, total, 256)
+    s2 = oracle.static_assign(tok, total, 256)
+    so2, sf2 = oracle.csr_from_assign(s2, 256)
+    assert np.array_equal(s1, s2) and np.array_equal(so1, so2) and np.array_equal(sf1, sf2)
+    g = B.skv_gather_items(items, o1)
+    assert np.array_equal(g, items[o1])
+
+
+def test_partial_layout():
+    w = _meta_only("c3", {})
+    p = _problem_from(w)
+    base, nchunk = p.partial_layout()
+    C_s = -(-w.n_ctx // w.cfg.chunk)
+    assert list(nchunk) == list(C_s)
+    mq = w.cfg.n_anchor * w.cfg.block
+    assert list(np.diff(base)) == list(C_s * w.cfg.hq * mq)
+
+
+def _bad(w, **kw):
+    p = _problem_from(w)
+    for k, v in kw.items():
+        setattr(p.c, k, v)
+    return p
+
+
+def test_problem_validation_codes():
+    w = make("c1", seed=0)
+    assert B.lib.skv_check_problem(C.byref(_problem_from(w).c)) == B.SKV_OK
+    cases = [({"hq": 3, "hkv": 2}, B.SKV_ESHAPE), ({"chunk": 100}, B.SKV_ESHAPE), ({"chunk": 0}, B.SKV_ESHAPE),
+             ({"d": 96}, B.SKV_ESHAPE), ({"dtype": 7}, B.SKV_EDTYPE), ({"block": 0}, B.SKV_EINVAL),
+             ({"sm_scale": float("nan")}, B.SKV_EINVAL), ({"h_anchor": None}, B.SKV_EINVAL),
+             ({"q_stride_tok": 3}, B.SKV_ESHAPE), ({"n_seq": -1}, B.SKV_EINVAL)]
+    for kw, code in cases:
+        p = _bad(w, **kw)
+        assert B.lib.skv_check_problem(C.byref(p.c)) == code, kw
+        assert B.last_error() != "no error"
+    # bf16 supports head_dim 128 only
+    p = _bad(w, dtype=B.SKV_BF16)
+    assert B.lib.skv_check_problem(C.byref(p.c)) == B.SKV_ESHAPE
+    # unsorted anchors
+    p = _problem_from(w)
+    p.h_anchor[:] = p.h_anchor[::-1].copy()
+    assert B.lib.skv_check_problem(C.byref(p.c)) == B.SKV_EINVAL
+    assert "sorted" in B.last_error()
+
+
+def test_device_calls_reject_bad_arguments_before_touching_the_gpu():
+    w = make("c1", seed=0)
+    p = _problem_from(w)           # host-only: device arrays NULL
+    plan = B.skv_plan(B.SKV_ITEM_FWD, 4, 1, 16, 16)
+    fake = C.c_void_p(4096)
+    rc = B.lib.sparse_attn_partial_fwd(C.byref(p.c), C.byref(plan), fake, fake, fake, fake, fake, fake, None)
+    assert rc == B.SKV_EINVAL and "device" in B.last_error()
+    # wrong plan kind
+    p.c.d_q_off = p.c.d_kv_off = p.c.d_anchor = 4096
+    bplan = B.skv_plan(B.SKV_ITEM_BWD, 4, 1, 16, 16)
+    rc = B.lib.sparse_attn_partial_fwd(C.byref(p.c), C.byref(bplan), fake, fake, fake, fake, fake, fake, None)
+    assert rc == B.SKV_EPLAN
+    zplan = B.skv_plan(B.SKV_ITEM_FWD, 0, 1, 16, 16)
+    rc = B.lib.sparse_attn_partial_fwd(C.byref(p.c), C.byref(zplan), fake, fake, fake, fake, fake, fake, None)
+    assert rc == B.SKV_EPLAN
+    rc = B.lib.sparse_attn_partial_fwd(C.byref(p.c), C.byref(plan), None, fake, fake, fake, fake, fake, None)
+    assert rc == B.SKV_EINVAL
+    rc = B.lib.sparse_attn_partial_fwd(C.byref(p.c), C.byref(plan), C.c_void_p(4098), fake, fake, fake, fake, fake,
+                                       None)
+    assert rc == B.SKV_ESHAPE
+    # bwd: fp32 problems are rejected, workspace is checked
+    rc = B.lib.sparse_attn_bwd(C.byref(p.c), C.byref(bplan), *([fake] * 10), 1 << 30, None)
+    assert rc == B.SKV_EDTYPE
+    wb = make("c2", seed=0, n_ctx=256, n_anchor=2)
+    pb = _problem_from(wb)
+    pb.c.d_q_off = pb.c.d_kv_off = pb.c.d_anchor = 4096
+    need = B.lib.skv_bwd_workspace_bytes(C.byref(pb.c))
+    assert need == 32 * 32 * 128 * 4 + 32 * 32 * 4
+    rc = B.lib.sparse_attn_bwd(C.byref(pb.c), C.byref(bplan), *([fake] * 10), need - 1, None)
+    assert rc == B.SKV_EWORKSPACE
+    # merge
+    rc = B.lib.lse_merge(4, 2, 64, 96, fake, fake, fake, fake, 128, 64, B.SKV_F32, fake, 2, None)
+    assert rc == B.SKV_ESHAPE
+    rc = B.lib.lse_merge(-1, 2, 64, 64, fake, fake, fake, fake, 128, 64, B.SKV_F32, fake, 2, None)
+    assert rc == B.SKV_EINVAL
+    rc = B.lib.lse_merge(4, 2, 64, 64, fake, fake, fake, fake, 128, 64, 5, fake, 2, None)
+    assert rc == B.SKV_EDTYPE
+    assert B.lib.lse_merge(4, 2, 0, 64, None, None, None, None, 128, 64, B.SKV_F32, None, 2, None) == B.SKV_OK

@@ -1,0 +1,271 @@
+"""GPU parity: the HIP path, called through the C ABI, against the float64
+oracle on identical seeded inputs (bf16 inputs are compared with the oracle
+fed the same bf16-rounded values).  Small cases span several tiles, chunks and
+a ragged tail; the full configurations are checked on sampled sequences / KV
+heads and through invariants that hold at any size."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from helpers import (BF16_ABS, BF16_FROB, BF16_LSE_REL, F32_ABS, assert_close, assert_lse, make_path, to_device,
+                     to_np64)
+from synthetic import make, make_custom
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _upload(w):
+    return [to_device(w, n, DEV) for n in ("q", "k", "v")]
+
+
+def _check_partials(path, w, seqs=None, heads=None, abs_tol=BF16_ABS, frob_tol=BF16_FROB, lse_tol=BF16_LSE_REL):
+    """Compare every visible partial row, normalised by its own LSE (the
+    chunk-local attention output), plus m_c and LSE_c."""
+    for s in (range(w.cfg.n_seq) if seqs is None else seqs):
+        op, mp, lp = oracle.partials_workload(w, s, heads=heads)
+        go, gm, gl = [to_np64(t) for t in path.partial_view(s)]
+        hs = list(range(w.cfg.hq)) if heads is None else list(heads)
+        op, mp, lp, go, gm, gl = op[:, hs], mp[:, hs], lp[:, hs], go[:, hs], gm[:, hs], gl[:, hs]
+        assert_lse(f"seq{s} lse_part", gl, lp, lse_tol)
+        assert_lse(f"seq{s} m_part", gm, mp, lse_tol)
+        vis = np.isfinite(lp)
+        with np.errstate(invalid="ignore", over="ignore"):
+            gn = go * np.exp(np.where(vis, gm - gl, 0.0))[..., None]
+            on = op * np.exp(np.where(vis, mp - lp, 0.0))[..., None]
+        assert_close(f"seq{s} normalised o_part", gn[vis], on[vis], abs_tol, frob_tol)
+
+
+def _check_merged(path, w, O, L, heads=None, rows=None, abs_tol=BF16_ABS, frob_tol=BF16_FROB, lse_tol=BF16_LSE_REL):
+    go, gl = to_np64(path.o), to_np64(path.lse)
+    hs = slice(None) if heads is None else list(heads)
+    rs = slice(None) if rows is None else rows
+    assert_close("O", go[rs][:, hs], O[rs][:, hs], abs_tol, frob_tol)
+    assert_lse("LSE", gl[rs][:, hs], L[rs][:, hs], lse_tol)
+
+
+# ---------------------------------------------------------------------------
+# fp32 (tiny config, full)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_c1_fp32_partials_and_merge(seed):
+    w = make("c1", seed=seed)
+    path = make_path(w, DEV)
+    q, k, v = _upload(w)
+    path.forward(q, k, v)
+    torch.cuda.synchronize()
+    _check_partials(path, w, abs_tol=F32_ABS, frob_tol=None, lse_tol=F32_ABS)
+    O, L = oracle.attention_workload(w)
+    _check_merged(path, w, O, L, abs_tol=F32_ABS, frob_tol=None, lse_tol=F32_ABS)
+
+
+def test_fp32_head_dim_128_ragged():
+    w = make("c1", seed=3, n_ctx=777, d=128, hq=4, hkv=2, chunk=192)
+    path = make_path(w, DEV)
+    q, k, v = _upload(w)
+    path.forward(q, k, v)
+    torch.cuda.synchronize()
+    O, L = oracle.attention_workload(w)
+    _check_merged(path, w, O, L, abs_tol=F32_ABS, frob_tol=None, lse_tol=F32_ABS)
+
+
+# ---------------------------------------------------------------------------
+# bf16 forward
+# ---------------------------------------------------------------------------
+
+SMALL_BF16 = {
+    # c2 recipe: 3 chunks, ragged tail (3000 = 46 tiles + 56), anchors reach the end
+    "c2_small": ("c2", dict(n_ctx=3000, n_anchor=8, hq=8, hkv=2, chunk=1024)),
+    # c3 recipe: several sequences of ragged lengths, GQA 4
+    "c3_small": ("c3", dict(n_ctx_range=(500, 2500), n_anchor=6, hq=8, hkv=2, chunk=512)),
+    # c5 recipe: G = 1, 32-token blocks, anchors clustered late
+    "c5_small": ("c5", dict(n_ctx=4100, n_anchor=12, hq=4, hkv=4, chunk=1024)),
+    # c4 recipe: many chunks merged
+    "c4_small": ("c4", dict(n_ctx=8192, n_anchor=8, hq=4, hkv=1, chunk=256)),
+}
+
+
+@pytest.mark.parametrize("case", sorted(SMALL_BF16))
+def test_bf16_forward_small(case):
+    cfg, over = SMALL_BF16[case]
+    w = make(cfg, seed=7, with_do=False, **over)
+    path = make_path(w, DEV, with_bwd=False)
+    q, k, v = _upload(w)
+    path.forward(q, k, v)
+    torch.cuda.synchronize()
+    _check_partials(path, w)
+    O, L = oracle.attention_workload(w)
+    _check_merged(path, w, O, L)
+
+
+def test_bf16_forward_edge_anchors():
+    """Anchors at 0, at N-1 (clipped block), duplicates, and a context whose
+    length is not a multiple of the tile."""
+    w = make_custom([1000, 130], [[0, 0, 63, 64, 700], [1, 2, 3, 128, 129]], block=16, hq=4, hkv=2, d=128,
+                    dtype="bf16", chunk=128, seed=4, with_do=True)
+    path = make_path(w, DEV)
+    q, k, v = _upload(w)
+    path.forward(q, k, v)
+    torch.cuda.synchronize()
+    _check_partials(path, w)
+    O, L = oracle.attention_workload(w)
+    _check_merged(path, w, O, L)
+
+
+def test_bf16_forward_c2_full():
+    w = make("c2", seed=0)
+    path = make_path(w, DEV)
+    q, k, v = _upload(w)
+    path.forward(q, k, v)
+    torch.cuda.synchronize()
+    O, L = oracle.attention_workload(w)
+    _check_merged(path, w, O, L)
+    _check_partials(path, w, heads=[0, 13, 31])
+
+
+# ---------------------------------------------------------------------------
+# bf16 backward
+# ---------------------------------------------------------------------------
+
+def _bwd(w, path, q, k, v):
+    do = to_device(w, "do", DEV)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    path.forward(q, k, v)
+    path.backward(q, k, v, do, dq, dk, dv)
+    torch.cuda.synchronize()
+    return to_np64(dq), to_np64(dk), to_np64(dv)
+
+
+def _check_grads(w, got, kv_heads=None, seqs=None):
+    dq, dk, dv = got
+    rq, rk, rv, _, _ = oracle.bwd_workload(w, kv_heads=kv_heads, seqs=seqs)
+    G = w.cfg.hq // w.cfg.hkv
+    gs = list(range(w.cfg.hkv)) if kv_heads is None else list(kv_heads)
+    hs = [h for g in gs for h in range(g * G, (g + 1) * G)]
+    ss = list(range(w.cfg.n_seq)) if seqs is None else list(seqs)
+    qr = np.concatenate([np.arange(w.q_off[s], w.q_off[s + 1]) for s in ss])
+    kr = np.concatenate([np.arange(w.kv_off[s], w.kv_off[s + 1]) for s in ss])
+    assert_close("dQ", dq[qr][:, hs], rq[qr][:, hs], BF16_ABS, BF16_FROB)
+    assert_close("dK", dk[kr][:, gs], rk[kr][:, gs], BF16_ABS, BF16_FROB)
+    assert_close("dV", dv[kr][:, gs], rv[kr][:, gs], BF16_ABS, BF16_FROB)
+
+
+@pytest.mark.parametrize("case", ["c2_small", "c3_small", "c5_small", "c4_small"])
+def test_bf16_backward_small(case):
+    cfg, over = SMALL_BF16[case]
+    w = make(cfg, seed=11, with_do=True, **over)
+    path = make_path(w, DEV, with_bwd=True, bwd_granule=192)
+    q, k, v = _upload(w)
+    got = _bwd(w, path, q, k, v)
+    _check_grads(w, got)
+
+
+def test_bf16_backward_edge_anchors():
+    w = make_custom([1000, 130], [[0, 0, 63, 64, 700], [1, 2, 3, 128, 129]], block=16, hq=4, hkv=2, d=128,
+                    dtype="bf16", chunk=128, seed=5, with_do=True)
+    path = make_path(w, DEV, with_bwd=True, bwd_granule=64)
+    q, k, v = _upload(w)
+    got = _bwd(w, path, q, k, v)
+    _check_grads(w, got)
+    # keys no query sees (716 .. 999 of the first sequence) get exactly zero gradient
+    dk, dv = got[1], got[2]
+    assert np.all(dk[716:1000] == 0) and np.all(dv[716:1000] == 0)
+    assert np.abs(dk[:716]).max() > 0
+
+
+@pytest.mark.parametrize("cfg,kv_heads,seqs", [("c3", [3], [1]), ("c4", [2], None), ("c5", [9], None)])
+def test_full_size_fwd_bwd_sampled(cfg, kv_heads, seqs):
+    """Full configuration on the GPU, compared with the oracle on one KV head
+    (and one sequence for the 4-sequence config)."""
+    w = make(cfg, seed=0)
+    path = make_path(w, DEV)
+    q, k, v = _upload(w)
+    got = _bwd(w, path, q, k, v)
+    G = w.cfg.hq // w.cfg.hkv
+    hs = list(range(kv_heads[0] * G, (kv_heads[0] + 1) * G))
+    ss = list(range(w.cfg.n_seq)) if seqs is None else seqs
+    O = np.zeros((int(w.q_off[-1]), w.cfg.hq, w.cfg.d))
+    L = np.full((int(w.q_off[-1]), w.cfg.hq), -np.inf)
+    for s in ss:
+        q64 = w.as_f64("q", rows=slice(int(w.q_off[s]), int(w.q_off[s + 1])))
+        k64 = w.as_f64("k", rows=slice(int(w.kv_off[s]), int(w.kv_off[s + 1])))
+        v64 = w.as_f64("v", rows=slice(int(w.kv_off[s]), int(w.kv_off[s + 1])))
+        o, l = oracle.attention(q64, k64, v64, w.seq_anchors(s), w.cfg.block, w.sm_scale, heads=hs)
+        O[int(w.q_off[s]):int(w.q_off[s + 1])] = o
+        L[int(w.q_off[s]):int(w.q_off[s + 1])] = l
+    rows = np.concatenate([np.arange(w.q_off[s], w.q_off[s + 1]) for s in ss])
+    _check_merged(path, w, O, L, heads=hs, rows=rows)
+    _check_grads(w, got, kv_heads=kv_heads, seqs=seqs)
+
+
+# ---------------------------------------------------------------------------
+# invariants at any size
+# ---------------------------------------------------------------------------
+
+def test_forward_and_merge_are_bitwise_deterministic_and_plan_independent():
+    w = make("c3", seed=2, with_do=False, n_ctx_range=(3000, 9000), n_anchor=16, hq=8, hkv=2, chunk=1024)
+    q, k, v = _upload(w)
+    a = make_path(w, DEV, with_bwd=False)
+    a.forward(q, k, v)
+    o1, l1 = a.o.clone(), a.lse.clone()
+    a.forward(q, k, v)
+    b = make_path(w, DEV, with_bwd=False, policy="static")
+    b.forward(q, k, v)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, a.o) and torch.equal(l1, a.lse)
+    assert torch.equal(o1, b.o) and torch.equal(l1, b.lse)
+
+
+def test_poisoned_invisible_tiles_are_never_read():
+    """NaN in every key tile that no draft block sees leaves outputs bitwise unchanged."""
+    w = make("c2", seed=3, with_do=False, n_ctx=6000, n_anchor=8, hq=8, hkv=2, chunk=1024)
+    q, k, v = _upload(w)
+    path = make_path(w, DEV, with_bwd=False)
+    path.forward(q, k, v)
+    o1, l1 = path.o.clone(), path.lse.clone()
+    e_max = int(min(w.anchors.max() + w.cfg.block, 6000))
+    first_dead_tile = -(-e_max // 64) * 64
+    assert first_dead_tile < 6000
+    k2, v2 = k.clone(), v.clone()
+    k2[first_dead_tile:] = float("nan")
+    v2[first_dead_tile:] = float("inf")
+    path.forward(q, k2, v2)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, path.o) and torch.equal(l1, path.lse)
+
+
+def test_split_matches_single_chunk():
+    """Split-then-merge equals the unsplit result (one chunk covering the context)."""
+    w = make("c2", seed=4, with_do=False, n_ctx=5000, n_anchor=8, hq=8, hkv=2, chunk=512)
+    q, k, v = _upload(w)
+    a = make_path(w, DEV, with_bwd=False)
+    a.forward(q, k, v)
+    import dataclasses
+    w1 = dataclasses.replace(w, cfg=dataclasses.replace(w.cfg, chunk=5056))
+    b = make_path(w1, DEV, with_bwd=False)
+    b.forward(q, k, v)
+    torch.cuda.synchronize()
+    assert_close("split vs unsplit O", to_np64(a.o), to_np64(b.o), 4e-3, 4e-3)
+    assert_lse("split vs unsplit LSE", to_np64(a.lse), to_np64(b.lse), 1e-5)
+
+
+def test_identical_keys_and_constant_values():
+    """Identical keys: O = mean of the visible V rows, dQ = 0.  Constant V: O = v."""
+    w = make("c2", seed=5, with_do=True, n_ctx=3000, n_anchor=8, hq=4, hkv=2, chunk=1024)
+    w.k[:] = w.k[0:1]
+    q, k, v = _upload(w)
+    path = make_path(w, DEV, with_bwd=True)
+    dq, dk, dv = _bwd(w, path, q, k, v)
+    O, _ = oracle.attention_workload(w)
+    assert_close("O (identical keys)", to_np64(path.o), O, BF16_ABS, BF16_FROB)
+    assert np.abs(dq).max() < 5e-3
+    w.v[:] = w.v[5:6]
+    q, k, v = _upload(w)
+    path.forward(q, k, v)
+    torch.cuda.synchronize()
+    o = to_np64(path.o)
+    for h in range(w.cfg.hq):
+        vv = w.as_f64("v", rows=slice(5, 6))[0, h // 2]
+        assert np.abs(o[:, h] - vv).max() <= 2 ** -7 * np.abs(vv).max()
