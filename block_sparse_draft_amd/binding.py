@@ -52,7 +52,7 @@ assert ITEM_DTYPE.itemsize == C.sizeof(skv_item) == 32
 
 class skv_plan(C.Structure):
     _fields_ = [("kind", C.c_int32), ("n_workers", C.c_int32), ("n_items", C.c_int64),
-                ("d_items", C.c_void_p), ("d_worker_off", C.c_void_p)]
+                ("d_items", C.c_void_p), ("d_worker_off", C.c_void_p), ("d_claim", C.c_void_p)]
 
 
 def _load():
@@ -76,7 +76,7 @@ def _load():
         "sparse_attn_partial_fwd": (C.c_int, [P(skv_problem), P(skv_plan), VP, VP, VP, VP, VP, VP, VP]),
         "lse_merge": (C.c_int, [I32, I32, I64, I32, VP, VP, VP, VP, I64, I64, I32, VP, I64, VP]),
         "skv_bwd_workspace_bytes": (C.c_size_t, [P(skv_problem)]),
-        "sparse_attn_bwd": (C.c_int, [P(skv_problem), P(skv_plan)] + [VP] * 10 + [C.c_size_t, VP]),
+        "sparse_attn_bwd": (C.c_int, [P(skv_problem), P(skv_plan), P(skv_plan)] + [VP] * 10 + [C.c_size_t, VP]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -233,7 +233,9 @@ class Plan:
         self.h_items = skv_gather_items(items, order)
         self.d_items = torch.from_numpy(self.h_items.view(np.uint8).copy()).to(problem.device)
         self.d_worker_off = torch.from_numpy(off).to(problem.device)
-        self.c = skv_plan(kind, n_workers, len(items), self.d_items.data_ptr(), self.d_worker_off.data_ptr())
+        self.d_claim = torch.zeros(n_workers, dtype=torch.int32, device=problem.device)
+        self.c = skv_plan(kind, n_workers, len(items), self.d_items.data_ptr(), self.d_worker_off.data_ptr(),
+                          self.d_claim.data_ptr())
 
     @property
     def imbalance(self) -> float:
@@ -264,7 +266,9 @@ def lse_merge(n_part: int, hq: int, mq: int, d: int, o_part, m_part, lse_part, o
                          _ptr(lse_out) + lse_offset * 4, lse_stride_tok, _stream(stream)))
 
 
-def sparse_attn_bwd(problem: Problem, plan: Plan, q, k, v, o, lse, dout, dq, dk, dv, workspace, stream=None):
+def sparse_attn_bwd(problem: Problem, plan_kv, plan_q, q, k, v, o, lse, dout, dq, dk, dv, workspace, stream=None):
+    """plan_kv: BWD plan (key ranges); plan_q: FWD plan (forward items, for dQ)."""
     nbytes = workspace.numel() * workspace.element_size()
-    _check(lib.sparse_attn_bwd(C.byref(problem.c), C.byref(plan.c), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
-                               _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), nbytes, _stream(stream)))
+    _check(lib.sparse_attn_bwd(C.byref(problem.c), C.byref(plan_kv.c), C.byref(plan_q.c), _ptr(q), _ptr(k), _ptr(v),
+                               _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), nbytes,
+                               _stream(stream)))

@@ -33,7 +33,9 @@ def hipcc() -> str:
 
 def _flags():
     return ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
-            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Wall", "-Wno-unused-function"]
+            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Wall", "-Wno-unused-function",
+            # MFMA results may live in arch VGPRs, so the softmax works on them in place
+            "-mllvm", "-amdgpu-mfma-vgpr-form"]
 
 
 def _compile(src: str) -> str:

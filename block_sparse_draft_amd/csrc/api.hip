@@ -16,7 +16,8 @@ int check_plan(const skv_plan* plan, int32_t kind) {
   if (plan->kind != kind) return fail(SKV_EPLAN, "plan kind %d does not match this call (%d)", plan->kind, kind);
   if (plan->n_workers < 1) return fail(SKV_EPLAN, "plan has %d workers", plan->n_workers);
   if (plan->n_items < 0) return fail(SKV_EPLAN, "plan has a negative item count");
-  if (!plan->d_worker_off || (plan->n_items > 0 && !plan->d_items)) return fail(SKV_EPLAN, "plan arrays are NULL");
+  if (!plan->d_worker_off || !plan->d_claim || (plan->n_items > 0 && !plan->d_items))
+    return fail(SKV_EPLAN, "plan arrays are NULL");
   return SKV_OK;
 }
 
@@ -47,12 +48,15 @@ extern "C" int sparse_attn_partial_fwd(const skv_problem* p, const skv_plan* pla
   a.q_st = p->q_stride_tok; a.q_sh = p->q_stride_head;
   a.kv_st = p->kv_stride_tok; a.kv_sh = p->kv_stride_head;
   a.q_off = p->d_q_off; a.kv_off = p->d_kv_off; a.anchor = p->d_anchor;
-  a.items = plan->d_items; a.worker_off = plan->d_worker_off;
+  a.items = plan->d_items; a.worker_off = plan->d_worker_off; a.claim = plan->d_claim;
   a.o_part = o_part; a.m_part = m_part; a.lse_part = lse_part;
   a.block = p->block; a.group = p->hq / p->hkv; a.hq = p->hq; a.chunk = p->chunk;
+  a.sm_scale = p->sm_scale;
   a.scale_log2 = p->sm_scale * kLog2e_host;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e = p->dtype == SKV_BF16 ? launch_fwd_bf16(a, plan->n_workers, st)
+  hipError_t e = launch_claim_reset(plan->d_claim, plan->n_workers, st);
+  if (e != hipSuccess) return hip_status(e, "sparse_attn_partial_fwd launch");
+  e = p->dtype == SKV_BF16 ? launch_fwd_bf16(a, plan->n_workers, st)
                                       : launch_fwd_f32(a, p->d, plan->n_workers, st);
   return hip_status(e, "sparse_attn_partial_fwd launch");
 }
@@ -83,39 +87,65 @@ extern "C" int lse_merge(int32_t n_part, int32_t hq, int64_t mq, int32_t d, cons
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-extern "C" size_t skv_bwd_workspace_bytes(const skv_problem* p) {
-  if (skv_check_problem(p)) return 0;
-  const size_t rows = (size_t)p->h_q_off[p->n_seq] * (size_t)p->hq;
-  return align256(rows * (size_t)p->d * sizeof(float)) + align256(rows * sizeof(float));
+// Workspace of sparse_attn_bwd: dQ partials (the forward's partial layout),
+// Delta, and the first partial row of each sequence.
+struct BwdWorkspace {
+  size_t dq_part, delta, part_base, total;
+};
+static BwdWorkspace bwd_workspace(const skv_problem* p) {
+  int64_t rows = 0;
+  for (int s = 0; s < p->n_seq; ++s) {
+    const SeqView v = seq_view(p, s);
+    rows += ceil_div(v.n, p->chunk) * p->hq * v.mq;
+  }
+  BwdWorkspace w;
+  w.dq_part = 0;
+  w.delta = align256((size_t)rows * (size_t)p->d * sizeof(float));
+  w.part_base = w.delta + align256((size_t)p->h_q_off[p->n_seq] * (size_t)p->hq * sizeof(float));
+  w.total = w.part_base + align256((size_t)(p->n_seq + 1) * sizeof(int64_t));
+  return w;
 }
 
-extern "C" int sparse_attn_bwd(const skv_problem* p, const skv_plan* plan, const void* q, const void* k, const void* v,
-                               const void* o, const float* lse, const void* dout, void* dq, void* dk, void* dv,
-                               void* workspace, size_t workspace_bytes, void* stream) {
+extern "C" size_t skv_bwd_workspace_bytes(const skv_problem* p) {
+  if (skv_check_problem(p)) return 0;
+  return bwd_workspace(p).total;
+}
+
+extern "C" int sparse_attn_bwd(const skv_problem* p, const skv_plan* plan_kv, const skv_plan* plan_q, const void* q,
+                               const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                               void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, void* stream) {
   int rc = skv_check_problem(p);
   if (rc) return rc;
   if (p->dtype != SKV_BF16) return fail(SKV_EDTYPE, "sparse_attn_bwd supports bf16 only");
   if ((rc = check_device_problem(p))) return rc;
-  if ((rc = check_plan(plan, SKV_ITEM_BWD))) return rc;
+  if ((rc = check_plan(plan_kv, SKV_ITEM_BWD))) return rc;
+  if ((rc = check_plan(plan_q, SKV_ITEM_FWD))) return rc;
+  if (plan_kv->d_claim == plan_q->d_claim) return fail(SKV_EPLAN, "the two plans must not share claim cursors");
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return fail(SKV_EINVAL, "tensor pointer is NULL");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) || !aligned16(dq))
     return fail(SKV_ESHAPE, "q, k, v, o, dout and dq must be 16-byte aligned");
-  const size_t need = skv_bwd_workspace_bytes(p);
-  if (!workspace || workspace_bytes < need)
-    return fail(SKV_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
+  const BwdWorkspace ws = bwd_workspace(p);
+  if (!workspace || workspace_bytes < ws.total)
+    return fail(SKV_EWORKSPACE, "workspace of %zu bytes needed, %zu given", ws.total, workspace_bytes);
   if (reinterpret_cast<uintptr_t>(workspace) & 255u) return fail(SKV_EWORKSPACE, "workspace must be 256-byte aligned");
-  const int64_t total_q = p->h_q_off[p->n_seq];
-  const size_t rows = (size_t)total_q * (size_t)p->hq;
+  char* w = static_cast<char*>(workspace);
   BwdArgs a{};
   a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.dout = dout; a.dq = dq; a.dk = dk; a.dv = dv;
-  a.dq_acc = static_cast<float*>(workspace);
-  a.delta = reinterpret_cast<float*>(static_cast<char*>(workspace) + align256(rows * (size_t)p->d * sizeof(float)));
+  a.dq_part = reinterpret_cast<float*>(w + ws.dq_part);
+  a.delta = reinterpret_cast<float*>(w + ws.delta);
+  a.part_base = reinterpret_cast<int64_t*>(w + ws.part_base);
   a.q_st = p->q_stride_tok; a.q_sh = p->q_stride_head;
   a.kv_st = p->kv_stride_tok; a.kv_sh = p->kv_stride_head;
   a.q_off = p->d_q_off; a.kv_off = p->d_kv_off; a.anchor = p->d_anchor;
-  a.items = plan->d_items; a.worker_off = plan->d_worker_off;
-  a.total_q = total_q;
-  a.block = p->block; a.group = p->hq / p->hkv; a.hq = p->hq; a.hkv = p->hkv;
+  a.kv_items = plan_kv->d_items; a.kv_worker_off = plan_kv->d_worker_off; a.kv_claim = plan_kv->d_claim;
+  a.q_items = plan_q->d_items; a.q_worker_off = plan_q->d_worker_off; a.q_claim = plan_q->d_claim;
+  a.total_q = p->h_q_off[p->n_seq];
+  a.n_seq = p->n_seq; a.block = p->block; a.group = p->hq / p->hkv; a.hq = p->hq; a.hkv = p->hkv;
+  a.chunk = p->chunk;
   a.sm_scale = p->sm_scale; a.scale_log2 = p->sm_scale * kLog2e_host;
-  return hip_status(launch_bwd_bf16(a, plan->n_workers, static_cast<hipStream_t>(stream)), "sparse_attn_bwd launch");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = launch_claim_reset(plan_kv->d_claim, plan_kv->n_workers, st);
+  if (e == hipSuccess) e = launch_claim_reset(plan_q->d_claim, plan_q->n_workers, st);
+  if (e == hipSuccess) e = launch_bwd_bf16(a, plan_kv->n_workers, plan_q->n_workers, st);
+  return hip_status(e, "sparse_attn_bwd launch");
 }

@@ -3,19 +3,28 @@
 // The merged log-sum-exp of the forward is reused, so P = exp(s - LSE) is
 // recomputed exactly without another softmax pass (pages: Split-KV article,
 // "Split-KV's Core Mechanism": the exact aggregation is what keeps gradients
-// correct).  Three launches on the caller's stream:
-//   1. preprocess: Delta = sum_x dO*O per (query row, head); zero the fp32 dQ
-//      accumulator.
-//   2. main (persistent workgroups over BWD items = (sequence, KV head, key
-//      range)): each workgroup owns 128 keys at a time (32 per wave), keeps
-//      their K, V operands and the dK, dV accumulators in registers, and
-//      walks the 64-row query tiles that see those keys.  Anchors are sorted,
-//      so the rows that see keys >= kb are the blocks with e_b > kb: a suffix.
-//      Per query tile:  S = Q K^T and dP = dO V^T (A from LDS), P and dS in
-//      registers, dV += P^T dO and dK += dS^T Q (B read transposed from LDS),
-//      dS^T staged in LDS, dQ += dS K split over the 4 waves and added to the
-//      fp32 accumulator with hardware float atomics.
-//   3. finalize: dQ = sm_scale * accumulator, rounded to bf16.
+// correct).  With dS = P * (dO.v - Delta), Delta = sum_x dO * O:
+//     dV_j = sum_rows P dO,   dK_j = scale * sum_rows dS q,   dQ = scale * dS K.
+//
+// Four launches on the caller's stream, none with atomics, so the result is
+// bitwise reproducible:
+//   1. preprocess: Delta per (query row, head), and the first partial row of
+//      every sequence (for the dQ partial layout).
+//   2. key-owner kernel (persistent workgroups over BWD items = (sequence, KV
+//      head, key range)): 128 keys at a time (32 per wave) with their K, V
+//      operands and fp32 dK, dV accumulators in registers, walking the 64-row
+//      query tiles that see those keys (anchors are sorted, so those rows are
+//      a suffix of the draft blocks); the next tile's Q, dO, LSE, Delta load
+//      while the current one is computed.  S = Q K^T, dP = dO V^T (A from
+//      LDS), P and dS in registers, dV += P^T dO and dK += dS^T Q (B read
+//      transposed from LDS).
+//   3. query-owner kernel over the forward's items (sequence, KV head, chunk,
+//      draft blocks), structured like the forward: 64 rows per wave with Q
+//      in registers and dO in LDS, K/V tiles of the chunk through two LDS
+//      buffers;
+//      S^T = K Q^T, dP^T = V dO^T, dS^T, then dQ^T += K^T dS^T.  Each item
+//      writes its chunk's dQ partial, like the forward's O partial.
+//   4. finalize: dQ = scale * sum of the row's visible chunk partials, bf16.
 #include "device.h"
 #include "launch.h"
 
@@ -23,10 +32,13 @@ namespace skv {
 namespace {
 
 constexpr int D = 128;
-constexpr int KT = 128;          // keys per workgroup tile (32 per wave)
-constexpr int QT = 64;           // query rows per tile
-constexpr int LDS_ROW = D + 8;   // bf16 per staged row of Q, dO, K (272 bytes)
-constexpr int DS_ROW = QT + 8;   // bf16 per staged key row of dS^T (144 bytes)
+constexpr int KT = 128;          // keys per key-owner workgroup tile (32 per wave)
+constexpr int QT = 64;           // query rows per query tile
+constexpr int LDS_ROW = D + 8;   // bf16 per staged row (272 bytes: conflict-free 16-byte reads)
+
+// ---------------------------------------------------------------------------
+// 1. preprocess
+// ---------------------------------------------------------------------------
 
 __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
   // 16 lanes per (row, head), 8 bf16 each.
@@ -49,39 +61,44 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
   }
   for (int o = 8; o > 0; o >>= 1) sum += __shfl_xor(sum, o, 16);
   if (ln == 0) a.delta[idx] = sum;
-  f32x4 z = {0.f, 0.f, 0.f, 0.f};
-  float* acc = a.dq_acc + idx * D + ln * 8;
-  *reinterpret_cast<f32x4*>(acc) = z;
-  *reinterpret_cast<f32x4*>(acc + 4) = z;
 }
 
-__global__ __launch_bounds__(256) void bwd_finalize_kernel(BwdArgs a) {
-  const int64_t idx = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
-  const int ln = threadIdx.x & 15;
-  if (idx >= a.total_q * a.hq) return;
-  const int64_t t = idx / a.hq;
-  const int h = (int)(idx % a.hq);
-  const float* acc = a.dq_acc + idx * D + ln * 8;
-  const f32x4 x0 = *reinterpret_cast<const f32x4*>(acc);
-  const f32x4 x1 = *reinterpret_cast<const f32x4*>(acc + 4);
-  uint4 pk;
-  pk.x = (uint32_t)f32_to_bf16_bits(a.sm_scale * x0[0]) | ((uint32_t)f32_to_bf16_bits(a.sm_scale * x0[1]) << 16);
-  pk.y = (uint32_t)f32_to_bf16_bits(a.sm_scale * x0[2]) | ((uint32_t)f32_to_bf16_bits(a.sm_scale * x0[3]) << 16);
-  pk.z = (uint32_t)f32_to_bf16_bits(a.sm_scale * x1[0]) | ((uint32_t)f32_to_bf16_bits(a.sm_scale * x1[1]) << 16);
-  pk.w = (uint32_t)f32_to_bf16_bits(a.sm_scale * x1[2]) | ((uint32_t)f32_to_bf16_bits(a.sm_scale * x1[3]) << 16);
-  *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.dq) + t * a.q_st + (int64_t)h * a.q_sh + ln * 8) = pk;
+// First partial row of every sequence: part_base[s] = sum_{s' < s} C_s' * hq * Mq_s'.
+__global__ void part_base_kernel(BwdArgs a) {
+  if (threadIdx.x != 0 || blockIdx.x != 0) return;
+  int64_t base = 0;
+  for (int s = 0; s < a.n_seq; ++s) {
+    a.part_base[s] = base;
+    const int64_t n = a.kv_off[s + 1] - a.kv_off[s];
+    base += (n + a.chunk - 1) / a.chunk * a.hq * (a.q_off[s + 1] - a.q_off[s]);
+  }
+  a.part_base[a.n_seq] = base;
 }
+
+// ---------------------------------------------------------------------------
+// 2. key-owner kernel: dK, dV
+// ---------------------------------------------------------------------------
+
+// Staging registers of one query tile (64 rows): each thread moves 4 x 16 bytes
+// of Q and of dO; threads 0..63 also carry their row's LSE, Delta and prefix end.
+struct QTileRegs {
+  uint4 q0, q1, q2, q3, o0, o1, o2, o3;
+  float lse, delta;
+  int end;
+};
+
+struct QTileMeta {
+  float lse[QT];     // LSE of each row, log2 units (+inf for padding rows: P = 0)
+  float delta[QT];
+  int end[QT];       // visible keys of the row inside this key tile: [kb, end)
+};
 
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void bwd_main_kernel(BwdArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t sK[KT * LDS_ROW];
-  __shared__ __attribute__((aligned(16))) uint16_t sQ[QT * LDS_ROW];
-  __shared__ __attribute__((aligned(16))) uint16_t sdO[QT * LDS_ROW];
-  __shared__ __attribute__((aligned(16))) uint16_t sdS[KT * DS_ROW];
-  __shared__ __attribute__((aligned(16))) float sLse[QT];
-  __shared__ __attribute__((aligned(16))) float sDelta[QT];
-  __shared__ __attribute__((aligned(16))) int sEnd[QT];
-  __shared__ int64_t sAcc[QT];  // dq_acc row of each query row, -1 if none
+void bwd_kv_kernel(BwdArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t sQ[2][QT * LDS_ROW];
+  __shared__ __attribute__((aligned(16))) uint16_t sdO[2][QT * LDS_ROW];
+  __shared__ __attribute__((aligned(16))) QTileMeta sMeta[2];
+  __shared__ int s_claim;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -94,16 +111,21 @@ void bwd_main_kernel(BwdArgs a) {
   uint16_t* dK = static_cast<uint16_t*>(a.dk);
   uint16_t* dV = static_cast<uint16_t*>(a.dv);
   const int GB = a.group * a.block;
+  const float c = a.scale_log2;
 
-  const int64_t slot_end = a.worker_off[blockIdx.x + 1];
-  for (int64_t slot = a.worker_off[blockIdx.x]; slot < slot_end; ++slot) {
-    const skv_item it = a.items[slot];
+  int victim = plan_worker(), visited = 0;
+  for (;;) {
+    const int64_t slot = claim_next(a.kv_worker_off, a.kv_claim, victim, visited, &s_claim);
+    if (slot < 0) break;
+    const skv_item it = a.kv_items[slot];
     const int s = it.seq, g = it.kv_head;
     const int64_t q0 = a.q_off[s];
     const int64_t k0 = a.kv_off[s];
     const int n_ctx = (int)(a.kv_off[s + 1] - k0);
     const int64_t blk0 = q0 / a.block;
     const int n_blk = (int)((a.q_off[s + 1] - q0) / a.block);
+    const uint16_t* Kseq = K + k0 * a.kv_st + (int64_t)g * a.kv_sh;
+    const uint16_t* Vseq = V + k0 * a.kv_st + (int64_t)g * a.kv_sh;
 
     for (int kb = it.lo; kb < it.hi; kb += KT) {
       const int kend = min(it.hi, kb + KT);
@@ -111,174 +133,165 @@ void bwd_main_kernel(BwdArgs a) {
       int b_first = 0;
       for (int b0 = 0; b0 < n_blk; b0 += 64) {
         const int b = b0 + lane;
-        const bool blind = b < n_blk && min(a.anchor[blk0 + b] + a.block, n_ctx) <= kb;
+        bool blind = false;
+        if (b < n_blk) blind = min(a.anchor[blk0 + b] + a.block, n_ctx) <= kb;
         b_first += __popcll(__ballot(blind));
       }
       const int nq = (n_blk - b_first) * GB;
+      const int ntq = (nq + QT - 1) / QT;
 
-      // This wave's 32 keys: K and V rows as MFMA B operands (k = head dim).
+      // Query tile loader: rows p = qt*64 + row of the visible suffix, packed
+      // block-major like the forward; padding rows read the last row and are masked.
+      auto load_q = [&](int qt) {
+        QTileRegs r;
+        const int row = tid >> 4;
+        const int64_t d8 = (tid & 15) * 8;
+        int64_t off[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int p = min(qt * QT + row + 16 * u, nq - 1);
+          const int b = b_first + p / GB;
+          const int h = g * a.group + (p / a.block) % a.group;
+          const int64_t t = q0 + (int64_t)b * a.block + p % a.block;
+          off[u] = t * a.q_st + (int64_t)h * a.q_sh + d8;
+        }
+        r.q0 = *reinterpret_cast<const uint4*>(Q + off[0]);
+        r.q1 = *reinterpret_cast<const uint4*>(Q + off[1]);
+        r.q2 = *reinterpret_cast<const uint4*>(Q + off[2]);
+        r.q3 = *reinterpret_cast<const uint4*>(Q + off[3]);
+        r.o0 = *reinterpret_cast<const uint4*>(dO + off[0]);
+        r.o1 = *reinterpret_cast<const uint4*>(dO + off[1]);
+        r.o2 = *reinterpret_cast<const uint4*>(dO + off[2]);
+        r.o3 = *reinterpret_cast<const uint4*>(dO + off[3]);
+        r.lse = INFINITY; r.delta = 0.f; r.end = kb;
+        if (tid < QT) {
+          const int p = qt * QT + tid;
+          const int pc = min(p, nq - 1);
+          const int b = b_first + pc / GB;
+          const int h = g * a.group + (pc / a.block) % a.group;
+          const int64_t rr = (q0 + (int64_t)b * a.block + pc % a.block) * a.hq + h;
+          const float lse = a.lse[rr];
+          const float del = a.delta[rr];
+          const int e = min(a.anchor[blk0 + b] + a.block, n_ctx);
+          if (p < nq) { r.lse = lse * kLog2e; r.delta = del; r.end = min(e, kend); }
+        }
+        return r;
+      };
+      auto store_q = [&](const QTileRegs& r, int buf) {
+        const int o = (tid >> 4) * LDS_ROW + (tid & 15) * 8;
+        constexpr int R16 = 16 * LDS_ROW;
+        uint16_t* q = sQ[buf];
+        uint16_t* d = sdO[buf];
+        *reinterpret_cast<uint4*>(q + o) = r.q0;
+        *reinterpret_cast<uint4*>(q + o + R16) = r.q1;
+        *reinterpret_cast<uint4*>(q + o + 2 * R16) = r.q2;
+        *reinterpret_cast<uint4*>(q + o + 3 * R16) = r.q3;
+        *reinterpret_cast<uint4*>(d + o) = r.o0;
+        *reinterpret_cast<uint4*>(d + o + R16) = r.o1;
+        *reinterpret_cast<uint4*>(d + o + 2 * R16) = r.o2;
+        *reinterpret_cast<uint4*>(d + o + 3 * R16) = r.o3;
+        if (tid < QT) {
+          sMeta[buf].lse[tid] = r.lse;
+          sMeta[buf].delta[tid] = r.delta;
+          sMeta[buf].end[tid] = r.end;
+        }
+      };
+
+      // This wave's 32 keys as MFMA B operands (k = head dim); keys past the
+      // context are clamped to its last key and masked.
       const int key_w = kb + wave * 32 + l32;
       bf16x8 kreg[8], vreg[8];
       {
-        const bool in = key_w < n_ctx;
-        const uint16_t* kp = K + (k0 + key_w) * a.kv_st + (int64_t)g * a.kv_sh + hf * 8;
-        const uint16_t* vp = V + (k0 + key_w) * a.kv_st + (int64_t)g * a.kv_sh + hf * 8;
+        const int kc = min(key_w, n_ctx - 1);
+        const uint16_t* kp = Kseq + (int64_t)kc * a.kv_st + hf * 8;
+        const uint16_t* vp = Vseq + (int64_t)kc * a.kv_st + hf * 8;
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) {
-          kreg[ks] = in ? load_bf16x8(kp + ks * 16) : bf16x8{};
-          vreg[ks] = in ? load_bf16x8(vp + ks * 16) : bf16x8{};
+          kreg[ks] = load_bf16x8(kp + ks * 16);
+          vreg[ks] = load_bf16x8(vp + ks * 16);
         }
       }
       f32x16 dk_acc[4], dv_acc[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) dk_acc[i] = dv_acc[i] = f32x16{};
 
-      if (nq > 0) {
-        __syncthreads();  // previous users of sK are done
-        // K tile [kb, kb + 128) for the dQ product
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int ci = tid + 256 * u;
-          const int key = ci >> 4, dc = ci & 15;
-          uint4 kx = {0, 0, 0, 0};
-          if (kb + key < n_ctx)
-            kx = *reinterpret_cast<const uint4*>(K + (k0 + kb + key) * a.kv_st + (int64_t)g * a.kv_sh + dc * 8);
-          *reinterpret_cast<uint4*>(&sK[key * LDS_ROW + dc * 8]) = kx;
-        }
-      }
+      if (ntq > 0) {
+        QTileRegs R = load_q(0);
+        __syncthreads();  // previous users of the query buffers are done
+        store_q(R, 0);
+        // Drain every load before the prefetch starts, so that inside the loop
+        // only the prefetch is in flight and the MFMA phase never waits on it.
+        __builtin_amdgcn_s_waitcnt(0);
+        if (ntq > 1) R = load_q(1);
 
-      for (int qt = 0; qt < nq; qt += QT) {
-        __syncthreads();  // sQ, sdO, sdS of the previous tile consumed
-        // ---- stage the query tile: Q, dO rows, LSE (log2 units), Delta, prefix end ----
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int ci = tid + 256 * u;
-          const int row = ci >> 4, dc = ci & 15;
-          const int p = qt + row;
-          uint4 qx = {0, 0, 0, 0}, ox = {0, 0, 0, 0};
-          if (p < nq) {
-            const int b = b_first + p / GB;
-            const int h = g * a.group + (p / a.block) % a.group;
-            const int64_t t = q0 + (int64_t)b * a.block + p % a.block;
-            qx = *reinterpret_cast<const uint4*>(Q + t * a.q_st + (int64_t)h * a.q_sh + dc * 8);
-            ox = *reinterpret_cast<const uint4*>(dO + t * a.q_st + (int64_t)h * a.q_sh + dc * 8);
+        for (int qt = 0; qt < ntq; ++qt) {
+          const int buf = qt & 1;
+          if (qt > 0) {
+            store_q(R, buf);                       // tile qt, loaded during tile qt-1
+            if (qt + 1 < ntq) R = load_q(qt + 1);  // in flight during this tile
           }
-          *reinterpret_cast<uint4*>(&sQ[row * LDS_ROW + dc * 8]) = qx;
-          *reinterpret_cast<uint4*>(&sdO[row * LDS_ROW + dc * 8]) = ox;
-        }
-        if (tid < QT) {
-          const int p = qt + tid;
-          if (p < nq) {
-            const int b = b_first + p / GB;
-            const int h = g * a.group + (p / a.block) % a.group;
-            const int64_t t = q0 + (int64_t)b * a.block + p % a.block;
-            const int64_t r = t * a.hq + h;
-            sLse[tid] = a.lse[r] * kLog2e;
-            sDelta[tid] = a.delta[r];
-            sEnd[tid] = min(min(a.anchor[blk0 + b] + a.block, n_ctx), kend);
-            sAcc[tid] = r;
-          } else {
-            sLse[tid] = INFINITY;  // P = 0
-            sDelta[tid] = 0.f;
-            sEnd[tid] = 0;
-            sAcc[tid] = -1;
-          }
-        }
-        __syncthreads();
+          // Two buffers suffice: the buffer written above was last read before
+          // the previous iteration's barrier.
+          __syncthreads();
+          const uint16_t* bq = sQ[buf];
+          const uint16_t* bo = sdO[buf];
+          const QTileMeta& M = sMeta[buf];
 
-        // ---- S = Q K^T and dP = dO V^T for 64 rows x this wave's 32 keys ----
-        f32x16 sacc[2], pacc[2];
-        sacc[0] = sacc[1] = pacc[0] = pacc[1] = f32x16{};
+          // ---- S = Q K^T and dP = dO V^T for 64 rows x this wave's 32 keys ----
+          f32x16 sacc[2], pacc[2];
+          sacc[0] = sacc[1] = pacc[0] = pacc[1] = f32x16{};
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
+          for (int ks = 0; ks < 8; ++ks) {
 #pragma unroll
-          for (int mt = 0; mt < 2; ++mt) {
-            const bf16x8 qa = lds_load_bf16x8(&sQ[(mt * 32 + l32) * LDS_ROW + ks * 16 + hf * 8]);
-            const bf16x8 oa = lds_load_bf16x8(&sdO[(mt * 32 + l32) * LDS_ROW + ks * 16 + hf * 8]);
-            sacc[mt] = mfma32x32x16(qa, kreg[ks], sacc[mt]);
-            pacc[mt] = mfma32x32x16(oa, vreg[ks], pacc[mt]);
-          }
-        }
-        // ---- P = exp2(s*log2e*scale - LSE2) on visible entries, dS = P (dP - Delta) ----
-        // lane holds key key_w, rows mt*32 + 8i + 4hf + j (element 4i + j)
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int r0 = mt * 32 + 8 * i + 4 * hf;
-            const f32x4 lse4 = *reinterpret_cast<const f32x4*>(&sLse[r0]);
-            const f32x4 del4 = *reinterpret_cast<const f32x4*>(&sDelta[r0]);
-            const int4 end4 = *reinterpret_cast<const int4*>(&sEnd[r0]);
-            const int ends[4] = {end4.x, end4.y, end4.z, end4.w};
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const int e = 4 * i + j;
-              float p = fast_exp2(sacc[mt][e] * a.scale_log2 - lse4[j]);
-              if (key_w >= ends[j]) p = 0.f;
-              sacc[mt][e] = p;
-              pacc[mt][e] = p * (pacc[mt][e] - del4[j]);
+            for (int mt = 0; mt < 2; ++mt) {
+              const bf16x8 qa = lds_load_bf16x8(bq + (mt * 32 + l32) * LDS_ROW + ks * 16 + hf * 8);
+              const bf16x8 oa = lds_load_bf16x8(bo + (mt * 32 + l32) * LDS_ROW + ks * 16 + hf * 8);
+              sacc[mt] = mfma32x32x16(qa, kreg[ks], sacc[mt]);
+              pacc[mt] = mfma32x32x16(oa, vreg[ks], pacc[mt]);
             }
           }
-        }
-        // ---- dV += P^T dO, dK += dS^T Q (A from registers, B transposed from LDS) ----
+          // ---- P = exp2(s*c - LSE2) on visible entries, dS = P (dP - Delta) ----
+          // lane holds key key_w, rows mt*32 + 8i + 4hf + j (element 4i + j)
 #pragma unroll
-        for (int kstep = 0; kstep < 4; ++kstep) {
-          const int mt = kstep >> 1, qh = (kstep & 1) * 8;
-          const f32x16& ps = sacc[mt];
-          const f32x16& ds = pacc[mt];
-          const bf16x8 pa = to_bf16x8(ps[qh], ps[qh + 1], ps[qh + 2], ps[qh + 3], ps[qh + 4], ps[qh + 5], ps[qh + 6],
-                                      ps[qh + 7]);
-          const bf16x8 da = to_bf16x8(ds[qh], ds[qh + 1], ds[qh + 2], ds[qh + 3], ds[qh + 4], ds[qh + 5], ds[qh + 6],
-                                      ds[qh + 7]);
-          const int row0 = kstep * 16 + 4 * hf + (li >> 2);
-#pragma unroll
-          for (int nd = 0; nd < 4; ++nd) {
-            const int col = nd * 32 + 16 * (gi & 1) + 4 * (li & 3);
-            const bf16x8 ob = lds_tr_pair(&sdO[row0 * LDS_ROW + col], &sdO[(row0 + 8) * LDS_ROW + col]);
-            const bf16x8 qb = lds_tr_pair(&sQ[row0 * LDS_ROW + col], &sQ[(row0 + 8) * LDS_ROW + col]);
-            dv_acc[nd] = mfma32x32x16(pa, ob, dv_acc[nd]);
-            dk_acc[nd] = mfma32x32x16(da, qb, dk_acc[nd]);
-          }
-        }
-        // ---- stage dS^T (bf16) in LDS: row key, columns = query rows ----
-        {
-          const int krow = wave * 32 + l32;
-#pragma unroll
-          for (int mt = 0; mt < 2; ++mt)
+          for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              const f32x16& ds = pacc[mt];
-              uint2 pk;
-              pk.x = (uint32_t)f32_to_bf16_bits(ds[4 * i]) | ((uint32_t)f32_to_bf16_bits(ds[4 * i + 1]) << 16);
-              pk.y = (uint32_t)f32_to_bf16_bits(ds[4 * i + 2]) | ((uint32_t)f32_to_bf16_bits(ds[4 * i + 3]) << 16);
-              *reinterpret_cast<uint2*>(&sdS[krow * DS_ROW + mt * 32 + 8 * i + 4 * hf]) = pk;
+              const int r0 = mt * 32 + 8 * i + 4 * hf;
+              const f32x4 lse4 = *reinterpret_cast<const f32x4*>(&M.lse[r0]);
+              const f32x4 del4 = *reinterpret_cast<const f32x4*>(&M.delta[r0]);
+              const int4 end4 = *reinterpret_cast<const int4*>(&M.end[r0]);
+              const int ends[4] = {end4.x, end4.y, end4.z, end4.w};
+#pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                const int e = 4 * i + j;
+                float p = fast_exp2(__builtin_fmaf(sacc[mt][e], c, -lse4[j]));
+                if (key_w >= ends[j]) p = 0.f;
+                sacc[mt][e] = p;
+                pacc[mt][e] = p * (pacc[mt][e] - del4[j]);
+              }
             }
-        }
-        __syncthreads();
-        // ---- dQ (64 rows x 32 head dims of this wave) += dS K over the 128 keys ----
-        f32x16 qacc[2];
-        qacc[0] = qacc[1] = f32x16{};
+          }
+          // ---- dV += P^T dO, dK += dS^T Q (A from registers, B transposed from LDS) ----
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-          const int key0 = ks * 16 + 4 * hf + (li >> 2);
-          const int kcol = wave * 32 + 16 * (gi & 1) + 4 * (li & 3);
-          const bf16x8 kb8 = lds_tr_pair(&sK[key0 * LDS_ROW + kcol], &sK[(key0 + 8) * LDS_ROW + kcol]);
+          for (int kstep = 0; kstep < 4; ++kstep) {
+            const int mt = kstep >> 1, qh = (kstep & 1) * 8;
+            const f32x16& ps = sacc[mt];
+            const f32x16& ds = pacc[mt];
+            const bf16x8 pa = to_bf16x8(ps[qh], ps[qh + 1], ps[qh + 2], ps[qh + 3], ps[qh + 4], ps[qh + 5],
+                                        ps[qh + 6], ps[qh + 7]);
+            const bf16x8 da = to_bf16x8(ds[qh], ds[qh + 1], ds[qh + 2], ds[qh + 3], ds[qh + 4], ds[qh + 5],
+                                        ds[qh + 6], ds[qh + 7]);
+            const int row0 = kstep * 16 + 4 * hf + (li >> 2);
 #pragma unroll
-          for (int mt = 0; mt < 2; ++mt) {
-            const int rcol = mt * 32 + 16 * (gi & 1) + 4 * (li & 3);
-            const bf16x8 da = lds_tr_pair(&sdS[key0 * DS_ROW + rcol], &sdS[(key0 + 8) * DS_ROW + rcol]);
-            qacc[mt] = mfma32x32x16(da, kb8, qacc[mt]);
+            for (int nd = 0; nd < 4; ++nd) {
+              const int col = nd * 32 + 16 * (gi & 1) + 4 * (li & 3);
+              const bf16x8 ob = lds_tr_pair(bo + row0 * LDS_ROW + col, bo + (row0 + 8) * LDS_ROW + col);
+              const bf16x8 qb = lds_tr_pair(bq + row0 * LDS_ROW + col, bq + (row0 + 8) * LDS_ROW + col);
+              dv_acc[nd] = mfma32x32x16(pa, ob, dv_acc[nd]);
+              dk_acc[nd] = mfma32x32x16(da, qb, dk_acc[nd]);
+            }
           }
         }
-        // lane holds head dim wave*32 + l32 of rows mt*32 + 8i + 4hf + j
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int row = mt * 32 + (e >> 2) * 8 + 4 * hf + (e & 3);
-            const int64_t r = sAcc[row];
-            if (r >= 0) unsafeAtomicAdd(a.dq_acc + r * D + wave * 32 + l32, qacc[mt][e]);
-          }
       }
 
       // ---- write dK (scaled) and dV for the keys of this tile inside the item ----
@@ -297,19 +310,271 @@ void bwd_main_kernel(BwdArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// 3. query-owner kernel: per-chunk dQ partials
+// ---------------------------------------------------------------------------
+
+constexpr int KT2 = 64;                 // keys per tile of the query-owner kernel
+constexpr int TILE_ELEMS = KT2 * LDS_ROW;
+
+struct KVTileRegs {
+  uint4 k0, k1, k2, k3, v0, v1, v2, v3;
+};
+
+__device__ __forceinline__ KVTileRegs load_kv_tile(const uint16_t* Kseq, const uint16_t* Vseq, int kb, int n_ctx,
+                                                   int64_t kv_st, int tid) {
+  KVTileRegs r;
+  const int64_t d8 = (tid & 15) * 8;
+  const int row = tid >> 4;
+  const int64_t o0 = (int64_t)min(kb + row, n_ctx - 1) * kv_st + d8;
+  const int64_t o1 = (int64_t)min(kb + row + 16, n_ctx - 1) * kv_st + d8;
+  const int64_t o2 = (int64_t)min(kb + row + 32, n_ctx - 1) * kv_st + d8;
+  const int64_t o3 = (int64_t)min(kb + row + 48, n_ctx - 1) * kv_st + d8;
+  r.k0 = *reinterpret_cast<const uint4*>(Kseq + o0);
+  r.k1 = *reinterpret_cast<const uint4*>(Kseq + o1);
+  r.k2 = *reinterpret_cast<const uint4*>(Kseq + o2);
+  r.k3 = *reinterpret_cast<const uint4*>(Kseq + o3);
+  r.v0 = *reinterpret_cast<const uint4*>(Vseq + o0);
+  r.v1 = *reinterpret_cast<const uint4*>(Vseq + o1);
+  r.v2 = *reinterpret_cast<const uint4*>(Vseq + o2);
+  r.v3 = *reinterpret_cast<const uint4*>(Vseq + o3);
+  return r;
+}
+
+__device__ __forceinline__ void store_kv_tile(KVTileRegs r, uint16_t* sK, uint16_t* sV, int tid) {
+  const int o = (tid >> 4) * LDS_ROW + (tid & 15) * 8;
+  constexpr int R16 = 16 * LDS_ROW;
+  *reinterpret_cast<uint4*>(sK + o) = r.k0;
+  *reinterpret_cast<uint4*>(sK + o + R16) = r.k1;
+  *reinterpret_cast<uint4*>(sK + o + 2 * R16) = r.k2;
+  *reinterpret_cast<uint4*>(sK + o + 3 * R16) = r.k3;
+  *reinterpret_cast<uint4*>(sV + o) = r.v0;
+  *reinterpret_cast<uint4*>(sV + o + R16) = r.v1;
+  *reinterpret_cast<uint4*>(sV + o + 2 * R16) = r.v2;
+  *reinterpret_cast<uint4*>(sV + o + 3 * R16) = r.v3;
+}
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void bwd_dq_kernel(BwdArgs a) {
+  // Two K/V buffers: tile t+1 is stored after the barrier that ends tile t-1,
+  // so one barrier per tile suffices.  dO rows of the pass live in LDS.
+  __shared__ __attribute__((aligned(16))) uint16_t sKV[2][2][TILE_ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t sdO[256 * LDS_ROW];
+  __shared__ int s_claim;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hf = lane >> 5;
+  const int gi = lane >> 4, li = lane & 15;
+  const uint16_t* Q = static_cast<const uint16_t*>(a.q);
+  const uint16_t* K = static_cast<const uint16_t*>(a.k);
+  const uint16_t* V = static_cast<const uint16_t*>(a.v);
+  const uint16_t* dO = static_cast<const uint16_t*>(a.dout);
+  const int GB = a.group * a.block;
+  const float c = a.scale_log2;
+  const uint16_t* my_dO = sdO + (wave * 64 + l32) * LDS_ROW + hf * 8;  // this lane's row, nt = 0
+
+  int victim = plan_worker(), visited = 0;
+  for (;;) {
+    const int64_t slot = claim_next(a.q_worker_off, a.q_claim, victim, visited, &s_claim);
+    if (slot < 0) break;
+    const skv_item it = a.q_items[slot];
+    const int s = it.seq;
+    const int64_t q0 = a.q_off[s];
+    const int64_t mq = a.q_off[s + 1] - q0;
+    const int64_t k0 = a.kv_off[s];
+    const int n_ctx = (int)(a.kv_off[s + 1] - k0);
+    const int64_t blk0 = q0 / a.block;
+    const int klo = it.chunk * a.chunk;
+    const int khi = min(klo + a.chunk, n_ctx);
+    const int nrows = (it.hi - it.lo) * GB;
+    const uint16_t* Kseq = K + k0 * a.kv_st + (int64_t)it.kv_head * a.kv_sh;
+    const uint16_t* Vseq = V + k0 * a.kv_st + (int64_t)it.kv_head * a.kv_sh;
+
+    for (int rt = 0; rt < nrows; rt += 256) {
+      const int p_last = min(nrows, rt + 256) - 1;
+      const int wg_hi = max(klo, min(khi, min(a.anchor[blk0 + it.lo + p_last / GB] + a.block, n_ctx)));
+      const int ntiles = (wg_hi - klo + KT2 - 1) / KT2;
+      if (ntiles == 0) continue;  // no row of the pass sees the chunk: no partial to write
+
+      __syncthreads();  // all waves are done with the previous pass's buffers (K/V and dO)
+      KVTileRegs R = load_kv_tile(Kseq, Vseq, klo, n_ctx, a.kv_st, tid);
+      // ---- this lane's two rows: Q as MFMA B operand, LSE, Delta; dO rows to LDS ----
+      int vend[2];
+      int64_t prow[2];
+      bool valid[2];
+      float lse2[2], del[2];
+      bf16x8 qf[2][8];
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const int p = rt + wave * 64 + nt * 32 + l32;
+        valid[nt] = p < nrows;
+        const int pc = valid[nt] ? p : p_last;
+        const int b = it.lo + pc / GB;
+        const int hl = (pc / a.block) % a.group;
+        const int64_t r = (int64_t)b * a.block + pc % a.block;
+        const int h = it.kv_head * a.group + hl;
+        const int e = min(a.anchor[blk0 + b] + a.block, n_ctx);
+        vend[nt] = valid[nt] ? max(klo, min(khi, e)) : klo;
+        prow[nt] = it.part_base + (int64_t)h * mq + r;
+        const int64_t qrow = (q0 + r) * a.q_st + (int64_t)h * a.q_sh + hf * 8;
+        lse2[nt] = a.lse[(q0 + r) * a.hq + h] * kLog2e;
+        del[nt] = a.delta[(q0 + r) * a.hq + h];
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) qf[nt][ks] = load_bf16x8(Q + qrow + ks * 16);
+      }
+      // dO of the pass's 256 rows: thread (row tid>>4 + 16u, 16-byte column tid&15)
+      uint4 dox[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const int p = min(rt + (tid >> 4) + 16 * u, p_last);
+        const int b = it.lo + p / GB;
+        const int h = it.kv_head * a.group + (p / a.block) % a.group;
+        const int64_t t = q0 + (int64_t)b * a.block + p % a.block;
+        dox[u] = *reinterpret_cast<const uint4*>(dO + t * a.q_st + (int64_t)h * a.q_sh + (tid & 15) * 8);
+      }
+#pragma unroll
+      for (int u = 0; u < 16; ++u)
+        *reinterpret_cast<uint4*>(sdO + ((tid >> 4) + 16 * u) * LDS_ROW + (tid & 15) * 8) = dox[u];
+      store_kv_tile(R, sKV[0][0], sKV[0][1], tid);
+      __builtin_amdgcn_s_waitcnt(0);  // drain before the prefetch (see the forward kernel)
+      if (ntiles > 1) R = load_kv_tile(Kseq, Vseq, klo + KT2, n_ctx, a.kv_st, tid);
+      const int wave_hi = wave_max_i(max(vend[0], vend[1]));
+      const int wave_full = wave_min_i(min(valid[0] ? vend[0] : INT32_MAX, valid[1] ? vend[1] : INT32_MAX));
+
+      f32x16 acc[4][2];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i][0] = acc[i][1] = f32x16{};
+
+      for (int t = 0; t < ntiles; ++t) {
+        const int kb = klo + t * KT2;
+        __syncthreads();  // tile t visible; every wave is done with tile t-1's buffer
+        if (t + 1 < ntiles) {
+          store_kv_tile(R, sKV[(t + 1) & 1][0], sKV[(t + 1) & 1][1], tid);
+          if (t + 2 < ntiles) R = load_kv_tile(Kseq, Vseq, kb + 2 * KT2, n_ctx, a.kv_st, tid);
+        }
+        if (kb >= wave_hi) continue;
+        const uint16_t* sK = sKV[t & 1][0];
+        const uint16_t* sV = sKV[t & 1][1];
+
+        const bool need_mask = kb + KT2 > wave_full;
+        // The 64 keys are handled as two halves of 32 (mt), which halves the
+        // live S^T / dP^T accumulators without re-reading any operand.
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+          // ---- S^T = K Q^T and dP^T = V dO^T for keys mt*32 .. +32 ----
+          f32x16 sacc[2], pacc[2];
+          sacc[0] = sacc[1] = pacc[0] = pacc[1] = f32x16{};
+#pragma unroll
+          for (int ks = 0; ks < 8; ++ks) {
+            const bf16x8 kf = lds_load_bf16x8(sK + (mt * 32 + l32) * LDS_ROW + ks * 16 + hf * 8);
+            const bf16x8 vf = lds_load_bf16x8(sV + (mt * 32 + l32) * LDS_ROW + ks * 16 + hf * 8);
+            sacc[0] = mfma32x32x16(kf, qf[0][ks], sacc[0]);
+            sacc[1] = mfma32x32x16(kf, qf[1][ks], sacc[1]);
+            pacc[0] = mfma32x32x16(vf, lds_load_bf16x8(my_dO + ks * 16), pacc[0]);
+            pacc[1] = mfma32x32x16(vf, lds_load_bf16x8(my_dO + 32 * LDS_ROW + ks * 16), pacc[1]);
+          }
+          // ---- dS^T = P^T (dP^T - Delta), P^T = exp2(s*c - LSE2) on visible keys ----
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+              float p = fast_exp2(__builtin_fmaf(sacc[nt][e], c, -lse2[nt]));
+              if (need_mask) {
+                const int key = kb + mt * 32 + (e >> 2) * 8 + hf * 4 + (e & 3);
+                if (key >= vend[nt]) p = 0.f;
+              }
+              sacc[nt][e] = p * (pacc[nt][e] - del[nt]);
+            }
+          // ---- dQ^T += K^T dS^T over these 32 keys (K^T read transposed from LDS) ----
+#pragma unroll
+          for (int half = 0; half < 2; ++half) {
+            const int qh = half * 8;
+            bf16x8 df[2];
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) {
+              const f32x16& sv = sacc[nt];
+              df[nt] = to_bf16x8(sv[qh + 0], sv[qh + 1], sv[qh + 2], sv[qh + 3], sv[qh + 4], sv[qh + 5],
+                                 sv[qh + 6], sv[qh + 7]);
+            }
+            const int key0 = (2 * mt + half) * 16 + 4 * hf + (li >> 2);
+#pragma unroll
+            for (int md = 0; md < 4; ++md) {
+              const int col = md * 32 + 16 * (gi & 1) + 4 * (li & 3);
+              const bf16x8 kt = lds_tr_pair(sK + key0 * LDS_ROW + col, sK + (key0 + 8) * LDS_ROW + col);
+              acc[md][0] = mfma32x32x16(kt, df[0], acc[md][0]);
+              acc[md][1] = mfma32x32x16(kt, df[1], acc[md][1]);
+            }
+          }
+        }
+      }
+
+      // ---- the chunk's dQ partial (unscaled) for rows that see the chunk ----
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        if (!valid[nt] || vend[nt] <= klo) continue;
+        float* op = a.dq_part + prow[nt] * D + hf * 4;
+#pragma unroll
+        for (int md = 0; md < 4; ++md)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            f32x4 v4 = {acc[md][nt][4 * i + 0], acc[md][nt][4 * i + 1], acc[md][nt][4 * i + 2],
+                        acc[md][nt][4 * i + 3]};
+            *reinterpret_cast<f32x4*>(op + md * 32 + 8 * i) = v4;
+          }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 4. finalize: dQ = scale * sum of visible chunk partials
+// ---------------------------------------------------------------------------
+
+__global__ __launch_bounds__(256) void bwd_finalize_kernel(BwdArgs a) {
+  // 32 lanes per (row, head), 4 fp32 each.
+  const int64_t idx = (int64_t)blockIdx.x * 8 + (threadIdx.x >> 5);
+  const int ln = threadIdx.x & 31;
+  if (idx >= a.total_q * a.hq) return;
+  const int64_t t = idx / a.hq;
+  const int h = (int)(idx % a.hq);
+  int lo = 0, hi = a.n_seq;  // sequence of token t: q_off[s] <= t < q_off[s+1]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (a.q_off[mid] <= t) lo = mid; else hi = mid;
+  }
+  const int s = lo;
+  const int64_t q0 = a.q_off[s], mq = a.q_off[s + 1] - q0;
+  const int64_t r = t - q0;
+  const int n_ctx = (int)(a.kv_off[s + 1] - a.kv_off[s]);
+  const int e = min(a.anchor[q0 / a.block + r / a.block] + a.block, n_ctx);
+  const int nc = (e + a.chunk - 1) / a.chunk;  // chunks the row sees
+  const float* src = a.dq_part + (a.part_base[s] + (int64_t)h * mq + r) * D + ln * 4;
+  const int64_t cstride = (int64_t)a.hq * mq * D;
+  f32x4 sum = {0.f, 0.f, 0.f, 0.f};
+  for (int cc = 0; cc < nc; ++cc) sum += *reinterpret_cast<const f32x4*>(src + cc * cstride);
+  uint2 pk;
+  pk.x = (uint32_t)f32_to_bf16_bits(a.sm_scale * sum[0]) | ((uint32_t)f32_to_bf16_bits(a.sm_scale * sum[1]) << 16);
+  pk.y = (uint32_t)f32_to_bf16_bits(a.sm_scale * sum[2]) | ((uint32_t)f32_to_bf16_bits(a.sm_scale * sum[3]) << 16);
+  *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.dq) + t * a.q_st + (int64_t)h * a.q_sh + ln * 4) = pk;
+}
+
 }  // namespace
 
-hipError_t launch_bwd_bf16(const BwdArgs& a, int n_workers, hipStream_t stream) {
+hipError_t launch_bwd_bf16(const BwdArgs& a, int kv_workers, int q_workers, hipStream_t stream) {
   const int64_t rows = a.total_q * a.hq;
+  hipLaunchKernelGGL(part_base_kernel, dim3(1), dim3(64), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   if (rows > 0) {
     hipLaunchKernelGGL(bwd_pre_kernel, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, stream, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(bwd_main_kernel, dim3(n_workers), dim3(256), 0, stream, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || rows == 0) return e;
-  hipLaunchKernelGGL(bwd_finalize_kernel, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(bwd_kv_kernel, dim3(kv_workers), dim3(256), 0, stream, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(bwd_dq_kernel, dim3(q_workers), dim3(256), 0, stream, a);
+  if ((e = hipGetLastError()) != hipSuccess || rows == 0) return e;
+  hipLaunchKernelGGL(bwd_finalize_kernel, dim3((unsigned)((rows + 7) / 8)), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

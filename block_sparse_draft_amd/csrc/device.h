@@ -79,4 +79,32 @@ __device__ __forceinline__ int wave_min_i(int x) {
   return x;
 }
 
+// Worker index of this workgroup.  Workgroups are dispatched to the 8 XCDs
+// round-robin, so consecutive plan workers (consecutive items of one chunk
+// under LPT) are mapped to workgroups of the same XCD and share its L2.
+__device__ __forceinline__ int plan_worker() {
+  const int b = blockIdx.x, w = gridDim.x;
+  return (w & 7) == 0 ? (b & 7) * (w >> 3) + (b >> 3) : b;
+}
+
+// Next plan slot for this workgroup, or -1 when every item is claimed.  The
+// workgroup first claims the items of list `victim` (its own list at start)
+// through the cursor claim[victim]; an exhausted list moves it on to the next
+// worker's list.  Uniform across the workgroup (contains barriers).
+__device__ __forceinline__ int64_t claim_next(const int64_t* worker_off, int32_t* claim, int& victim, int& visited,
+                                              int* s_claim) {
+  const int W = gridDim.x;
+  while (visited < W) {
+    if (threadIdx.x == 0) *s_claim = atomicAdd(&claim[victim], 1);
+    __syncthreads();
+    const int idx = *s_claim;
+    __syncthreads();
+    const int64_t base = worker_off[victim];
+    if (idx < worker_off[victim + 1] - base) return base + idx;
+    victim = victim + 1 == W ? 0 : victim + 1;
+    ++visited;
+  }
+  return -1;
+}
+
 }  // namespace skv

@@ -18,10 +18,12 @@ struct FwdArgs {
   const int32_t* anchor;
   const skv_item* items;
   const int64_t* worker_off;
+  int32_t* claim;
   float* o_part;
   float* m_part;
   float* lse_part;
   int32_t block, group, hq, chunk;
+  float sm_scale;
   float scale_log2;  // sm_scale * log2(e)
 };
 
@@ -45,22 +47,28 @@ struct BwdArgs {
   void* dq;
   void* dk;
   void* dv;
-  float* dq_acc;  // [sum Mq][hq][d] fp32
-  float* delta;   // [sum Mq][hq] fp32
+  float* dq_part;     // per-chunk dQ partials, the forward's partial layout, [rows][d] fp32
+  float* delta;       // [sum Mq][hq] fp32
+  int64_t* part_base; // [n_seq + 1] first partial row of each sequence
   int64_t q_st, q_sh, kv_st, kv_sh;
   const int64_t* q_off;
   const int64_t* kv_off;
   const int32_t* anchor;
-  const skv_item* items;
-  const int64_t* worker_off;
+  const skv_item* kv_items;      // BWD plan: key ranges
+  const int64_t* kv_worker_off;
+  int32_t* kv_claim;
+  const skv_item* q_items;       // FWD plan: draft-block ranges of one chunk
+  const int64_t* q_worker_off;
+  int32_t* q_claim;
   int64_t total_q;  // sum Mq
-  int32_t block, group, hq, hkv;
+  int32_t n_seq, block, group, hq, hkv, chunk;
   float sm_scale, scale_log2;
 };
 
+hipError_t launch_claim_reset(int32_t* claim, int n_workers, hipStream_t stream);
 hipError_t launch_fwd_bf16(const FwdArgs& a, int n_workers, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdArgs& a, int d, int n_workers, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, int d, hipStream_t stream);
-hipError_t launch_bwd_bf16(const BwdArgs& a, int n_workers, hipStream_t stream);
+hipError_t launch_bwd_bf16(const BwdArgs& a, int kv_workers, int q_workers, hipStream_t stream);
 
 }  // namespace skv

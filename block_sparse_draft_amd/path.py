@@ -20,6 +20,61 @@ def default_workers(device) -> int:
     return torch.cuda.get_device_properties(device).multi_processor_count
 
 
+class _PlanSlots:
+    """Two pinned-host / device buffer pairs for one kind of plan, so that the
+    next step's plan uploads (asynchronously, on the compute stream) while the
+    previous step's kernels may still read the other pair."""
+
+    def __init__(self, problem: B.Problem, kind: int, granule: int, n_workers: int, policy: str):
+        import torch
+        self.problem, self.kind, self.granule, self.n_workers, self.policy = problem, kind, granule, n_workers, policy
+        n = len(problem.item_table(kind, granule)[1])
+        dev = problem.device
+        self.n_items = n
+        self.slots = []
+        for _ in range(2):
+            self.slots.append({
+                "h_items": torch.empty(max(n, 1) * 32, dtype=torch.uint8, pin_memory=True),
+                "h_off": torch.empty(n_workers + 1, dtype=torch.int64, pin_memory=True),
+                "d_items": torch.empty(max(n, 1) * 32, dtype=torch.uint8, device=dev),
+                "d_off": torch.empty(n_workers + 1, dtype=torch.int64, device=dev),
+                "event": torch.cuda.Event(), "used": False})
+        self.claim = torch.zeros(n_workers, dtype=torch.int32, device=dev)  # reset by the library per call
+        self.next = 0
+        self.c = None
+        self.load = self.cost = None
+
+    def replan(self):
+        """Realized costs -> LPT (or static) plan -> async upload.  Returns the skv_plan."""
+        items, cost, tok, total = self.problem.item_table(self.kind, self.granule)
+        if self.policy == "lpt":
+            _, order, off, load = B.lpt_plan(cost, self.n_workers)
+        elif self.policy == "static":
+            assign, order, off = B.skv_static_plan(tok, total, self.n_workers)
+            load = np.bincount(assign, weights=cost, minlength=self.n_workers).astype(np.int64)
+        else:
+            raise ValueError(self.policy)
+        slot = self.slots[self.next]
+        self.next ^= 1
+        if slot["used"]:
+            slot["event"].synchronize()   # its previous upload has left the pinned buffer
+        slot["h_items"].numpy()[:len(items) * 32] = B.skv_gather_items(items, order).view(np.uint8)
+        slot["h_off"].numpy()[:] = off
+        slot["d_items"].copy_(slot["h_items"], non_blocking=True)
+        slot["d_off"].copy_(slot["h_off"], non_blocking=True)
+        slot["event"].record()
+        slot["used"] = True
+        self.cost, self.load = cost, load
+        self.c = B.skv_plan(self.kind, self.n_workers, len(items), slot["d_items"].data_ptr(),
+                            slot["d_off"].data_ptr(), self.claim.data_ptr())
+        return self.c
+
+    @property
+    def imbalance(self) -> float:
+        mean = self.load.mean()
+        return float(self.load.max() / mean - 1.0) if mean > 0 else 0.0
+
+
 class SplitKVAttention:
     """Block-sparse draft attention of a packed batch, Split-KV style.
 
@@ -43,9 +98,13 @@ class SplitKVAttention:
         G = hq // hkv
         self.fwd_granule = fwd_granule or max(1, 256 // (G * block))
         self.bwd_granule = bwd_granule
-        self.fwd_plan = B.Plan(self.problem, B.SKV_ITEM_FWD, self.fwd_granule, self.n_workers, policy)
-        self.bwd_plan = (B.Plan(self.problem, B.SKV_ITEM_BWD, self.bwd_granule, self.n_workers, policy)
+        self.fwd_plan = _PlanSlots(self.problem, B.SKV_ITEM_FWD, self.fwd_granule, self.n_workers, policy)
+        self.bwd_plan = (_PlanSlots(self.problem, B.SKV_ITEM_BWD, self.bwd_granule, self.n_workers, policy)
                          if with_bwd else None)
+        # dQ runs over the forward's items; its own slots give it separate claim cursors
+        self.dq_plan = (_PlanSlots(self.problem, B.SKV_ITEM_FWD, self.fwd_granule, self.n_workers, policy)
+                        if with_bwd else None)
+        self.replan()
         self.part_base, self.n_chunk = self.problem.partial_layout()
         rows = int(self.part_base[-1])
         tq = self.problem.total_q
@@ -60,6 +119,13 @@ class SplitKVAttention:
             self.workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=self.device)
 
     # -- steps -------------------------------------------------------------
+    def replan(self):
+        """Mask descriptor -> realized cost per item -> LPT plan, uploaded for the next kernels."""
+        self.fwd_plan.replan()
+        if self.bwd_plan is not None:
+            self.bwd_plan.replan()
+            self.dq_plan.replan()
+
     def partial_fwd(self, q, k, v, stream=None):
         B.sparse_attn_partial_fwd(self.problem, self.fwd_plan, q, k, v, self.o_part, self.m_part, self.lse_part,
                                   stream)
@@ -82,8 +148,8 @@ class SplitKVAttention:
 
     def backward(self, q, k, v, dout, dq, dk, dv, stream=None):
         """dQ, dK, dV from the merged O and LSE of the last forward."""
-        B.sparse_attn_bwd(self.problem, self.bwd_plan, q, k, v, self.o, self.lse, dout, dq, dk, dv, self.workspace,
-                          stream)
+        B.sparse_attn_bwd(self.problem, self.bwd_plan, self.dq_plan, q, k, v, self.o, self.lse, dout, dq, dk, dv,
+                          self.workspace, stream)
         return dq, dk, dv
 
     # -- views ---------------------------------------------------------------

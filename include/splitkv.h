@@ -94,14 +94,22 @@ typedef struct skv_item {
 } skv_item;
 
 /* A plan as the kernels read it: items grouped by persistent workgroup.
- * Workgroup w runs d_items[d_worker_off[w] .. d_worker_off[w+1]) in order.
- * n_workers is the launched grid size. */
+ * Worker w's list is d_items[d_worker_off[w] .. d_worker_off[w+1]), in the
+ * order the planner assigned them.  n_workers is the launched grid size.
+ * Each worker claims the items of its own list in order through the atomic
+ * cursor d_claim[w]; once its list is exhausted it claims the remaining
+ * items of the other lists (the next workers first), so a slow compute unit
+ * delays the call by at most the item it holds.  Every item is processed
+ * exactly once.  d_claim is caller-owned scratch of n_workers int32 that the
+ * library resets at the start of every call; two calls in flight at the same
+ * time must not share it. */
 typedef struct skv_plan {
   int32_t kind;       /* skv_item_kind */
   int32_t n_workers;  /* >= 1 */
   int64_t n_items;
   const skv_item* d_items;      /* device, [n_items] */
   const int64_t* d_worker_off;  /* device, [n_workers+1], d_worker_off[0] = 0 */
+  int32_t* d_claim;             /* device scratch, [n_workers] */
 } skv_plan;
 
 /* Thread-local description of the last error (never NULL). */
@@ -178,8 +186,10 @@ int lse_merge(int32_t n_part, int32_t hq, int64_t mq, int32_t d, const float* o_
               const float* lse_part, void* o_out, int64_t o_stride_tok, int64_t o_stride_head, int32_t out_dtype,
               float* lse_out, int64_t lse_stride_tok, void* stream);
 
-/* Bytes of device workspace sparse_attn_bwd needs: an fp32 dQ accumulator
- * [sum Mq][hq][d] and fp32 Delta [sum Mq][hq], each 256-byte aligned. */
+/* Bytes of device workspace sparse_attn_bwd needs (256-byte aligned pieces):
+ * fp32 dQ partials in the layout of skv_partial_layout ([rows][d]), fp32
+ * Delta [sum Mq][hq], and n_seq+1 int64 partial offsets.  0 for an invalid
+ * problem. */
 size_t skv_bwd_workspace_bytes(const skv_problem* p);
 
 /* Backward of O with respect to Q, K, V, reusing the merged LSE.
@@ -188,13 +198,15 @@ size_t skv_bwd_workspace_bytes(const skv_problem* p);
  * dK_j = sm_scale * sum dS q, summed over the query heads of each KV head.
  * o = merged output (problem dtype, Q layout), lse = merged LSE (float
  * [sum Mq][hq]), dout = dO.  Outputs dq (Q layout), dk and dv (K/V layout)
- * are fully written, dk = dv = 0 for keys no query sees.  `plan` must be a
- * BWD plan over skv_item_table items covering every key range once.  dQ is
- * accumulated with fp32 atomics, so it is not bitwise reproducible.
+ * are fully written, dk = dv = 0 for keys no query sees.
+ * plan_kv is a BWD plan (key ranges; dK, dV are owned by their item);
+ * plan_q is a FWD plan over the forward's items (each writes the dQ partial of
+ * its chunk, summed per row afterwards).  The two plans need distinct claim
+ * arrays.  No atomics: the result is bitwise reproducible.
  * Only SKV_BF16 with d = 128 is supported. */
-int sparse_attn_bwd(const skv_problem* p, const skv_plan* plan, const void* q, const void* k, const void* v,
-                    const void* o, const float* lse, const void* dout, void* dq, void* dk, void* dv,
-                    void* workspace, size_t workspace_bytes, void* stream);
+int sparse_attn_bwd(const skv_problem* p, const skv_plan* plan_kv, const skv_plan* plan_q, const void* q,
+                    const void* k, const void* v, const void* o, const float* lse, const void* dout, void* dq,
+                    void* dk, void* dv, void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

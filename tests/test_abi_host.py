@@ -154,17 +154,20 @@ def test_problem_validation_codes():
 def test_device_calls_reject_bad_arguments_before_touching_the_gpu():
     w = make("c1", seed=0)
     p = _problem_from(w)           # host-only: device arrays NULL
-    plan = B.skv_plan(B.SKV_ITEM_FWD, 4, 1, 16, 16)
+    plan = B.skv_plan(B.SKV_ITEM_FWD, 4, 1, 16, 16, 16)
     fake = C.c_void_p(4096)
     rc = B.lib.sparse_attn_partial_fwd(C.byref(p.c), C.byref(plan), fake, fake, fake, fake, fake, fake, None)
     assert rc == B.SKV_EINVAL and "device" in B.last_error()
     # wrong plan kind
     p.c.d_q_off = p.c.d_kv_off = p.c.d_anchor = 4096
-    bplan = B.skv_plan(B.SKV_ITEM_BWD, 4, 1, 16, 16)
+    bplan = B.skv_plan(B.SKV_ITEM_BWD, 4, 1, 16, 16, 16)
     rc = B.lib.sparse_attn_partial_fwd(C.byref(p.c), C.byref(bplan), fake, fake, fake, fake, fake, fake, None)
     assert rc == B.SKV_EPLAN
-    zplan = B.skv_plan(B.SKV_ITEM_FWD, 0, 1, 16, 16)
+    zplan = B.skv_plan(B.SKV_ITEM_FWD, 0, 1, 16, 16, 16)
     rc = B.lib.sparse_attn_partial_fwd(C.byref(p.c), C.byref(zplan), fake, fake, fake, fake, fake, fake, None)
+    assert rc == B.SKV_EPLAN
+    nclaim = B.skv_plan(B.SKV_ITEM_FWD, 4, 1, 16, 16, None)   # claim cursors are required
+    rc = B.lib.sparse_attn_partial_fwd(C.byref(p.c), C.byref(nclaim), fake, fake, fake, fake, fake, fake, None)
     assert rc == B.SKV_EPLAN
     rc = B.lib.sparse_attn_partial_fwd(C.byref(p.c), C.byref(plan), None, fake, fake, fake, fake, fake, None)
     assert rc == B.SKV_EINVAL
@@ -172,15 +175,21 @@ def test_device_calls_reject_bad_arguments_before_touching_the_gpu():
                                        None)
     assert rc == B.SKV_ESHAPE
     # bwd: fp32 problems are rejected, workspace is checked
-    rc = B.lib.sparse_attn_bwd(C.byref(p.c), C.byref(bplan), *([fake] * 10), 1 << 30, None)
+    rc = B.lib.sparse_attn_bwd(C.byref(p.c), C.byref(bplan), C.byref(plan), *([fake] * 10), 1 << 30, None)
     assert rc == B.SKV_EDTYPE
     wb = make("c2", seed=0, n_ctx=256, n_anchor=2)
     pb = _problem_from(wb)
     pb.c.d_q_off = pb.c.d_kv_off = pb.c.d_anchor = 4096
     need = B.lib.skv_bwd_workspace_bytes(C.byref(pb.c))
-    assert need == 32 * 32 * 128 * 4 + 32 * 32 * 4
-    rc = B.lib.sparse_attn_bwd(C.byref(pb.c), C.byref(bplan), *([fake] * 10), need - 1, None)
+    # dQ partials: 1 chunk (256 keys, chunk 1024) x 32 heads x 32 rows x 128 fp32; Delta; 2 offsets
+    assert need == 32 * 32 * 128 * 4 + 32 * 32 * 4 + 256
+    qplan = B.skv_plan(B.SKV_ITEM_FWD, 4, 1, 16, 16, 32)
+    rc = B.lib.sparse_attn_bwd(C.byref(pb.c), C.byref(bplan), C.byref(qplan), *([fake] * 10), need - 1, None)
     assert rc == B.SKV_EWORKSPACE
+    rc = B.lib.sparse_attn_bwd(C.byref(pb.c), C.byref(bplan), C.byref(bplan), *([fake] * 10), need, None)
+    assert rc == B.SKV_EPLAN                       # second plan must be a forward plan
+    rc = B.lib.sparse_attn_bwd(C.byref(pb.c), C.byref(bplan), C.byref(plan), *([fake] * 10), need, None)
+    assert rc == B.SKV_EPLAN                       # shared claim cursors are rejected
     # merge
     rc = B.lib.lse_merge(4, 2, 64, 96, fake, fake, fake, fake, 128, 64, B.SKV_F32, fake, 2, None)
     assert rc == B.SKV_ESHAPE
