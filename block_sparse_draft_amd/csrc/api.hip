@@ -51,6 +51,7 @@ extern "C" int sparse_attn_partial_fwd(const skv_problem* p, const skv_plan* pla
   a.items = plan->d_items; a.worker_off = plan->d_worker_off; a.claim = plan->d_claim;
   a.o_part = o_part; a.m_part = m_part; a.lse_part = lse_part;
   a.block = p->block; a.group = p->hq / p->hkv; a.hq = p->hq; a.chunk = p->chunk;
+  a.fd_block = FastDiv::make(a.block); a.fd_group = FastDiv::make(a.group); a.fd_gb = FastDiv::make(a.block * a.group);
   a.sm_scale = p->sm_scale;
   a.scale_log2 = p->sm_scale * kLog2e_host;
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -142,6 +143,7 @@ extern "C" int sparse_attn_bwd(const skv_problem* p, const skv_plan* plan_kv, co
   a.total_q = p->h_q_off[p->n_seq];
   a.n_seq = p->n_seq; a.block = p->block; a.group = p->hq / p->hkv; a.hq = p->hq; a.hkv = p->hkv;
   a.chunk = p->chunk;
+  a.fd_block = FastDiv::make(a.block); a.fd_group = FastDiv::make(a.group); a.fd_gb = FastDiv::make(a.block * a.group);
   a.sm_scale = p->sm_scale; a.scale_log2 = p->sm_scale * kLog2e_host;
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e = launch_claim_reset(plan_kv->d_claim, plan_kv->n_workers, st);

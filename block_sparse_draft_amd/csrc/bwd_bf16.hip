@@ -150,9 +150,10 @@ void bwd_kv_kernel(BwdArgs a) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const int p = min(qt * QT + row + 16 * u, nq - 1);
-          const int b = b_first + p / GB;
-          const int h = g * a.group + (p / a.block) % a.group;
-          const int64_t t = q0 + (int64_t)b * a.block + p % a.block;
+          const int pb = a.fd_block.div(p);
+          const int b = b_first + a.fd_group.div(pb);
+          const int h = g * a.group + (pb - a.fd_group.div(pb) * a.group);
+          const int64_t t = q0 + (int64_t)b * a.block + (p - pb * a.block);
           off[u] = t * a.q_st + (int64_t)h * a.q_sh + d8;
         }
         r.q0 = *reinterpret_cast<const uint4*>(Q + off[0]);
@@ -167,9 +168,10 @@ void bwd_kv_kernel(BwdArgs a) {
         if (tid < QT) {
           const int p = qt * QT + tid;
           const int pc = min(p, nq - 1);
-          const int b = b_first + pc / GB;
-          const int h = g * a.group + (pc / a.block) % a.group;
-          const int64_t rr = (q0 + (int64_t)b * a.block + pc % a.block) * a.hq + h;
+          const int pb = a.fd_block.div(pc);
+          const int b = b_first + a.fd_group.div(pb);
+          const int h = g * a.group + (pb - a.fd_group.div(pb) * a.group);
+          const int64_t rr = (q0 + (int64_t)b * a.block + (pc - pb * a.block)) * a.hq + h;
           const float lse = a.lse[rr];
           const float del = a.delta[rr];
           const int e = min(a.anchor[blk0 + b] + a.block, n_ctx);
@@ -251,7 +253,22 @@ void bwd_kv_kernel(BwdArgs a) {
             }
           }
           // ---- P = exp2(s*c - LSE2) on visible entries, dS = P (dP - Delta) ----
-          // lane holds key key_w, rows mt*32 + 8i + 4hf + j (element 4i + j)
+          // lane holds key key_w, rows mt*32 + 8i + 4hf + j (element 4i + j).
+          // Rows are sorted by prefix end, so if the tile's first row sees all
+          // 128 keys (and no row is padding) no entry needs masking.
+          const bool full = M.end[0] >= kb + KT && qt * QT + QT <= nq;
+          if (!full) {
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const int4 end4 = *reinterpret_cast<const int4*>(&M.end[mt * 32 + 8 * i + 4 * hf]);
+                const int ends[4] = {end4.x, end4.y, end4.z, end4.w};
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                  if (key_w >= ends[j]) sacc[mt][4 * i + j] = -INFINITY;
+              }
+          }
 #pragma unroll
           for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
@@ -259,13 +276,10 @@ void bwd_kv_kernel(BwdArgs a) {
               const int r0 = mt * 32 + 8 * i + 4 * hf;
               const f32x4 lse4 = *reinterpret_cast<const f32x4*>(&M.lse[r0]);
               const f32x4 del4 = *reinterpret_cast<const f32x4*>(&M.delta[r0]);
-              const int4 end4 = *reinterpret_cast<const int4*>(&M.end[r0]);
-              const int ends[4] = {end4.x, end4.y, end4.z, end4.w};
 #pragma unroll
               for (int j = 0; j < 4; ++j) {
                 const int e = 4 * i + j;
-                float p = fast_exp2(__builtin_fmaf(sacc[mt][e], c, -lse4[j]));
-                if (key_w >= ends[j]) p = 0.f;
+                const float p = fast_exp2(__builtin_fmaf(sacc[mt][e], c, -lse4[j]));
                 sacc[mt][e] = p;
                 pacc[mt][e] = p * (pacc[mt][e] - del4[j]);
               }
@@ -393,7 +407,7 @@ void bwd_dq_kernel(BwdArgs a) {
 
     for (int rt = 0; rt < nrows; rt += 256) {
       const int p_last = min(nrows, rt + 256) - 1;
-      const int wg_hi = max(klo, min(khi, min(a.anchor[blk0 + it.lo + p_last / GB] + a.block, n_ctx)));
+      const int wg_hi = max(klo, min(khi, min(a.anchor[blk0 + it.lo + a.fd_gb.div(p_last)] + a.block, n_ctx)));
       const int ntiles = (wg_hi - klo + KT2 - 1) / KT2;
       if (ntiles == 0) continue;  // no row of the pass sees the chunk: no partial to write
 
@@ -410,9 +424,9 @@ void bwd_dq_kernel(BwdArgs a) {
         const int p = rt + wave * 64 + nt * 32 + l32;
         valid[nt] = p < nrows;
         const int pc = valid[nt] ? p : p_last;
-        const int b = it.lo + pc / GB;
-        const int hl = (pc / a.block) % a.group;
-        const int64_t r = (int64_t)b * a.block + pc % a.block;
+        const int b = it.lo + a.fd_gb.div(pc);
+        const int hl = a.fd_group.mod(a.fd_block.div(pc));
+        const int64_t r = (int64_t)b * a.block + a.fd_block.mod(pc);
         const int h = it.kv_head * a.group + hl;
         const int e = min(a.anchor[blk0 + b] + a.block, n_ctx);
         vend[nt] = valid[nt] ? max(klo, min(khi, e)) : klo;
@@ -428,9 +442,10 @@ void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
       for (int u = 0; u < 16; ++u) {
         const int p = min(rt + (tid >> 4) + 16 * u, p_last);
-        const int b = it.lo + p / GB;
-        const int h = it.kv_head * a.group + (p / a.block) % a.group;
-        const int64_t t = q0 + (int64_t)b * a.block + p % a.block;
+        const int pb = a.fd_block.div(p);
+        const int b = it.lo + a.fd_group.div(pb);
+        const int h = it.kv_head * a.group + (pb - a.fd_group.div(pb) * a.group);
+        const int64_t t = q0 + (int64_t)b * a.block + (p - pb * a.block);
         dox[u] = *reinterpret_cast<const uint4*>(dO + t * a.q_st + (int64_t)h * a.q_sh + (tid & 15) * 8);
       }
 #pragma unroll
@@ -547,7 +562,7 @@ __global__ __launch_bounds__(256) void bwd_finalize_kernel(BwdArgs a) {
   const int64_t q0 = a.q_off[s], mq = a.q_off[s + 1] - q0;
   const int64_t r = t - q0;
   const int n_ctx = (int)(a.kv_off[s + 1] - a.kv_off[s]);
-  const int e = min(a.anchor[q0 / a.block + r / a.block] + a.block, n_ctx);
+  const int e = min(a.anchor[(q0 + r) / a.block] + a.block, n_ctx);
   const int nc = (e + a.chunk - 1) / a.chunk;  // chunks the row sees
   const float* src = a.dq_part + (a.part_base[s] + (int64_t)h * mq + r) * D + ln * 4;
   const int64_t cstride = (int64_t)a.hq * mq * D;

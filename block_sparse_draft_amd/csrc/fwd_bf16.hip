@@ -115,7 +115,7 @@ void fwd_bf16_kernel(FwdArgs a) {
     for (int rt = 0; rt < nrows; rt += ROWS) {
       // Anchors are sorted, so the last row of the pass has the largest prefix end.
       const int p_last = min(nrows, rt + ROWS) - 1;
-      const int wg_hi = max(klo, min(khi, min(a.anchor[blk0 + it.lo + p_last / GB] + a.block, n_ctx)));
+      const int wg_hi = max(klo, min(khi, min(a.anchor[blk0 + it.lo + a.fd_gb.div(p_last)] + a.block, n_ctx)));
       const int ntiles = (wg_hi - klo + KT - 1) / KT;
 
       // ---- start the K/V pipeline around the loads of this lane's two Q rows ----
@@ -133,9 +133,9 @@ void fwd_bf16_kernel(FwdArgs a) {
         const int p = rt + wave * 64 + nt * 32 + l32;
         valid[nt] = p < nrows;
         const int pc = valid[nt] ? p : p_last;  // clamp: loads stay in bounds, results unused
-        const int b = it.lo + pc / GB;
-        const int hl = (pc / a.block) % a.group;
-        const int64_t r = (int64_t)b * a.block + pc % a.block;
+        const int b = it.lo + a.fd_gb.div(pc);
+        const int hl = a.fd_group.mod(a.fd_block.div(pc));
+        const int64_t r = (int64_t)b * a.block + a.fd_block.mod(pc);
         const int h = it.kv_head * a.group + hl;
         const int e = min(a.anchor[blk0 + b] + a.block, n_ctx);
         vend[nt] = valid[nt] ? max(klo, min(khi, e)) : klo;

@@ -46,6 +46,7 @@ extern "C" int skv_check_problem(const skv_problem* p) {
   if (p->block < 1) return fail(SKV_EINVAL, "block = %d < 1", p->block);
   if (p->hq < 1 || p->hkv < 1) return fail(SKV_ESHAPE, "hq = %d, hkv = %d must be >= 1", p->hq, p->hkv);
   if (p->hq % p->hkv) return fail(SKV_ESHAPE, "hq = %d is not a multiple of hkv = %d", p->hq, p->hkv);
+  if ((int64_t)p->block * (p->hq / p->hkv) > (1 << 20)) return fail(SKV_ESHAPE, "block * hq/hkv exceeds 2^20");
   if (p->dtype != SKV_F32 && p->dtype != SKV_BF16) return fail(SKV_EDTYPE, "unknown dtype %d", p->dtype);
   if (p->dtype == SKV_BF16 && p->d != 128) return fail(SKV_ESHAPE, "bf16 supports head_dim 128, got %d", p->d);
   if (p->dtype == SKV_F32 && p->d != 64 && p->d != 128)

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "fastdiv.h"
 #include "splitkv.h"
 
 namespace skv {
@@ -23,6 +24,7 @@ struct FwdArgs {
   float* m_part;
   float* lse_part;
   int32_t block, group, hq, chunk;
+  FastDiv fd_block, fd_group, fd_gb;  // division by block, hq/hkv and their product
   float sm_scale;
   float scale_log2;  // sm_scale * log2(e)
 };
@@ -62,6 +64,7 @@ struct BwdArgs {
   int32_t* q_claim;
   int64_t total_q;  // sum Mq
   int32_t n_seq, block, group, hq, hkv, chunk;
+  FastDiv fd_block, fd_group, fd_gb;  // division by block, hq/hkv and their product
   float sm_scale, scale_log2;
 };
 
