@@ -5,19 +5,29 @@
 One step = one pass of the whole hot path over one synthetic batch: realized
 cost model + LPT plan (host, uploaded asynchronously), the partial forward of
 every (sequence, KV head, chunk, draft-block range) item, the log-sum-exp merge
-of each sequence, and the backward (Delta, key-owning main kernel, dQ
-finalize).  Inputs are resident in HBM before the timed region.
+of each sequence, and the backward (Delta, key-owning dK/dV kernel,
+query-owning dQ kernel, dQ finalize).  Inputs are resident in HBM before the
+timed region.
 
 Prints ONE JSON line.  ``value`` is unmasked fwd+bwd TFLOP/s: 4*d (forward) +
 10*d (backward, including the QK^T recompute that reusing the LSE needs) FLOPs
 per token-exact visible (query head, query row, key) triple, divided by the
 wall time of the K timed steps.  Per-kernel times come from HIP events recorded
-on the stream the kernels run on.  ``cpu_baseline`` times the float64 CPU oracle
-on a bounded sample of the same workload on this host.
+on the stream the kernels run on; the library brackets each of its own
+launches with events as well (skv_timing_*), which gives the per-kernel
+durations behind ``roofline``.  ``cpu_baseline`` times the float64 CPU oracle on
+a bounded sample of the same workload on this host.
+
+    --plan-compare     also run the workload under static and LPT plans, with
+                       and without tail stealing, and report cost-model and
+                       measured per-workgroup imbalance and step times
+    --copy-calibration MB   run one device copy of MB MiB before the steps
+                       (reference dispatch for HBM byte counters)
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -90,6 +100,124 @@ def cpu_baseline(w, budget_s: float = 12.0):
                       f"slice(s) {done} of {c.name}, {t:.1f} s"}
 
 
+# Algorithmic FLOPs per token-exact visible (q head, row, key) triple, in units
+# of head_dim, that each kernel contributes to the 4d + 10d count: the forward
+# does QK^T and PV; the key-owner backward recomputes QK^T and forms dP, dV and
+# dK; the query-owner backward forms dQ (it also recomputes QK^T and dP, 4d
+# more per triple, which the count leaves out).
+KERNEL_FLOPS_D = {"partial_fwd_bf16": 4, "partial_fwd_f32": 4, "bwd_kv": 8, "bwd_dq": 2}
+KERNEL_EXEC_FLOPS_D = {"partial_fwd_bf16": 4, "partial_fwd_f32": 4, "bwd_kv": 8, "bwd_dq": 6}
+KERNEL_SOURCES = {
+    "bwd_kv": ["bwd_bf16.hip", "device.h", "fastdiv.h", "launch.h"],
+    "bwd_dq": ["bwd_bf16.hip", "device.h", "fastdiv.h", "launch.h"],
+    "partial_fwd_bf16": ["fwd_bf16.hip", "device.h", "fastdiv.h", "launch.h"],
+}
+
+
+def kernel_source_hash(kernel: str) -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES.get(kernel, []):
+        with open(os.path.join(ROOT, "block_sparse_draft_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def hbm_traffic(kernel: str, config: str):
+    """HBM bytes per launch of `kernel` on `config` from the committed counter
+    summary (rocprofv3 FETCH_SIZE / WRITE_SIZE, scaled by a copy kernel of
+    known size), or None when there is none or the kernel source has changed
+    since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{config}_hbm_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line and not line.startswith((" ", "#")):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("source_sha256_16") != kernel_source_hash(kernel):
+        return None
+    try:
+        return int(float(kv["fetch_bytes_per_launch"]) + float(kv["write_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def run_steps(path, q, k, v, do, grads, K: int, warmup: int, replan: bool, with_bwd: bool):
+    """Warm up, then time K steps.  Returns wall seconds, per-phase event ms
+    (lists) and the library's per-kernel event times."""
+    import torch
+    from block_sparse_draft_amd import binding as Bd
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    plan_s = []
+
+    def step(e=None):
+        if replan:
+            path.replan()
+            plan_s.append(path.plan_s)
+        if e: e[0].record()
+        path.partial_fwd(q, k, v)
+        if e: e[1].record()
+        path.merge()
+        if e: e[2].record()
+        if with_bwd:
+            path.backward(q, k, v, do, *grads)
+        if e: e[3].record()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    plan_s.clear()
+    Bd.timing_collect()
+    Bd.timing_enable(True)
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(ev[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    Bd.timing_enable(False)
+    kt = Bd.timing_collect()
+    ph = {"fwd": [e[0].elapsed_time(e[1]) for e in ev], "merge": [e[1].elapsed_time(e[2]) for e in ev],
+          "bwd": [e[2].elapsed_time(e[3]) for e in ev]}
+    return wall, ph, kt, plan_s
+
+
+def imbalance(x) -> float:
+    x = np.asarray(x, dtype=np.float64)
+    m = x.mean()
+    return float(x.max() / m - 1.0) if m > 0 else 0.0
+
+
+def plan_compare(w, q, k, v, do, grads, dt, dev, K: int, warmup: int, bwd_granule: int, with_bwd: bool):
+    """Static token-count vs cost-aware LPT plans, each with and without tail
+    stealing: cost-model imbalance of the plan, measured imbalance of the
+    per-workgroup busy times (s_memrealtime) and the step times."""
+    import torch
+    from block_sparse_draft_amd import SplitKVAttention
+    c = w.cfg
+    out = []
+    for policy in ("static", "lpt"):
+        for steal in (False, True):
+            path = SplitKVAttention(w.q_off, w.kv_off, w.anchors, c.block, c.hq, c.hkv, c.d, c.chunk, w.sm_scale,
+                                    dt, dev, policy=policy, bwd_granule=bwd_granule, with_bwd=with_bwd,
+                                    steal=steal, ticks=True)
+            wall, ph, kt, _ = run_steps(path, q, k, v, do, grads, K, warmup, False, with_bwd)
+            rec = {"policy": policy, "steal": steal, "ms_per_step": round(wall / K * 1e3, 4),
+                   "fwd_ms": round(float(np.mean(ph["fwd"])), 4),
+                   "bwd_ms": round(float(np.mean(ph["bwd"])), 4) if with_bwd else None,
+                   "fwd_cost_imbalance": round(path.fwd_plan.imbalance, 5),
+                   "fwd_measured_imbalance": round(imbalance(path.fwd_plan.ticks.cpu().numpy()), 5)}
+            if with_bwd:
+                rec.update({"bwd_kv_cost_imbalance": round(path.bwd_plan.imbalance, 5),
+                            "bwd_kv_measured_imbalance": round(imbalance(path.bwd_plan.ticks.cpu().numpy()), 5),
+                            "bwd_dq_measured_imbalance": round(imbalance(path.dq_plan.ticks.cpu().numpy()), 5)})
+            out.append(rec)
+            del path
+            torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -101,6 +229,9 @@ def main():
     ap.add_argument("--bwd-granule", type=int, default=256)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-replan", action="store_true", help="plan once outside the timed region")
+    ap.add_argument("--no-steal", action="store_true", help="workgroups run only their own plan lists")
+    ap.add_argument("--plan-compare", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -113,10 +244,8 @@ def main():
     from synthetic import make
 
     dev = torch.device("cuda:0")
-    t_gen = time.perf_counter()
     w = make(args.config, seed=args.seed)
     c = w.cfg
-    t_gen = time.perf_counter() - t_gen
     dt = torch.bfloat16 if w.is_bf16 else torch.float32
 
     def up(name):
@@ -128,61 +257,57 @@ def main():
     q, k, v = up("q"), up("k"), up("v")
     with_bwd = c.bwd and w.is_bf16
     do = up("do") if with_bwd else None
+    grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)) if with_bwd else None
+
+    if args.copy_calibration > 0:
+        # one plain device-to-device copy of known size, for scaling HBM byte counters
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     path = SplitKVAttention(w.q_off, w.kv_off, w.anchors, c.block, c.hq, c.hkv, c.d, c.chunk, w.sm_scale, dt, dev,
-                            policy=args.policy, bwd_granule=args.bwd_granule, with_bwd=with_bwd)
-    if with_bwd:
-        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-
+                            policy=args.policy, bwd_granule=args.bwd_granule, with_bwd=with_bwd,
+                            steal=not args.no_steal)
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
-    plan_s = []
+    wall, ph, kt, plan_s = run_steps(path, q, k, v, do, grads, K, args.warmup, not args.no_replan, with_bwd)
 
-    def step(i=None):
-        if not args.no_replan:
-            t0 = time.perf_counter()
-            path.replan()
-            plan_s.append(time.perf_counter() - t0)
-        e = ev[i] if i is not None else None
-        if e: e[0].record()
-        path.partial_fwd(q, k, v)
-        if e: e[1].record()
-        path.merge()
-        if e: e[2].record()
-        if with_bwd:
-            path.backward(q, k, v, do, dq, dk, dv)
-        if e: e[3].record()
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    plan_s.clear()
-    t0 = time.perf_counter()
-    for i in range(K):
-        step(i)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-
-    fwd_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
-    mrg_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
-    bwd_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in ev]))
+    fwd_ms = float(np.mean(ph["fwd"]))
+    mrg_ms = float(np.mean(ph["merge"]))
+    bwd_ms = float(np.mean(ph["bwd"]))
     pairs = unmasked_pairs(w.q_off, w.kv_off, w.anchors, c.block, c.hq)
     fwd_flops = 4.0 * c.d * pairs
     bwd_flops = 10.0 * c.d * pairs if with_bwd else 0.0
     ms_per_step = wall / K * 1e3
     value = (fwd_flops + bwd_flops) / (wall / K) / 1e12
     mbytes = merge_bytes(path, c.d)
-    n_merge = c.n_seq
     fwd_tf = fwd_flops / (fwd_ms * 1e-3) / 1e12
     bwd_tf = bwd_flops / (bwd_ms * 1e-3) / 1e12 if with_bwd else 0.0
     merge_gbs = mbytes / (mrg_ms * 1e-3) / 1e9
-    if with_bwd:
-        roof = {"bound": "mfma", "kernel": "sparse_attn_bwd (bwd_main_kernel; with its Delta and dQ-finalize launches)",
-                "achieved": round(bwd_tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(bwd_tf / PEAK_BF16_TFLOPS, 4), "traffic": None}
-    else:
-        roof = {"bound": "mfma", "kernel": "sparse_attn_partial_fwd (fwd_bf16_kernel)", "achieved": round(fwd_tf, 2),
-                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(fwd_tf / PEAK_BF16_TFLOPS, 4),
-                "traffic": None}
+
+    kernels = {}
+    for name, (n_launch, tot) in kt.items():
+        avg = tot / max(n_launch, 1)
+        rec = {"launches_per_step": n_launch / K, "avg_ms": round(avg, 4)}
+        if name in KERNEL_FLOPS_D:
+            alg = KERNEL_FLOPS_D[name] * c.d * pairs
+            rec["alg_tflops"] = round(alg / (avg * 1e-3) / 1e12, 2)
+            rec["exec_tflops"] = round(KERNEL_EXEC_FLOPS_D[name] * c.d * pairs / (avg * 1e-3) / 1e12, 2)
+        if name == "lse_merge":
+            rec["gbs"] = round(mbytes / (tot / K * 1e-3) / 1e9, 1)
+        kernels[name] = rec
+    compute = {n: kt[n][1] for n in KERNEL_FLOPS_D if n in kt}
+    dom = max(compute, key=compute.get)
+    dom_avg = kt[dom][1] / kt[dom][0]
+    dom_flops = KERNEL_FLOPS_D[dom] * c.d * pairs
+    achieved = dom_flops / (dom_avg * 1e-3) / 1e12
+    roof = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS
+            if w.is_bf16 else 157.3, "unit": "TFLOP/s",
+            "frac": round(achieved / (PEAK_BF16_TFLOPS if w.is_bf16 else 157.3), 4),
+            "traffic": hbm_traffic(dom, c.name),
+            "alg_flops_per_launch": dom_flops, "avg_launch_ms": round(dom_avg, 4)}
     out = {
         "metric": "unmasked-FLOP TFLOP/s fwd+bwd, % of bf16 MFMA peak; merge GB/s",
         "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
@@ -190,20 +315,26 @@ def main():
         "dtype": "bf16" if w.is_bf16 else "f32", "data": "synthetic",
         "config": {"workload": f"{c.name}: {WORKLOAD_TEXT.get(c.name, c.note)}", "seed": args.seed,
                    "n_ctx": [int(x) for x in w.n_ctx], "unmasked_pairs": int(pairs), "policy": args.policy,
-                   "n_workers": path.n_workers, "fwd_granule_blocks": path.fwd_granule,
+                   "steal": not args.no_steal, "n_workers": path.n_workers, "fwd_granule_blocks": path.fwd_granule,
                    "bwd_granule_keys": path.bwd_granule if with_bwd else None},
         "pct_of_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "fwd": {"ms": round(fwd_ms, 4), "tflops": round(fwd_tf, 2), "frac": round(fwd_tf / PEAK_BF16_TFLOPS, 4)},
-        "merge": {"ms": round(mrg_ms, 4), "launches": n_merge, "bytes": mbytes, "gbs": round(merge_gbs, 1),
+        "merge": {"ms": round(mrg_ms, 4), "launches": c.n_seq, "bytes": mbytes, "gbs": round(merge_gbs, 1),
                   "frac": round(merge_gbs / PEAK_HBM_GBS, 4)},
         "bwd": {"ms": round(bwd_ms, 4), "tflops": round(bwd_tf, 2), "frac": round(bwd_tf / PEAK_BF16_TFLOPS, 4)}
         if with_bwd else None,
-        "plan": {"ms_per_step": round(1e3 * float(np.mean(plan_s)), 3) if plan_s else None,
+        "kernels": kernels,
+        "plan": {"host_ms_per_step": round(1e3 * float(np.mean(plan_s)), 3) if plan_s else None,
                  "fwd_items": path.fwd_plan.n_items, "fwd_imbalance": round(path.fwd_plan.imbalance, 5),
                  "bwd_items": path.bwd_plan.n_items if with_bwd else None,
                  "bwd_imbalance": round(path.bwd_plan.imbalance, 5) if with_bwd else None},
         "roofline": roof,
     }
+    del path
+    torch.cuda.empty_cache()
+    if args.plan_compare:
+        out["plan_compare"] = plan_compare(w, q, k, v, do, grads, dt, dev, max(3, K // 2), 2, args.bwd_granule,
+                                           with_bwd)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(out), flush=True)

@@ -21,6 +21,7 @@ SKV_OK, SKV_EINVAL, SKV_EDTYPE, SKV_ESHAPE, SKV_EHIP, SKV_EWORKSPACE, SKV_EPLAN 
 SKV_F32, SKV_BF16 = 0, 1
 SKV_ITEM_FWD, SKV_ITEM_BWD = 0, 1
 SKV_TILE = 64
+SKV_PLAN_NO_STEAL = 1
 _STATUS = {0: "SKV_OK", -1: "SKV_EINVAL", -2: "SKV_EDTYPE", -3: "SKV_ESHAPE", -4: "SKV_EHIP",
            -5: "SKV_EWORKSPACE", -6: "SKV_EPLAN"}
 
@@ -52,7 +53,12 @@ assert ITEM_DTYPE.itemsize == C.sizeof(skv_item) == 32
 
 class skv_plan(C.Structure):
     _fields_ = [("kind", C.c_int32), ("n_workers", C.c_int32), ("n_items", C.c_int64),
-                ("d_items", C.c_void_p), ("d_worker_off", C.c_void_p), ("d_claim", C.c_void_p)]
+                ("d_items", C.c_void_p), ("d_worker_off", C.c_void_p), ("d_claim", C.c_void_p),
+                ("flags", C.c_int32), ("reserved", C.c_int32), ("d_ticks", C.c_void_p)]
+
+
+class skv_kernel_time(C.Structure):
+    _fields_ = [("name", C.c_char_p), ("launches", C.c_int64), ("total_ms", C.c_double)]
 
 
 def _load():
@@ -77,6 +83,8 @@ def _load():
         "lse_merge": (C.c_int, [I32, I32, I64, I32, VP, VP, VP, VP, I64, I64, I32, VP, I64, VP]),
         "skv_bwd_workspace_bytes": (C.c_size_t, [P(skv_problem)]),
         "sparse_attn_bwd": (C.c_int, [P(skv_problem), P(skv_plan), P(skv_plan)] + [VP] * 10 + [C.c_size_t, VP]),
+        "skv_timing_enable": (C.c_int, [I32]),
+        "skv_timing_collect": (C.c_int, [P(skv_kernel_time), I32, P(I32)]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -87,7 +95,7 @@ def _load():
 lib = _load()
 EXPORTED = ("skv_last_error", "skv_check_problem", "skv_partial_layout", "skv_item_table", "lpt_plan",
             "skv_static_plan", "skv_gather_items", "sparse_attn_partial_fwd", "lse_merge",
-            "skv_bwd_workspace_bytes", "sparse_attn_bwd")
+            "skv_bwd_workspace_bytes", "sparse_attn_bwd", "skv_timing_enable", "skv_timing_collect")
 
 
 def last_error() -> str:
@@ -120,6 +128,19 @@ def _stream(stream) -> Optional[int]:
 # ---------------------------------------------------------------------------
 # Host calls
 # ---------------------------------------------------------------------------
+
+def timing_enable(on: bool = True):
+    """Bracket every library kernel launch with HIP events on its stream."""
+    _check(lib.skv_timing_enable(1 if on else 0))
+
+
+def timing_collect() -> dict:
+    """{kernel name: (launches, total ms)} since the last collect (waits for the events)."""
+    n = C.c_int32(0)
+    buf = (skv_kernel_time * 16)()  # more entries than the library has kernels
+    _check(lib.skv_timing_collect(buf, len(buf), C.byref(n)))
+    return {buf[i].name.decode(): (int(buf[i].launches), float(buf[i].total_ms)) for i in range(min(n.value, len(buf)))}
+
 
 def lpt_plan(cost, n_workers: int):
     """LPT planning (host).  Returns (assign int32, order int64, worker_off int64, load int64)."""
@@ -235,7 +256,7 @@ class Plan:
         self.d_worker_off = torch.from_numpy(off).to(problem.device)
         self.d_claim = torch.zeros(n_workers, dtype=torch.int32, device=problem.device)
         self.c = skv_plan(kind, n_workers, len(items), self.d_items.data_ptr(), self.d_worker_off.data_ptr(),
-                          self.d_claim.data_ptr())
+                          self.d_claim.data_ptr(), 0, 0, None)
 
     @property
     def imbalance(self) -> float:

@@ -18,6 +18,7 @@ int check_plan(const skv_plan* plan, int32_t kind) {
   if (plan->n_items < 0) return fail(SKV_EPLAN, "plan has a negative item count");
   if (!plan->d_worker_off || !plan->d_claim || (plan->n_items > 0 && !plan->d_items))
     return fail(SKV_EPLAN, "plan arrays are NULL");
+  if (plan->flags & ~SKV_PLAN_NO_STEAL) return fail(SKV_EPLAN, "unknown plan flags 0x%x", plan->flags);
   return SKV_OK;
 }
 
@@ -49,6 +50,7 @@ extern "C" int sparse_attn_partial_fwd(const skv_problem* p, const skv_plan* pla
   a.kv_st = p->kv_stride_tok; a.kv_sh = p->kv_stride_head;
   a.q_off = p->d_q_off; a.kv_off = p->d_kv_off; a.anchor = p->d_anchor;
   a.items = plan->d_items; a.worker_off = plan->d_worker_off; a.claim = plan->d_claim;
+  a.ticks = plan->d_ticks; a.steal = !(plan->flags & SKV_PLAN_NO_STEAL);
   a.o_part = o_part; a.m_part = m_part; a.lse_part = lse_part;
   a.block = p->block; a.group = p->hq / p->hkv; a.hq = p->hq; a.chunk = p->chunk;
   a.fd_block = FastDiv::make(a.block); a.fd_group = FastDiv::make(a.group); a.fd_gb = FastDiv::make(a.block * a.group);
@@ -122,6 +124,8 @@ extern "C" int sparse_attn_bwd(const skv_problem* p, const skv_plan* plan_kv, co
   if ((rc = check_plan(plan_kv, SKV_ITEM_BWD))) return rc;
   if ((rc = check_plan(plan_q, SKV_ITEM_FWD))) return rc;
   if (plan_kv->d_claim == plan_q->d_claim) return fail(SKV_EPLAN, "the two plans must not share claim cursors");
+  if (plan_kv->d_ticks && plan_kv->d_ticks == plan_q->d_ticks)
+    return fail(SKV_EPLAN, "the two plans must not share a ticks array");
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return fail(SKV_EINVAL, "tensor pointer is NULL");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) || !aligned16(dq))
     return fail(SKV_ESHAPE, "q, k, v, o, dout and dq must be 16-byte aligned");
@@ -140,6 +144,8 @@ extern "C" int sparse_attn_bwd(const skv_problem* p, const skv_plan* plan_kv, co
   a.q_off = p->d_q_off; a.kv_off = p->d_kv_off; a.anchor = p->d_anchor;
   a.kv_items = plan_kv->d_items; a.kv_worker_off = plan_kv->d_worker_off; a.kv_claim = plan_kv->d_claim;
   a.q_items = plan_q->d_items; a.q_worker_off = plan_q->d_worker_off; a.q_claim = plan_q->d_claim;
+  a.kv_ticks = plan_kv->d_ticks; a.kv_steal = !(plan_kv->flags & SKV_PLAN_NO_STEAL);
+  a.q_ticks = plan_q->d_ticks; a.q_steal = !(plan_q->flags & SKV_PLAN_NO_STEAL);
   a.total_q = p->h_q_off[p->n_seq];
   a.n_seq = p->n_seq; a.block = p->block; a.group = p->hq / p->hkv; a.hq = p->hq; a.hkv = p->hkv;
   a.chunk = p->chunk;

@@ -27,6 +27,7 @@
 //   4. finalize: dQ = scale * sum of the row's visible chunk partials, bf16.
 #include "device.h"
 #include "launch.h"
+#include "timing.h"
 
 namespace skv {
 namespace {
@@ -113,9 +114,11 @@ void bwd_kv_kernel(BwdArgs a) {
   const int GB = a.group * a.block;
   const float c = a.scale_log2;
 
-  int victim = plan_worker(), visited = 0;
+  const uint64_t t_start = __builtin_amdgcn_s_memrealtime();
+  const int me = plan_worker();
+  int victim = me, visited = 0;
   for (;;) {
-    const int64_t slot = claim_next(a.kv_worker_off, a.kv_claim, victim, visited, &s_claim);
+    const int64_t slot = claim_next(a.kv_worker_off, a.kv_claim, victim, visited, &s_claim, a.kv_steal);
     if (slot < 0) break;
     const skv_item it = a.kv_items[slot];
     const int s = it.seq, g = it.kv_head;
@@ -322,6 +325,7 @@ void bwd_kv_kernel(BwdArgs a) {
         }
     }
   }
+  record_ticks(a.kv_ticks, me, t_start);
 }
 
 // ---------------------------------------------------------------------------
@@ -388,9 +392,11 @@ void bwd_dq_kernel(BwdArgs a) {
   const float c = a.scale_log2;
   const uint16_t* my_dO = sdO + (wave * 64 + l32) * LDS_ROW + hf * 8;  // this lane's row, nt = 0
 
-  int victim = plan_worker(), visited = 0;
+  const uint64_t t_start = __builtin_amdgcn_s_memrealtime();
+  const int me = plan_worker();
+  int victim = me, visited = 0;
   for (;;) {
-    const int64_t slot = claim_next(a.q_worker_off, a.q_claim, victim, visited, &s_claim);
+    const int64_t slot = claim_next(a.q_worker_off, a.q_claim, victim, visited, &s_claim, a.q_steal);
     if (slot < 0) break;
     const skv_item it = a.q_items[slot];
     const int s = it.seq;
@@ -540,6 +546,7 @@ void bwd_dq_kernel(BwdArgs a) {
       }
     }
   }
+  record_ticks(a.q_ticks, me, t_start);
 }
 
 // ---------------------------------------------------------------------------
@@ -578,17 +585,28 @@ __global__ __launch_bounds__(256) void bwd_finalize_kernel(BwdArgs a) {
 
 hipError_t launch_bwd_bf16(const BwdArgs& a, int kv_workers, int q_workers, hipStream_t stream) {
   const int64_t rows = a.total_q * a.hq;
-  hipLaunchKernelGGL(part_base_kernel, dim3(1), dim3(64), 0, stream, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  hipError_t e;
+  {
+    TimedLaunch t(kBwdPartBase, stream);
+    hipLaunchKernelGGL(part_base_kernel, dim3(1), dim3(64), 0, stream, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   if (rows > 0) {
+    TimedLaunch t(kBwdDelta, stream);
     hipLaunchKernelGGL(bwd_pre_kernel, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(bwd_kv_kernel, dim3(kv_workers), dim3(256), 0, stream, a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_dq_kernel, dim3(q_workers), dim3(256), 0, stream, a);
-  if ((e = hipGetLastError()) != hipSuccess || rows == 0) return e;
+  {
+    TimedLaunch t(kBwdKv, stream);
+    hipLaunchKernelGGL(bwd_kv_kernel, dim3(kv_workers), dim3(256), 0, stream, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  {
+    TimedLaunch t(kBwdDq, stream);
+    hipLaunchKernelGGL(bwd_dq_kernel, dim3(q_workers), dim3(256), 0, stream, a);
+    if ((e = hipGetLastError()) != hipSuccess || rows == 0) return e;
+  }
+  TimedLaunch t(kBwdFinalize, stream);
   hipLaunchKernelGGL(bwd_finalize_kernel, dim3((unsigned)((rows + 7) / 8)), dim3(256), 0, stream, a);
   return hipGetLastError();
 }

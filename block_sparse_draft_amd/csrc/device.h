@@ -87,14 +87,16 @@ __device__ __forceinline__ int plan_worker() {
   return (w & 7) == 0 ? (b & 7) * (w >> 3) + (b >> 3) : b;
 }
 
-// Next plan slot for this workgroup, or -1 when every item is claimed.  The
+// Next plan slot for this workgroup, or -1 when its work is done.  The
 // workgroup first claims the items of list `victim` (its own list at start)
-// through the cursor claim[victim]; an exhausted list moves it on to the next
-// worker's list.  Uniform across the workgroup (contains barriers).
+// through the cursor claim[victim]; with `steal`, an exhausted list moves it on
+// to the next worker's list, otherwise it stops there.  Uniform across the
+// workgroup (contains barriers).
 __device__ __forceinline__ int64_t claim_next(const int64_t* worker_off, int32_t* claim, int& victim, int& visited,
-                                              int* s_claim) {
+                                              int* s_claim, bool steal) {
   const int W = gridDim.x;
-  while (visited < W) {
+  const int lists = steal ? W : 1;
+  while (visited < lists) {
     if (threadIdx.x == 0) *s_claim = atomicAdd(&claim[victim], 1);
     __syncthreads();
     const int idx = *s_claim;
@@ -105,6 +107,12 @@ __device__ __forceinline__ int64_t claim_next(const int64_t* worker_off, int32_t
     ++visited;
   }
   return -1;
+}
+
+// Busy time of a workgroup in s_memrealtime ticks (100 MHz), written by its
+// first thread to ticks[worker] when `ticks` is not NULL.
+__device__ __forceinline__ void record_ticks(int64_t* ticks, int worker, uint64_t t_start) {
+  if (ticks && threadIdx.x == 0) ticks[worker] = (int64_t)(__builtin_amdgcn_s_memrealtime() - t_start);
 }
 
 }  // namespace skv

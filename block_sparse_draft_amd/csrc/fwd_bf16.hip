@@ -27,6 +27,7 @@
 // order inside each 16-key step is permuted identically on both operands).
 #include "device.h"
 #include "launch.h"
+#include "timing.h"
 
 namespace skv {
 namespace {
@@ -95,9 +96,11 @@ void fwd_bf16_kernel(FwdArgs a) {
   const float c = a.scale_log2;
 
   __shared__ int s_claim;
-  int victim = plan_worker(), visited = 0;
+  const uint64_t t_start = __builtin_amdgcn_s_memrealtime();
+  const int me = plan_worker();
+  int victim = me, visited = 0;
   for (;;) {
-    const int64_t slot = claim_next(a.worker_off, a.claim, victim, visited, &s_claim);
+    const int64_t slot = claim_next(a.worker_off, a.claim, victim, visited, &s_claim, a.steal);
     if (slot < 0) break;
     const skv_item it = a.items[slot];
     const int s = it.seq;
@@ -283,6 +286,7 @@ void fwd_bf16_kernel(FwdArgs a) {
       }
     }
   }
+  record_ticks(a.ticks, me, t_start);
 }
 
 // Resets the per-worker claim cursors of a plan before a launch.
@@ -294,11 +298,13 @@ __global__ void claim_reset_kernel(int32_t* claim, int n) {
 }  // namespace
 
 hipError_t launch_claim_reset(int32_t* claim, int n_workers, hipStream_t stream) {
+  TimedLaunch t(kClaimReset, stream);
   hipLaunchKernelGGL(claim_reset_kernel, dim3((n_workers + 255) / 256), dim3(256), 0, stream, claim, n_workers);
   return hipGetLastError();
 }
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, int n_workers, hipStream_t stream) {
+  TimedLaunch t(kFwdBf16, stream);
   hipLaunchKernelGGL(fwd_bf16_kernel, dim3(n_workers), dim3(256), 0, stream, a);
   return hipGetLastError();
 }

@@ -7,6 +7,7 @@
 // walks the row's visible keys of the chunk one by one with an online softmax.
 #include "device.h"
 #include "launch.h"
+#include "timing.h"
 
 namespace skv {
 namespace {
@@ -17,6 +18,7 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdArgs a) {
   const float* K = static_cast<const float*>(a.k);
   const float* V = static_cast<const float*>(a.v);
   const int GB = a.group * a.block;
+  const uint64_t t_start = __builtin_amdgcn_s_memrealtime();
   const int64_t slot_end = a.worker_off[blockIdx.x + 1];
   for (int64_t slot = a.worker_off[blockIdx.x]; slot < slot_end; ++slot) {
     const skv_item it = a.items[slot];
@@ -70,11 +72,13 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdArgs a) {
       for (int x = 0; x < D; ++x) op[x] = o[x];
     }
   }
+  record_ticks(a.ticks, blockIdx.x, t_start);
 }
 
 }  // namespace
 
 hipError_t launch_fwd_f32(const FwdArgs& a, int d, int n_workers, hipStream_t stream) {
+  TimedLaunch t(kFwdF32, stream);
   if (d == 64)
     hipLaunchKernelGGL(fwd_f32_kernel<64>, dim3(n_workers), dim3(256), 0, stream, a);
   else

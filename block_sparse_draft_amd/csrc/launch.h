@@ -20,6 +20,8 @@ struct FwdArgs {
   const skv_item* items;
   const int64_t* worker_off;
   int32_t* claim;
+  int64_t* ticks;  // optional per-workgroup busy time
+  int32_t steal;   // claim from other workers' lists once the own list is done
   float* o_part;
   float* m_part;
   float* lse_part;
@@ -59,9 +61,12 @@ struct BwdArgs {
   const skv_item* kv_items;      // BWD plan: key ranges
   const int64_t* kv_worker_off;
   int32_t* kv_claim;
+  int64_t* kv_ticks;
   const skv_item* q_items;       // FWD plan: draft-block ranges of one chunk
   const int64_t* q_worker_off;
   int32_t* q_claim;
+  int64_t* q_ticks;
+  int32_t kv_steal, q_steal;
   int64_t total_q;  // sum Mq
   int32_t n_seq, block, group, hq, hkv, chunk;
   FastDiv fd_block, fd_group, fd_gb;  // division by block, hq/hkv and their product

@@ -11,6 +11,7 @@
 // their (unwritten) rows are never read.
 #include "device.h"
 #include "launch.h"
+#include "timing.h"
 
 namespace skv {
 namespace {
@@ -115,6 +116,7 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
 hipError_t launch_merge(const MergeArgs& a, int d, hipStream_t stream) {
   if (a.mq == 0) return hipSuccess;
   dim3 grid((unsigned)((a.mq + MROWS - 1) / MROWS), (unsigned)a.hq);
+  TimedLaunch t(kMerge, stream);
   if (d == 64)
     hipLaunchKernelGGL(merge_kernel<64>, grid, dim3(256), 0, stream, a);
   else

@@ -25,9 +25,11 @@ class _PlanSlots:
     next step's plan uploads (asynchronously, on the compute stream) while the
     previous step's kernels may still read the other pair."""
 
-    def __init__(self, problem: B.Problem, kind: int, granule: int, n_workers: int, policy: str):
+    def __init__(self, problem: B.Problem, kind: int, granule: int, n_workers: int, policy: str,
+                 steal: bool = True, ticks: bool = False):
         import torch
         self.problem, self.kind, self.granule, self.n_workers, self.policy = problem, kind, granule, n_workers, policy
+        self.flags = 0 if steal else B.SKV_PLAN_NO_STEAL
         n = len(problem.item_table(kind, granule)[1])
         dev = problem.device
         self.n_items = n
@@ -40,12 +42,18 @@ class _PlanSlots:
                 "d_off": torch.empty(n_workers + 1, dtype=torch.int64, device=dev),
                 "event": torch.cuda.Event(), "used": False})
         self.claim = torch.zeros(n_workers, dtype=torch.int32, device=dev)  # reset by the library per call
+        # per-workgroup busy time (100 MHz ticks) of the last call, when asked for
+        self.ticks = torch.zeros(n_workers, dtype=torch.int64, device=dev) if ticks else None
         self.next = 0
+        self.plan_s = 0.0
         self.c = None
         self.load = self.cost = None
 
     def replan(self):
-        """Realized costs -> LPT (or static) plan -> async upload.  Returns the skv_plan."""
+        """Realized costs -> LPT (or static) plan -> async upload.  Returns the skv_plan.
+        ``plan_s`` receives the host planning time (cost model, plan, gather)."""
+        import time
+        t0 = time.perf_counter()
         items, cost, tok, total = self.problem.item_table(self.kind, self.granule)
         if self.policy == "lpt":
             _, order, off, load = B.lpt_plan(cost, self.n_workers)
@@ -54,11 +62,13 @@ class _PlanSlots:
             load = np.bincount(assign, weights=cost, minlength=self.n_workers).astype(np.int64)
         else:
             raise ValueError(self.policy)
+        gathered = B.skv_gather_items(items, order).view(np.uint8)
+        self.plan_s = time.perf_counter() - t0
         slot = self.slots[self.next]
         self.next ^= 1
         if slot["used"]:
             slot["event"].synchronize()   # its previous upload has left the pinned buffer
-        slot["h_items"].numpy()[:len(items) * 32] = B.skv_gather_items(items, order).view(np.uint8)
+        slot["h_items"].numpy()[:len(items) * 32] = gathered
         slot["h_off"].numpy()[:] = off
         slot["d_items"].copy_(slot["h_items"], non_blocking=True)
         slot["d_off"].copy_(slot["h_off"], non_blocking=True)
@@ -66,7 +76,8 @@ class _PlanSlots:
         slot["used"] = True
         self.cost, self.load = cost, load
         self.c = B.skv_plan(self.kind, self.n_workers, len(items), slot["d_items"].data_ptr(),
-                            slot["d_off"].data_ptr(), self.claim.data_ptr())
+                            slot["d_off"].data_ptr(), self.claim.data_ptr(), self.flags, 0,
+                            None if self.ticks is None else self.ticks.data_ptr())
         return self.c
 
     @property
@@ -86,7 +97,7 @@ class SplitKVAttention:
     def __init__(self, q_off, kv_off, anchors, block: int, hq: int, hkv: int, d: int, chunk: int,
                  sm_scale: float, dtype, device, n_workers: Optional[int] = None,
                  fwd_granule: Optional[int] = None, bwd_granule: int = 256, policy: str = "lpt",
-                 with_bwd: bool = True):
+                 with_bwd: bool = True, steal: bool = True, ticks: bool = False):
         import torch
         self.device = torch.device(device)
         self.dtype = dtype
@@ -98,11 +109,12 @@ class SplitKVAttention:
         G = hq // hkv
         self.fwd_granule = fwd_granule or max(1, 256 // (G * block))
         self.bwd_granule = bwd_granule
-        self.fwd_plan = _PlanSlots(self.problem, B.SKV_ITEM_FWD, self.fwd_granule, self.n_workers, policy)
-        self.bwd_plan = (_PlanSlots(self.problem, B.SKV_ITEM_BWD, self.bwd_granule, self.n_workers, policy)
+        kw = dict(steal=steal, ticks=ticks)
+        self.fwd_plan = _PlanSlots(self.problem, B.SKV_ITEM_FWD, self.fwd_granule, self.n_workers, policy, **kw)
+        self.bwd_plan = (_PlanSlots(self.problem, B.SKV_ITEM_BWD, self.bwd_granule, self.n_workers, policy, **kw)
                          if with_bwd else None)
         # dQ runs over the forward's items; its own slots give it separate claim cursors
-        self.dq_plan = (_PlanSlots(self.problem, B.SKV_ITEM_FWD, self.fwd_granule, self.n_workers, policy)
+        self.dq_plan = (_PlanSlots(self.problem, B.SKV_ITEM_FWD, self.fwd_granule, self.n_workers, policy, **kw)
                         if with_bwd else None)
         self.replan()
         self.part_base, self.n_chunk = self.problem.partial_layout()
@@ -122,9 +134,11 @@ class SplitKVAttention:
     def replan(self):
         """Mask descriptor -> realized cost per item -> LPT plan, uploaded for the next kernels."""
         self.fwd_plan.replan()
+        self.plan_s = self.fwd_plan.plan_s
         if self.bwd_plan is not None:
             self.bwd_plan.replan()
             self.dq_plan.replan()
+            self.plan_s += self.bwd_plan.plan_s + self.dq_plan.plan_s
 
     def partial_fwd(self, q, k, v, stream=None):
         B.sparse_attn_partial_fwd(self.problem, self.fwd_plan, q, k, v, self.o_part, self.m_part, self.lse_part,

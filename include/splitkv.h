@@ -102,7 +102,13 @@ typedef struct skv_item {
  * delays the call by at most the item it holds.  Every item is processed
  * exactly once.  d_claim is caller-owned scratch of n_workers int32 that the
  * library resets at the start of every call; two calls in flight at the same
- * time must not share it. */
+ * time must not share it.
+ * flags: SKV_PLAN_NO_STEAL makes every worker run exactly its own list (the
+ * plan's assignment as computed, for measuring a plan's balance); the fp32
+ * forward never steals.  d_ticks (optional, NULL = off): device int64
+ * [n_workers]; the call writes each worker's busy time, from its start to
+ * finding no more work, in ticks of the 100 MHz s_memrealtime clock. */
+enum { SKV_PLAN_NO_STEAL = 1 };
 typedef struct skv_plan {
   int32_t kind;       /* skv_item_kind */
   int32_t n_workers;  /* >= 1 */
@@ -110,6 +116,9 @@ typedef struct skv_plan {
   const skv_item* d_items;      /* device, [n_items] */
   const int64_t* d_worker_off;  /* device, [n_workers+1], d_worker_off[0] = 0 */
   int32_t* d_claim;             /* device scratch, [n_workers] */
+  int32_t flags;                /* 0 or SKV_PLAN_NO_STEAL */
+  int32_t reserved;             /* 0 */
+  int64_t* d_ticks;             /* device, [n_workers], optional */
 } skv_plan;
 
 /* Thread-local description of the last error (never NULL). */
@@ -207,6 +216,25 @@ size_t skv_bwd_workspace_bytes(const skv_problem* p);
 int sparse_attn_bwd(const skv_problem* p, const skv_plan* plan_kv, const skv_plan* plan_q, const void* q,
                     const void* k, const void* v, const void* o, const float* lse, const void* dout, void* dq,
                     void* dk, void* dv, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---- Instrumentation (host) ----
+ * Per-kernel timing with HIP events, off by default.  While enabled, every
+ * kernel the library launches is bracketed by two events recorded on the
+ * stream it is launched on (the library creates and reuses the events; this
+ * adds a few microseconds per launch and must stay off under graph capture).
+ * skv_timing_collect waits for every recorded event, writes per kernel name
+ * the number of launches and their summed event-to-event time into
+ * out[0 .. min(max_entries, *n_entries)) and resets the tallies; *n_entries
+ * receives the number of kernels with at least one launch.  Kernel names:
+ * "claim_reset", "partial_fwd_bf16", "partial_fwd_f32", "lse_merge",
+ * "bwd_part_base", "bwd_delta", "bwd_kv", "bwd_dq", "bwd_finalize". */
+typedef struct skv_kernel_time {
+  const char* name;   /* static string */
+  int64_t launches;
+  double total_ms;
+} skv_kernel_time;
+int skv_timing_enable(int32_t on);
+int skv_timing_collect(skv_kernel_time* out, int32_t max_entries, int32_t* n_entries);
 
 #ifdef __cplusplus
 }

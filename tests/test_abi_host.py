@@ -190,6 +190,13 @@ def test_device_calls_reject_bad_arguments_before_touching_the_gpu():
     assert rc == B.SKV_EPLAN                       # second plan must be a forward plan
     rc = B.lib.sparse_attn_bwd(C.byref(pb.c), C.byref(bplan), C.byref(plan), *([fake] * 10), need, None)
     assert rc == B.SKV_EPLAN                       # shared claim cursors are rejected
+    tk = B.skv_plan(B.SKV_ITEM_BWD, 4, 1, 16, 16, 48, 0, 0, 64)
+    tq = B.skv_plan(B.SKV_ITEM_FWD, 4, 1, 16, 16, 32, 0, 0, 64)
+    rc = B.lib.sparse_attn_bwd(C.byref(pb.c), C.byref(tk), C.byref(tq), *([fake] * 10), need, None)
+    assert rc == B.SKV_EPLAN and "ticks" in B.last_error()   # shared ticks arrays are rejected
+    badflags = B.skv_plan(B.SKV_ITEM_FWD, 4, 1, 16, 16, 16, 2, 0, None)
+    rc = B.lib.sparse_attn_partial_fwd(C.byref(p.c), C.byref(badflags), fake, fake, fake, fake, fake, fake, None)
+    assert rc == B.SKV_EPLAN and "flags" in B.last_error()
     # merge
     rc = B.lib.lse_merge(4, 2, 64, 96, fake, fake, fake, fake, 128, 64, B.SKV_F32, fake, 2, None)
     assert rc == B.SKV_ESHAPE
@@ -198,3 +205,20 @@ def test_device_calls_reject_bad_arguments_before_touching_the_gpu():
     rc = B.lib.lse_merge(4, 2, 64, 64, fake, fake, fake, fake, 128, 64, 5, fake, 2, None)
     assert rc == B.SKV_EDTYPE
     assert B.lib.lse_merge(4, 2, 0, 64, None, None, None, None, 128, 64, B.SKV_F32, None, 2, None) == B.SKV_OK
+
+
+def test_timing_api_without_launches():
+    """Timing switches on and off and collects an empty tally without any GPU work."""
+    B.timing_enable(True)
+    assert B.timing_collect() == {}
+    B.timing_enable(False)
+    assert B.timing_collect() == {}
+    n = C.c_int32(-1)
+    assert B.lib.skv_timing_collect(None, 0, C.byref(n)) == B.SKV_OK and n.value == 0
+    assert B.lib.skv_timing_collect(None, 3, C.byref(n)) == B.SKV_EINVAL
+
+
+def test_plan_struct_layout():
+    """skv_plan as the header lays it out on LP64: 56 bytes, d_ticks last."""
+    assert C.sizeof(B.skv_plan) == 56
+    assert B.skv_plan.flags.offset == 40 and B.skv_plan.d_ticks.offset == 48

@@ -269,3 +269,32 @@ def test_identical_keys_and_constant_values():
     for h in range(w.cfg.hq):
         vv = w.as_f64("v", rows=slice(5, 6))[0, h // 2]
         assert np.abs(o[:, h] - vv).max() <= 2 ** -7 * np.abs(vv).max()
+
+
+def test_backward_bitwise_deterministic_across_plans_and_stealing():
+    """The backward has no atomics: dQ, dK, dV are bitwise the same on a rerun,
+    under the static plan and with tail stealing off; every workgroup reports
+    its busy time when asked."""
+    w = make("c3", seed=6, with_do=True, n_ctx_range=(2000, 7000), n_anchor=12, hq=8, hkv=2, chunk=1024)
+    q, k, v = _upload(w)
+    ref = None
+    for kw in (dict(), dict(), dict(policy="static"), dict(steal=False, ticks=True),
+               dict(policy="static", steal=False, ticks=True)):
+        path = make_path(w, DEV, with_bwd=True, bwd_granule=128, **kw)
+        do = to_device(w, "do", DEV)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        path.forward(q, k, v)
+        path.backward(q, k, v, do, dq, dk, dv)
+        torch.cuda.synchronize()
+        got = (path.o.clone(), path.lse.clone(), dq, dk, dv)
+        if ref is None:
+            ref = got
+            _check_grads(w, (to_np64(dq), to_np64(dk), to_np64(dv)))
+        else:
+            for name, a, b in zip(("O", "LSE", "dQ", "dK", "dV"), ref, got):
+                assert torch.equal(a, b), f"{name} differs under {kw}"
+        if kw.get("ticks"):
+            for plan in (path.fwd_plan, path.bwd_plan, path.dq_plan):
+                t = plan.ticks.cpu().numpy()
+                busy = np.diff(plan.slots[(plan.next + 1) % 2]["h_off"].numpy()) > 0
+                assert (t >= 0).all() and (t[busy] > 0).all()
