@@ -12,8 +12,8 @@ Sources followed (pages as published, cited by title and section):
   [P3] arXiv:2611.05926 listing "Split-KV: Efficient Context Parallelism for
        Training Diffusion Drafters" — Abstract.
 
-Readings of points the pages leave open are listed in each function's
-docstring and collected in DESIGN.md.
+Readings of points the pages leave open are stated in each function's
+docstring.
 
 Parity status: every function here is pinned by tests under ``tests/`` marked
 ``not gpu`` (brute force, closed forms, library special cases, finite
