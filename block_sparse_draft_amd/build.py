@@ -38,10 +38,18 @@ def _flags():
             "-mllvm", "-amdgpu-mfma-vgpr-form"]
 
 
+# The attention kernels never see NaN inputs on purpose; without IEEE mode the
+# row maxima compile to plain v_max_f32 / v_max3_f32 (no quieting of inputs).
+EXTRA_FLAGS = {
+    "fwd_bf16.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"],
+    "bwd_bf16.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"],
+}
+
+
 def _compile(src: str) -> str:
     os.makedirs(BUILD, exist_ok=True)
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc()] + _flags() + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc()] + _flags() + EXTRA_FLAGS.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -42,6 +42,11 @@ __device__ __forceinline__ bf16x8 lds_load_bf16x8(const uint16_t* p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p));
 }
 
+// 32-bit LDS byte address of a pointer into shared memory.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)(p);
+}
+
 // Two transposed 4 x 16 reads (see the header comment) joined into one MFMA operand.
 __device__ __forceinline__ bf16x8 lds_tr_pair(const uint16_t* p0, const uint16_t* p1) {
   i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p0));
@@ -49,6 +54,23 @@ __device__ __forceinline__ bf16x8 lds_tr_pair(const uint16_t* p0, const uint16_t
   typedef short i16x8 __attribute__((ext_vector_type(8)));
   i16x8 c = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
   return __builtin_bit_cast(bf16x8, c);
+}
+
+// The same from 32-bit LDS byte addresses, so that constant offsets fold into
+// the instructions' immediate offset fields.
+__device__ __forceinline__ bf16x8 lds_tr_pair(uint32_t a0, uint32_t a1) {
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)a0);
+  i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)a1);
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  i16x8 c = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  return __builtin_bit_cast(bf16x8, c);
+}
+
+// 16-byte LDS read from a 32-bit LDS byte address.
+__device__ __forceinline__ bf16x8 lds_read_b128(uint32_t addr) {
+  typedef __attribute__((address_space(3))) const uint4 lds_u4;
+  return __builtin_bit_cast(bf16x8, *(lds_u4*)(uintptr_t)addr);
 }
 
 // Round-to-nearest-even fp32 -> bf16 of 8 consecutive values.

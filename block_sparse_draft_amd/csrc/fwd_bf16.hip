@@ -4,27 +4,29 @@
 // (pages: Split-KV article, "Split-KV's Core Mechanism": each KV shard stays
 // local and yields a query-sized result that is later aggregated exactly).
 //
-// Persistent workgroups: each runs the work items the planner gave its worker,
-// then claims whatever is left on other workers' lists.
-// An item is (sequence, KV head g with its G query heads, chunk c, draft
-// blocks [lo, hi)).  Its query rows are packed block-major as
-// p = ((b - lo) * G + head) * B + token, 256 rows per pass: 4 waves x 64 rows.
-// Each wave keeps its 64 Q rows in registers and the unnormalised O^T
-// (128 x 64, fp32) in accumulators.  Only the 64-key tiles that some row of
+// Persistent workgroups of 8 waves (two per SIMD, so one wave's softmax and
+// memory waits overlap the other's MFMA work): each runs the work items the
+// planner gave its worker, then claims whatever is left on other workers'
+// lists.  An item is (sequence, KV head g with its G query heads, chunk c,
+// draft blocks [lo, hi)).  Its query rows are packed block-major as
+// p = ((b - lo) * G + head) * B + token, 256 rows per pass: 8 waves x 32 rows.
+// Each wave keeps its 32 Q rows in registers and the unnormalised O^T
+// (128 x 32, fp32) in accumulators.  Only the 64-key tiles that some row of
 // the pass sees are visited; the rest of the chunk is never read.
 //
 // Pipeline: K/V tiles rotate through three LDS buffers.  While tile t is
 // computed, tile t+1 sits in LDS and tile t+2 is in flight from memory into
-// registers, so a single barrier per tile suffices and load latency hides
-// behind a tile of MFMA work.
+// registers, so a single barrier per tile suffices.  K is staged row-major;
+// V is staged transposed (V^T, one row per head-dim index), its keys permuted
+// within each 16-key group to the order the PV product consumes them, so every
+// MFMA operand read is one 16-byte LDS read.
 //
-// Per key tile and wave:  S^T = K Q^T (MFMA 32x32x16, K from LDS), masking of
-// keys at or beyond the row's prefix end e_b (partial tiles only), online
-// softmax in the exp2 domain with lazy rescaling (the reference maximum only
-// moves when the true maximum exceeds it by 2^8; the output is corrected to
-// the true maximum once per item), O^T += V^T P^T with V^T read from LDS by
-// ds_read_b64_tr_b16 and P^T taken straight from the S^T accumulators (the key
-// order inside each 16-key step is permuted identically on both operands).
+// Per key tile and wave:  S^T = K Q^T (MFMA 32x32x16), masking of keys at or
+// beyond the row's prefix end e_b (partial tiles only), online softmax in the
+// exp2 domain with lazy rescaling (the reference maximum only moves when the
+// true maximum exceeds it by 2^8; the output is corrected to the true maximum
+// once per item), O^T += V^T P^T with P^T taken straight from the S^T
+// accumulators.
 #include "device.h"
 #include "launch.h"
 #include "timing.h"
@@ -33,17 +35,24 @@ namespace skv {
 namespace {
 
 constexpr int D = 128;
-constexpr int KT = 64;             // keys per tile
-constexpr int NWAVE = 4;
-constexpr int ROWS = 64 * NWAVE;   // packed query rows per pass
-constexpr int LDS_ROW = D + 8;     // bf16 per staged key row (272 bytes: conflict-free 16-byte reads)
-constexpr int TILE_ELEMS = KT * LDS_ROW;
+constexpr int KT = 64;              // keys per tile
+constexpr int NWAVE = 8;
+constexpr int NTHR = 64 * NWAVE;
+constexpr int ROWS = 32 * NWAVE;    // packed query rows per pass
 constexpr int NBUF = 3;
-constexpr float LAZY_LOG2 = 8.f;   // rescale only when the max grows by more than 2^8
+constexpr float LAZY_LOG2 = 8.f;    // rescale only when the max grows by more than 2^8
+// Padded LDS rows: 272-byte K rows and 144-byte V^T rows put the 16-byte
+// operand reads of 8 consecutive rows in distinct banks.
+constexpr int LDS_ROW_K = D + 8;
+constexpr int LDS_ROW_VT = KT + 8;
+constexpr int TILE_K = KT * LDS_ROW_K;
+constexpr int TILE_VT = D * LDS_ROW_VT;
 
-// Staging registers of one K/V tile: each thread moves 4 x 16 bytes of K and of V.
+// Staging registers of one K/V tile.  K: 2 x 16 bytes (rows r and r + 32,
+// 8 head-dim values each).  V: 4 keys x 4 head-dim values (8 bytes per key).
 struct TileRegs {
-  uint4 k0, k1, k2, k3, v0, v1, v2, v3;
+  uint4 k0, k1;
+  uint2 v0, v1, v2, v3;
 };
 
 // Issue the loads of key tile [kb, kb+64) (sequence-relative).  Keys past the
@@ -51,44 +60,50 @@ struct TileRegs {
 __device__ __forceinline__ TileRegs load_tile(const uint16_t* Kseq, const uint16_t* Vseq, int kb, int n_ctx,
                                               int64_t kv_st, int tid) {
   TileRegs r;
-  const int64_t d8 = (tid & 15) * 8;
-  const int row = tid >> 4;  // 16 rows per 256 threads; rows row, row+16, row+32, row+48
-  const int64_t o0 = (int64_t)min(kb + row, n_ctx - 1) * kv_st + d8;
-  const int64_t o1 = (int64_t)min(kb + row + 16, n_ctx - 1) * kv_st + d8;
-  const int64_t o2 = (int64_t)min(kb + row + 32, n_ctx - 1) * kv_st + d8;
-  const int64_t o3 = (int64_t)min(kb + row + 48, n_ctx - 1) * kv_st + d8;
-  r.k0 = *reinterpret_cast<const uint4*>(Kseq + o0);
-  r.k1 = *reinterpret_cast<const uint4*>(Kseq + o1);
-  r.k2 = *reinterpret_cast<const uint4*>(Kseq + o2);
-  r.k3 = *reinterpret_cast<const uint4*>(Kseq + o3);
-  r.v0 = *reinterpret_cast<const uint4*>(Vseq + o0);
-  r.v1 = *reinterpret_cast<const uint4*>(Vseq + o1);
-  r.v2 = *reinterpret_cast<const uint4*>(Vseq + o2);
-  r.v3 = *reinterpret_cast<const uint4*>(Vseq + o3);
+  const int krow = tid >> 4;               // 0..31
+  const int64_t kd = (tid & 15) * 8;
+  r.k0 = *reinterpret_cast<const uint4*>(Kseq + (int64_t)min(kb + krow, n_ctx - 1) * kv_st + kd);
+  r.k1 = *reinterpret_cast<const uint4*>(Kseq + (int64_t)min(kb + krow + 32, n_ctx - 1) * kv_st + kd);
+  const int vk = (tid >> 5) * 4;           // 4 consecutive keys
+  const int64_t vd = (tid & 31) * 4;       // 4 consecutive head-dim values
+  r.v0 = *reinterpret_cast<const uint2*>(Vseq + (int64_t)min(kb + vk + 0, n_ctx - 1) * kv_st + vd);
+  r.v1 = *reinterpret_cast<const uint2*>(Vseq + (int64_t)min(kb + vk + 1, n_ctx - 1) * kv_st + vd);
+  r.v2 = *reinterpret_cast<const uint2*>(Vseq + (int64_t)min(kb + vk + 2, n_ctx - 1) * kv_st + vd);
+  r.v3 = *reinterpret_cast<const uint2*>(Vseq + (int64_t)min(kb + vk + 3, n_ctx - 1) * kv_st + vd);
   return r;
 }
 
-__device__ __forceinline__ void store_tile(TileRegs r, uint16_t* sK, uint16_t* sV, int tid) {
-  const int o = (tid >> 4) * LDS_ROW + (tid & 15) * 8;
-  constexpr int R16 = 16 * LDS_ROW;
-  *reinterpret_cast<uint4*>(sK + o) = r.k0;
-  *reinterpret_cast<uint4*>(sK + o + R16) = r.k1;
-  *reinterpret_cast<uint4*>(sK + o + 2 * R16) = r.k2;
-  *reinterpret_cast<uint4*>(sK + o + 3 * R16) = r.k3;
-  *reinterpret_cast<uint4*>(sV + o) = r.v0;
-  *reinterpret_cast<uint4*>(sV + o + R16) = r.v1;
-  *reinterpret_cast<uint4*>(sV + o + 2 * R16) = r.v2;
-  *reinterpret_cast<uint4*>(sV + o + 3 * R16) = r.v3;
+// Position of key kk (0..15) of a 16-key group inside a V^T row: lane half h
+// of the PV operand reads positions 8h..8h+7, which hold keys 4h..4h+3 and
+// 8+4h..8+4h+3 (the order the S^T accumulators deliver P^T in).
+__device__ __forceinline__ void store_tile(const TileRegs& r, uint16_t* sK, uint16_t* sVt, int tid) {
+  *reinterpret_cast<uint4*>(sK + (tid >> 4) * LDS_ROW_K + (tid & 15) * 8) = r.k0;
+  *reinterpret_cast<uint4*>(sK + ((tid >> 4) + 32) * LDS_ROW_K + (tid & 15) * 8) = r.k1;
+  // 4 keys x 4 values -> 4 rows of V^T with 4 keys each
+  const int kg = tid >> 5;                                  // keys 4kg .. 4kg+3
+  const int pos = (kg >> 2) * 16 + ((kg >> 1) & 1) * 4 + (kg & 1) * 8;
+  uint16_t* dst = sVt + (tid & 31) * 4 * LDS_ROW_VT + pos;
+  // byte selectors of v_perm_b32(hi, lo, sel): bytes 0-3 from lo, 4-7 from hi
+  const uint32_t lo16 = 0x05040100u, hi16 = 0x07060302u;
+  uint2 y0, y1, y2, y3;
+  y0.x = __builtin_amdgcn_perm(r.v1.x, r.v0.x, lo16); y0.y = __builtin_amdgcn_perm(r.v3.x, r.v2.x, lo16);
+  y1.x = __builtin_amdgcn_perm(r.v1.x, r.v0.x, hi16); y1.y = __builtin_amdgcn_perm(r.v3.x, r.v2.x, hi16);
+  y2.x = __builtin_amdgcn_perm(r.v1.y, r.v0.y, lo16); y2.y = __builtin_amdgcn_perm(r.v3.y, r.v2.y, lo16);
+  y3.x = __builtin_amdgcn_perm(r.v1.y, r.v0.y, hi16); y3.y = __builtin_amdgcn_perm(r.v3.y, r.v2.y, hi16);
+  *reinterpret_cast<uint2*>(dst) = y0;
+  *reinterpret_cast<uint2*>(dst + LDS_ROW_VT) = y1;
+  *reinterpret_cast<uint2*>(dst + 2 * LDS_ROW_VT) = y2;
+  *reinterpret_cast<uint2*>(dst + 3 * LDS_ROW_VT) = y3;
 }
 
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_bf16_kernel(FwdArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t sKV[NBUF][2][TILE_ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t sKb[NBUF][TILE_K];
+  __shared__ __attribute__((aligned(16))) uint16_t sVb[NBUF][TILE_VT];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hf = lane >> 5;
-  const int gi = lane >> 4, li = lane & 15;
   const uint16_t* Q = static_cast<const uint16_t*>(a.q);
   const uint16_t* K = static_cast<const uint16_t*>(a.k);
   const uint16_t* V = static_cast<const uint16_t*>(a.v);
@@ -121,165 +136,134 @@ void fwd_bf16_kernel(FwdArgs a) {
       const int wg_hi = max(klo, min(khi, min(a.anchor[blk0 + it.lo + a.fd_gb.div(p_last)] + a.block, n_ctx)));
       const int ntiles = (wg_hi - klo + KT - 1) / KT;
 
-      // ---- start the K/V pipeline around the loads of this lane's two Q rows ----
+      // ---- start the K/V pipeline around the loads of this lane's Q row ----
       TileRegs R;
       if (ntiles > 0) {
         __syncthreads();  // all waves are done with the previous pass's buffers
         R = load_tile(Kseq, Vseq, klo, n_ctx, a.kv_st, tid);
       }
-      int vend[2];          // visible keys of the row in this chunk: [klo, vend)
-      int64_t prow[2];      // partial row index
-      bool valid[2];
-      bf16x8 qf[2][8];
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        const int p = rt + wave * 64 + nt * 32 + l32;
-        valid[nt] = p < nrows;
-        const int pc = valid[nt] ? p : p_last;  // clamp: loads stay in bounds, results unused
-        const int b = it.lo + a.fd_gb.div(pc);
-        const int hl = a.fd_group.mod(a.fd_block.div(pc));
-        const int64_t r = (int64_t)b * a.block + a.fd_block.mod(pc);
-        const int h = it.kv_head * a.group + hl;
-        const int e = min(a.anchor[blk0 + b] + a.block, n_ctx);
-        vend[nt] = valid[nt] ? max(klo, min(khi, e)) : klo;
-        prow[nt] = it.part_base + (int64_t)h * mq + r;
+      const int p = rt + wave * 32 + l32;
+      const bool valid = p < nrows;
+      const int pc = valid ? p : p_last;  // clamp: loads stay in bounds, results unused
+      const int b = it.lo + a.fd_gb.div(pc);
+      const int hl = a.fd_group.mod(a.fd_block.div(pc));
+      const int64_t r = (int64_t)b * a.block + a.fd_block.mod(pc);
+      const int h = it.kv_head * a.group + hl;
+      const int e = min(a.anchor[blk0 + b] + a.block, n_ctx);
+      const int vend = valid ? max(klo, min(khi, e)) : klo;  // visible keys of the row: [klo, vend)
+      const int64_t prow = it.part_base + (int64_t)h * mq + r;
+      bf16x8 qf[8];
+      {
         const uint16_t* qp = Q + (q0 + r) * a.q_st + (int64_t)h * a.q_sh + hf * 8;
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) qf[nt][ks] = load_bf16x8(qp + ks * 16);
+        for (int ks = 0; ks < 8; ++ks) qf[ks] = load_bf16x8(qp + ks * 16);
       }
-      if (ntiles > 0) store_tile(R, sKV[0][0], sKV[0][1], tid);
+      if (ntiles > 0) store_tile(R, sKb[0], sVb[0], tid);
       // Drain every outstanding load (Q included) before the prefetch starts, so
-      // that inside the tile loop only the prefetch itself is in flight and no
-      // wait for it is needed before the S = K Q^T products.
+      // that inside the tile loop only the prefetch itself is in flight.
       __builtin_amdgcn_s_waitcnt(0);
       if (ntiles > 1) R = load_tile(Kseq, Vseq, klo + KT, n_ctx, a.kv_st, tid);
-      const int wave_hi = wave_max_i(max(vend[0], vend[1]));
-      const int wave_full = wave_min_i(min(valid[0] ? vend[0] : INT32_MAX, valid[1] ? vend[1] : INT32_MAX));
+      const int wave_hi = wave_max_i(vend);
+      const int wave_full = wave_min_i(valid ? vend : INT32_MAX);
 
-      float m_true[2] = {-INFINITY, -INFINITY};  // running row max of raw scores
-      float m_ref[2] = {-INFINITY, -INFINITY};   // max the exponentials are taken against
-      float l[2] = {0.f, 0.f};                   // this lane-half's running row sum
-      f32x16 acc_o[4][2];
+      float m_true = -INFINITY;  // running row max of raw scores
+      float m_ref = -INFINITY;   // max the exponentials are taken against
+      float l = 0.f;             // this lane-half's running row sum
+      f32x16 acc_o[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc_o[i][0] = acc_o[i][1] = f32x16{};
+      for (int i = 0; i < 4; ++i) acc_o[i] = f32x16{};
 
       for (int t = 0; t < ntiles; ++t) {
         const int kb = klo + t * KT;
         if (t + 1 < ntiles) {
-          store_tile(R, sKV[(t + 1) % NBUF][0], sKV[(t + 1) % NBUF][1], tid);
+          store_tile(R, sKb[(t + 1) % NBUF], sVb[(t + 1) % NBUF], tid);
           if (t + 2 < ntiles) R = load_tile(Kseq, Vseq, kb + 2 * KT, n_ctx, a.kv_st, tid);
         }
         __syncthreads();
         if (kb >= wave_hi) continue;  // no row of this wave sees the tile
-        const uint16_t* sK = sKV[t % NBUF][0];
-        const uint16_t* sV = sKV[t % NBUF][1];
+        // 32-bit LDS addresses of this lane's operand rows; the empty asm keeps
+        // the per-read offsets as immediates.
+        uint32_t ka = lds_addr(sKb[t % NBUF] + l32 * LDS_ROW_K + hf * 8);
+        uint32_t va = lds_addr(sVb[t % NBUF] + l32 * LDS_ROW_VT + hf * 8);
+        asm volatile("" : "+v"(ka), "+v"(va));
 
         // ---- S^T = K Q^T (raw scores) ----
-        f32x16 sacc[2][2];
-#pragma unroll
-        for (int i = 0; i < 2; ++i) sacc[i][0] = sacc[i][1] = f32x16{};
+        f32x16 sacc[2];
+        sacc[0] = sacc[1] = f32x16{};
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) {
 #pragma unroll
           for (int mt = 0; mt < 2; ++mt) {
-            const bf16x8 kf = lds_load_bf16x8(sK + (mt * 32 + l32) * LDS_ROW + ks * 16 + hf * 8);
-            sacc[mt][0] = mfma32x32x16(kf, qf[0][ks], sacc[mt][0]);
-            sacc[mt][1] = mfma32x32x16(kf, qf[1][ks], sacc[mt][1]);
+            const bf16x8 kf = lds_read_b128(ka + 2u * (mt * 32 * LDS_ROW_K + ks * 16));
+            sacc[mt] = mfma32x32x16(kf, qf[ks], sacc[mt]);
           }
         }
         // ---- mask keys at or past the row's prefix end (partial tiles only) ----
         if (kb + KT > wave_full) {
 #pragma unroll
-          for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-            for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-              for (int e = 0; e < 16; ++e) {
-                const int key = kb + mt * 32 + (e >> 2) * 8 + hf * 4 + (e & 3);
-                if (key >= vend[nt]) sacc[mt][nt][e] = -INFINITY;
-              }
-        }
-        // ---- row max; lazy rescale when some row's max grew past 2^8 ----
-        bool grow = false;
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-          float r0 = fmaxf(sacc[0][nt][0], sacc[1][nt][0]);
-#pragma unroll
-          for (int e = 1; e < 16; ++e) r0 = fmaxf(r0, fmaxf(sacc[0][nt][e], sacc[1][nt][e]));
-          r0 = fmaxf(r0, __shfl_xor(r0, 32));
-          m_true[nt] = fmaxf(m_true[nt], r0);
-          grow |= (m_true[nt] - m_ref[nt]) * c > LAZY_LOG2;  // false while both are -inf
-        }
-        if (__any(grow)) {
-#pragma unroll
-          for (int nt = 0; nt < 2; ++nt) {
-            const float alpha = fast_exp2((m_ref[nt] - m_true[nt]) * c);  // 0 from -inf, 1 if unchanged
-            const bool keep = m_true[nt] == -INFINITY;
-            m_ref[nt] = m_true[nt];
-            if (!keep) {
-              l[nt] *= alpha;
-#pragma unroll
-              for (int md = 0; md < 4; ++md) acc_o[md][nt] *= alpha;
-            }
-          }
-        }
-        // ---- P = exp2(s*c - m_ref*c) ----
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-          const float mc = m_ref[nt] == -INFINITY ? 0.f : m_ref[nt] * c;
-          float psum = 0.f;
-#pragma unroll
           for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-              const float pe = fast_exp2(__builtin_fmaf(sacc[mt][nt][e], c, -mc));
-              sacc[mt][nt][e] = pe;
-              psum += pe;
+            for (int e2 = 0; e2 < 16; ++e2) {
+              const int key = kb + mt * 32 + (e2 >> 2) * 8 + hf * 4 + (e2 & 3);
+              if (key >= vend) sacc[mt][e2] = -INFINITY;
             }
-          l[nt] += psum;
         }
-        // ---- O^T += V^T P^T ----
+        // ---- row max; lazy rescale when the row's max grew past 2^8 ----
+        float r0 = fmaxf(sacc[0][0], sacc[1][0]);
+#pragma unroll
+        for (int e2 = 1; e2 < 16; ++e2) r0 = fmaxf(r0, fmaxf(sacc[0][e2], sacc[1][e2]));
+        r0 = fmaxf(r0, __shfl_xor(r0, 32));
+        m_true = fmaxf(m_true, r0);
+        const bool grow = (m_true - m_ref) * c > LAZY_LOG2;  // false while both are -inf
+        if (__any(grow)) {
+          const float alpha = fast_exp2((m_ref - m_true) * c);  // 0 from -inf, 1 if unchanged
+          const bool keep = m_true == -INFINITY;
+          m_ref = m_true;
+          if (!keep) {
+            l *= alpha;
+#pragma unroll
+            for (int md = 0; md < 4; ++md) acc_o[md] *= alpha;
+          }
+        }
+        // ---- P = exp2(s*c - m_ref*c), 16 keys at a time right before their
+        //      part of O^T += V^T P^T; the row sum in fp32 (bf16-rounded P
+        //      would cost the log-sum-exp up to 2^-9 relative on short rows) ----
+        const float mc = m_ref == -INFINITY ? 0.f : m_ref * c;
 #pragma unroll
         for (int kstep = 0; kstep < 4; ++kstep) {
           const int mt = kstep >> 1, qh = (kstep & 1) * 8;
-          bf16x8 pf[2];
+          const f32x16& sv = sacc[mt];
+          float pe[8];
 #pragma unroll
-          for (int nt = 0; nt < 2; ++nt) {
-            const f32x16& sv = sacc[mt][nt];
-            pf[nt] = to_bf16x8(sv[qh + 0], sv[qh + 1], sv[qh + 2], sv[qh + 3], sv[qh + 4], sv[qh + 5], sv[qh + 6],
-                               sv[qh + 7]);
-          }
-          const int key0 = kstep * 16 + 4 * hf + (li >> 2);
+          for (int u = 0; u < 8; ++u) pe[u] = fast_exp2(__builtin_fmaf(sv[qh + u], c, -mc));
+          const bf16x8 pf = to_bf16x8(pe[0], pe[1], pe[2], pe[3], pe[4], pe[5], pe[6], pe[7]);
+          l += ((pe[0] + pe[1]) + (pe[2] + pe[3])) + ((pe[4] + pe[5]) + (pe[6] + pe[7]));
 #pragma unroll
           for (int md = 0; md < 4; ++md) {
-            const int col = md * 32 + 16 * (gi & 1) + 4 * (li & 3);
-            const bf16x8 vf = lds_tr_pair(sV + key0 * LDS_ROW + col, sV + (key0 + 8) * LDS_ROW + col);
-            acc_o[md][0] = mfma32x32x16(vf, pf[0], acc_o[md][0]);
-            acc_o[md][1] = mfma32x32x16(vf, pf[1], acc_o[md][1]);
+            const bf16x8 vf = lds_read_b128(va + 2u * (md * 32 * LDS_ROW_VT + kstep * 16));
+            acc_o[md] = mfma32x32x16(vf, pf, acc_o[md]);
           }
         }
       }
 
       // ---- epilogue: unnormalised O_c against the true row max, max and log-sum-exp ----
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        float lt = l[nt] + __shfl_xor(l[nt], 32);
-        if (!valid[nt]) continue;
+      float lt = l + __shfl_xor(l, 32);
+      if (valid) {
         const bool seen = lt > 0.f;
-        const float fix = seen ? fast_exp2((m_ref[nt] - m_true[nt]) * c) : 1.f;
+        const float fix = seen ? fast_exp2((m_ref - m_true) * c) : 1.f;
         lt *= fix;
         if (hf == 0) {
-          a.m_part[prow[nt]] = seen ? m_true[nt] * a.sm_scale : -INFINITY;
-          a.lse_part[prow[nt]] = seen ? (m_true[nt] * c + __log2f(lt)) * kLn2 : -INFINITY;
+          a.m_part[prow] = seen ? m_true * a.sm_scale : -INFINITY;
+          a.lse_part[prow] = seen ? (m_true * c + __log2f(lt)) * kLn2 : -INFINITY;
         }
         if (seen) {
-          float* op = a.o_part + prow[nt] * D + hf * 4;
+          float* op = a.o_part + prow * D + hf * 4;
 #pragma unroll
           for (int md = 0; md < 4; ++md)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              f32x4 v4 = {acc_o[md][nt][4 * i + 0] * fix, acc_o[md][nt][4 * i + 1] * fix,
-                          acc_o[md][nt][4 * i + 2] * fix, acc_o[md][nt][4 * i + 3] * fix};
+              f32x4 v4 = {acc_o[md][4 * i + 0] * fix, acc_o[md][4 * i + 1] * fix, acc_o[md][4 * i + 2] * fix,
+                          acc_o[md][4 * i + 3] * fix};
               *reinterpret_cast<f32x4*>(op + md * 32 + 8 * i) = v4;
             }
         }
@@ -305,7 +289,7 @@ hipError_t launch_claim_reset(int32_t* claim, int n_workers, hipStream_t stream)
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, int n_workers, hipStream_t stream) {
   TimedLaunch t(kFwdBf16, stream);
-  hipLaunchKernelGGL(fwd_bf16_kernel, dim3(n_workers), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(fwd_bf16_kernel, dim3(n_workers), dim3(NTHR), 0, stream, a);
   return hipGetLastError();
 }
 
