@@ -67,6 +67,34 @@ __device__ __forceinline__ bf16x8 lds_tr_pair(uint32_t a0, uint32_t a1) {
   return __builtin_bit_cast(bf16x8, c);
 }
 
+// Raw buffer descriptor over `bytes` bytes from p: loads whose offset reaches
+// past the range return zeros.  Word 3 is the gfx9 raw-buffer format.  Only
+// the per-lane offset may carry the position (the scalar offset of a buffer
+// load is not part of the range check), so every load passes soffset = 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, bytes, 0x00020000);
+}
+
+// A value the caller knows to be the same in every lane, moved to a scalar
+// register (the compiler cannot always prove it, e.g. for fields of a work
+// item loaded through a vector load).
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ int64_t uniform(int64_t x) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)x >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+template <typename T>
+__device__ __forceinline__ const T* uniform(const T* p) {
+  return reinterpret_cast<const T*>(uniform(reinterpret_cast<int64_t>(p)));
+}
+__device__ __forceinline__ uint4 buffer_load_b128(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ uint2 buffer_load_b64(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
+
 // 16-byte LDS read from a 32-bit LDS byte address.
 __device__ __forceinline__ bf16x8 lds_read_b128(uint32_t addr) {
   typedef __attribute__((address_space(3))) const uint4 lds_u4;
@@ -121,7 +149,9 @@ __device__ __forceinline__ int64_t claim_next(const int64_t* worker_off, int32_t
   while (visited < lists) {
     if (threadIdx.x == 0) *s_claim = atomicAdd(&claim[victim], 1);
     __syncthreads();
-    const int idx = *s_claim;
+    // Uniform by construction; readfirstlane lets the compiler keep the item
+    // and everything derived from it in scalar registers.
+    const int idx = __builtin_amdgcn_readfirstlane(*s_claim);
     __syncthreads();
     const int64_t base = worker_off[victim];
     if (idx < worker_off[victim + 1] - base) return base + idx;

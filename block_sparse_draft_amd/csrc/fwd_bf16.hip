@@ -26,7 +26,10 @@
 // exp2 domain with lazy rescaling (the reference maximum only moves when the
 // true maximum exceeds it by 2^8; the output is corrected to the true maximum
 // once per item), O^T += V^T P^T with P^T taken straight from the S^T
-// accumulators.
+// accumulators.  The scores of tile t+1 are issued in the same scheduling
+// block as the exponentials and PV products of tile t (software pipeline),
+// and K/V tiles are fetched through buffer descriptors so that the per-tile
+// address work is scalar.
 #include "device.h"
 #include "launch.h"
 #include "timing.h"
@@ -55,21 +58,42 @@ struct TileRegs {
   uint2 v0, v1, v2, v3;
 };
 
-// Issue the loads of key tile [kb, kb+64) (sequence-relative).  Keys past the
-// context are clamped to its last key: they are masked for every row.
+// Byte offsets of this thread's staging loads inside a tile: K rows tid/16 and
+// tid/16 + 32 (16 bytes at head-dim 8*(tid%16)); V rows 4*(tid/32) + j
+// (8 bytes at head-dim 4*(tid%32)).
+struct TileOffsets {
+  int k0, k1, v0, v1, v2, v3;
+};
+
+__device__ __forceinline__ TileOffsets tile_offsets(int kv_st, int tid) {
+  TileOffsets o;
+  const int rb = kv_st * 2;  // bytes per key row
+  o.k0 = (tid >> 4) * rb + (tid & 15) * 16;
+  o.k1 = o.k0 + 32 * rb;
+  o.v0 = (tid >> 5) * 4 * rb + (tid & 31) * 8;
+  o.v1 = o.v0 + rb;
+  o.v2 = o.v0 + 2 * rb;
+  o.v3 = o.v0 + 3 * rb;
+  return o;
+}
+
+// Issue the loads of key tile [kb, kb+64) (sequence-relative) through buffer
+// descriptors based at key kb whose range ends with the context: keys past
+// the context read as zeros (they are masked for every row).  The per-tile
+// address work is scalar and each thread keeps six 32-bit offsets.
 __device__ __forceinline__ TileRegs load_tile(const uint16_t* Kseq, const uint16_t* Vseq, int kb, int n_ctx,
-                                              int64_t kv_st, int tid) {
+                                              int kv_st, const TileOffsets& o) {
+  const int64_t start = (int64_t)kb * kv_st;
+  const int range = (n_ctx - kb) * kv_st * 2;
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kseq + start, range);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vseq + start, range);
   TileRegs r;
-  const int krow = tid >> 4;               // 0..31
-  const int64_t kd = (tid & 15) * 8;
-  r.k0 = *reinterpret_cast<const uint4*>(Kseq + (int64_t)min(kb + krow, n_ctx - 1) * kv_st + kd);
-  r.k1 = *reinterpret_cast<const uint4*>(Kseq + (int64_t)min(kb + krow + 32, n_ctx - 1) * kv_st + kd);
-  const int vk = (tid >> 5) * 4;           // 4 consecutive keys
-  const int64_t vd = (tid & 31) * 4;       // 4 consecutive head-dim values
-  r.v0 = *reinterpret_cast<const uint2*>(Vseq + (int64_t)min(kb + vk + 0, n_ctx - 1) * kv_st + vd);
-  r.v1 = *reinterpret_cast<const uint2*>(Vseq + (int64_t)min(kb + vk + 1, n_ctx - 1) * kv_st + vd);
-  r.v2 = *reinterpret_cast<const uint2*>(Vseq + (int64_t)min(kb + vk + 2, n_ctx - 1) * kv_st + vd);
-  r.v3 = *reinterpret_cast<const uint2*>(Vseq + (int64_t)min(kb + vk + 3, n_ctx - 1) * kv_st + vd);
+  r.k0 = buffer_load_b128(rk, o.k0);
+  r.k1 = buffer_load_b128(rk, o.k1);
+  r.v0 = buffer_load_b64(rv, o.v0);
+  r.v1 = buffer_load_b64(rv, o.v1);
+  r.v2 = buffer_load_b64(rv, o.v2);
+  r.v3 = buffer_load_b64(rv, o.v3);
   return r;
 }
 
@@ -109,6 +133,8 @@ void fwd_bf16_kernel(FwdArgs a) {
   const uint16_t* V = static_cast<const uint16_t*>(a.v);
   const int GB = a.group * a.block;
   const float c = a.scale_log2;
+  const int kv_st = (int)a.kv_st;  // the host checks that a sequence's K/V span fits 31 bits of bytes
+  const TileOffsets toff = tile_offsets(kv_st, tid);
 
   __shared__ int s_claim;
   const uint64_t t_start = __builtin_amdgcn_s_memrealtime();
@@ -117,12 +143,14 @@ void fwd_bf16_kernel(FwdArgs a) {
   for (;;) {
     const int64_t slot = claim_next(a.worker_off, a.claim, victim, visited, &s_claim, a.steal);
     if (slot < 0) break;
-    const skv_item it = a.items[slot];
+    skv_item it = a.items[slot];
+    it.seq = uniform(it.seq); it.kv_head = uniform(it.kv_head); it.chunk = uniform(it.chunk);
+    it.lo = uniform(it.lo); it.hi = uniform(it.hi); it.part_base = uniform(it.part_base);
     const int s = it.seq;
-    const int64_t q0 = a.q_off[s];
-    const int64_t mq = a.q_off[s + 1] - q0;
-    const int64_t k0 = a.kv_off[s];
-    const int n_ctx = (int)(a.kv_off[s + 1] - k0);
+    const int64_t q0 = uniform(a.q_off[s]);
+    const int64_t mq = uniform(a.q_off[s + 1]) - q0;
+    const int64_t k0 = uniform(a.kv_off[s]);
+    const int n_ctx = (int)(uniform(a.kv_off[s + 1]) - k0);
     const int64_t blk0 = q0 / a.block;
     const int klo = it.chunk * a.chunk;
     const int khi = min(klo + a.chunk, n_ctx);
@@ -140,7 +168,7 @@ void fwd_bf16_kernel(FwdArgs a) {
       TileRegs R;
       if (ntiles > 0) {
         __syncthreads();  // all waves are done with the previous pass's buffers
-        R = load_tile(Kseq, Vseq, klo, n_ctx, a.kv_st, tid);
+        R = load_tile(Kseq, Vseq, klo, n_ctx, kv_st, toff);
       }
       const int p = rt + wave * 32 + l32;
       const bool valid = p < nrows;
@@ -162,7 +190,7 @@ void fwd_bf16_kernel(FwdArgs a) {
       // Drain every outstanding load (Q included) before the prefetch starts, so
       // that inside the tile loop only the prefetch itself is in flight.
       __builtin_amdgcn_s_waitcnt(0);
-      if (ntiles > 1) R = load_tile(Kseq, Vseq, klo + KT, n_ctx, a.kv_st, tid);
+      if (ntiles > 1) R = load_tile(Kseq, Vseq, klo + KT, n_ctx, kv_st, toff);
       const int wave_hi = wave_max_i(vend);
       const int wave_full = wave_min_i(valid ? vend : INT32_MAX);
 
@@ -173,45 +201,50 @@ void fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc_o[i] = f32x16{};
 
-      for (int t = 0; t < ntiles; ++t) {
-        const int kb = klo + t * KT;
-        if (t + 1 < ntiles) {
-          store_tile(R, sKb[(t + 1) % NBUF], sVb[(t + 1) % NBUF], tid);
-          if (t + 2 < ntiles) R = load_tile(Kseq, Vseq, kb + 2 * KT, n_ctx, a.kv_st, tid);
-        }
-        __syncthreads();
-        if (kb >= wave_hi) continue;  // no row of this wave sees the tile
-        // 32-bit LDS addresses of this lane's operand rows; the empty asm keeps
-        // the per-read offsets as immediates.
-        uint32_t ka = lds_addr(sKb[t % NBUF] + l32 * LDS_ROW_K + hf * 8);
-        uint32_t va = lds_addr(sVb[t % NBUF] + l32 * LDS_ROW_VT + hf * 8);
-        asm volatile("" : "+v"(ka), "+v"(va));
-
-        // ---- S^T = K Q^T (raw scores) ----
-        f32x16 sacc[2];
+      // S^T = K Q^T of the tile in buffer `buf` (raw scores), 16 MFMAs.
+      auto scores = [&](int buf, f32x16 (&sacc)[2]) {
+        uint32_t ka = lds_addr(sKb[buf] + l32 * LDS_ROW_K + hf * 8);
+        asm volatile("" : "+v"(ka));  // keeps the per-read offsets as immediates
         sacc[0] = sacc[1] = f32x16{};
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) {
+          if (ks & 1) asm volatile("" ::: "memory");  // bounds how far the compiler hoists the reads
 #pragma unroll
           for (int mt = 0; mt < 2; ++mt) {
             const bf16x8 kf = lds_read_b128(ka + 2u * (mt * 32 * LDS_ROW_K + ks * 16));
             sacc[mt] = mfma32x32x16(kf, qf[ks], sacc[mt]);
           }
         }
+      };
+
+      // Software pipeline: the scores of tile t+1 are issued together with
+      // the softmax and PV products of tile t, so no wave waits on its own
+      // MFMA results inside a tile.
+      f32x16 scur[2], snext[2];
+      for (int t = 0; t < ntiles; ++t) {
+        const int kb = klo + t * KT;
+        if (t + 1 < ntiles) {
+          store_tile(R, sKb[(t + 1) % NBUF], sVb[(t + 1) % NBUF], tid);
+          if (t + 2 < ntiles) R = load_tile(Kseq, Vseq, kb + 2 * KT, n_ctx, kv_st, toff);
+        }
+        __syncthreads();
+        if (kb >= wave_hi) continue;  // no row of this wave sees the tile (nor any later one)
+        if (t == 0) scores(0, scur);
+
         // ---- mask keys at or past the row's prefix end (partial tiles only) ----
         if (kb + KT > wave_full) {
+          // element e2 of half mt holds key kb + mt*32 + 8*(e2/4) + 4*hf + e2%4
+          const int lim = vend - kb - 4 * hf;
 #pragma unroll
           for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-            for (int e2 = 0; e2 < 16; ++e2) {
-              const int key = kb + mt * 32 + (e2 >> 2) * 8 + hf * 4 + (e2 & 3);
-              if (key >= vend) sacc[mt][e2] = -INFINITY;
-            }
+            for (int e2 = 0; e2 < 16; ++e2)
+              if (mt * 32 + (e2 >> 2) * 8 + (e2 & 3) >= lim) scur[mt][e2] = -INFINITY;
         }
         // ---- row max; lazy rescale when the row's max grew past 2^8 ----
-        float r0 = fmaxf(sacc[0][0], sacc[1][0]);
+        float r0 = fmaxf(scur[0][0], scur[1][0]);
 #pragma unroll
-        for (int e2 = 1; e2 < 16; ++e2) r0 = fmaxf(r0, fmaxf(sacc[0][e2], sacc[1][e2]));
+        for (int e2 = 1; e2 < 16; ++e2) r0 = fmaxf(r0, fmaxf(scur[0][e2], scur[1][e2]));
         r0 = fmaxf(r0, __shfl_xor(r0, 32));
         m_true = fmaxf(m_true, r0);
         const bool grow = (m_true - m_ref) * c > LAZY_LOG2;  // false while both are -inf
@@ -225,14 +258,20 @@ void fwd_bf16_kernel(FwdArgs a) {
             for (int md = 0; md < 4; ++md) acc_o[md] *= alpha;
           }
         }
+        // ---- scores of tile t+1 (the buffer holds stale keys after the last
+        //      tile: computed and discarded) ----
+        scores((t + 1) % NBUF, snext);
         // ---- P = exp2(s*c - m_ref*c), 16 keys at a time right before their
         //      part of O^T += V^T P^T; the row sum in fp32 (bf16-rounded P
         //      would cost the log-sum-exp up to 2^-9 relative on short rows) ----
+        uint32_t va = lds_addr(sVb[t % NBUF] + l32 * LDS_ROW_VT + hf * 8);
+        asm volatile("" : "+v"(va));
         const float mc = m_ref == -INFINITY ? 0.f : m_ref * c;
 #pragma unroll
         for (int kstep = 0; kstep < 4; ++kstep) {
+          asm volatile("" ::: "memory");
           const int mt = kstep >> 1, qh = (kstep & 1) * 8;
-          const f32x16& sv = sacc[mt];
+          const f32x16& sv = scur[mt];
           float pe[8];
 #pragma unroll
           for (int u = 0; u < 8; ++u) pe[u] = fast_exp2(__builtin_fmaf(sv[qh + u], c, -mc));
@@ -244,6 +283,16 @@ void fwd_bf16_kernel(FwdArgs a) {
             acc_o[md] = mfma32x32x16(vf, pf, acc_o[md]);
           }
         }
+        // Interleave the block's 32 MFMAs with its operand reads and VALU work
+        // (exponentials of this tile) instead of issuing them in bursts.
+#pragma unroll
+        for (int g = 0; g < 32; ++g) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
+          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // 4 VALU
+        }
+        scur[0] = snext[0];
+        scur[1] = snext[1];
       }
 
       // ---- epilogue: unnormalised O_c against the true row max, max and log-sum-exp ----

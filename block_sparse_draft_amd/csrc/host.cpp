@@ -70,6 +70,9 @@ extern "C" int skv_check_problem(const skv_problem* p) {
     if (q0 % p->block || q1 % p->block)
       return fail(SKV_EINVAL, "query offsets of sequence %d are not multiples of block %d", s, p->block);
     if (k1 - k0 > (int64_t)INT32_MAX - p->block) return fail(SKV_ESHAPE, "sequence %d is too long", s);
+    // bf16 kernels address one sequence's K/V rows with 32-bit byte offsets
+    if (p->dtype == SKV_BF16 && (k1 - k0) * p->kv_stride_tok * 2 > (int64_t)INT32_MAX)
+      return fail(SKV_ESHAPE, "sequence %d spans more than 2^31 bytes of K/V rows", s);
     const SeqView v = seq_view(p, s);
     for (int64_t b = 0; b < v.n_blk; ++b) {
       const int32_t a = p->h_anchor[v.blk0 + b];

@@ -144,6 +144,13 @@ def test_problem_validation_codes():
     # bf16 supports head_dim 128 only
     p = _bad(w, dtype=B.SKV_BF16)
     assert B.lib.skv_check_problem(C.byref(p.c)) == B.SKV_ESHAPE
+    # bf16 K/V rows of one sequence must span at most 2^31 bytes (32-bit buffer offsets)
+    wb = make("c2", seed=0, n_ctx=1024, n_anchor=2)
+    pb = _problem_from(wb)
+    assert B.lib.skv_check_problem(C.byref(pb.c)) == B.SKV_OK
+    pb.c.kv_stride_tok = (1 << 30) // 1024 + 8          # 1024 rows * stride * 2 bytes > 2^31
+    pb.c.kv_stride_head = 128
+    assert B.lib.skv_check_problem(C.byref(pb.c)) == B.SKV_ESHAPE and "2^31" in B.last_error()
     # unsorted anchors
     p = _problem_from(w)
     p.h_anchor[:] = p.h_anchor[::-1].copy()
