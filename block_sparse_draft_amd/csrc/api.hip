@@ -90,10 +90,12 @@ extern "C" int lse_merge(int32_t n_part, int32_t hq, int64_t mq, int32_t d, cons
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Workspace of sparse_attn_bwd: dQ partials (the forward's partial layout),
-// Delta, and the first partial row of each sequence.
+// Workspace of sparse_attn_bwd: dQ partials (the forward's partial layout);
+// Q, dO, LSE (log2 units), Delta and the prefix end e_b copied into packed row
+// order (sequence, KV head, packed row p = (b*G + hl)*B + i), which is the
+// order both backward kernels walk; the first partial row of each sequence.
 struct BwdWorkspace {
-  size_t dq_part, delta, part_base, total;
+  size_t dq_part, qp, dop, lsep, deltap, endp, part_base, total;
 };
 static BwdWorkspace bwd_workspace(const skv_problem* p) {
   int64_t rows = 0;
@@ -101,10 +103,15 @@ static BwdWorkspace bwd_workspace(const skv_problem* p) {
     const SeqView v = seq_view(p, s);
     rows += ceil_div(v.n, p->chunk) * p->hq * v.mq;
   }
+  const size_t prow = (size_t)p->h_q_off[p->n_seq] * (size_t)p->hq;  // packed rows
   BwdWorkspace w;
   w.dq_part = 0;
-  w.delta = align256((size_t)rows * (size_t)p->d * sizeof(float));
-  w.part_base = w.delta + align256((size_t)p->h_q_off[p->n_seq] * (size_t)p->hq * sizeof(float));
+  w.qp = align256((size_t)rows * (size_t)p->d * sizeof(float));
+  w.dop = w.qp + align256(prow * (size_t)p->d * 2);
+  w.lsep = w.dop + align256(prow * (size_t)p->d * 2);
+  w.deltap = w.lsep + align256(prow * sizeof(float));
+  w.endp = w.deltap + align256(prow * sizeof(float));
+  w.part_base = w.endp + align256(prow * sizeof(int32_t));
   w.total = w.part_base + align256((size_t)(p->n_seq + 1) * sizeof(int64_t));
   return w;
 }
@@ -137,7 +144,11 @@ extern "C" int sparse_attn_bwd(const skv_problem* p, const skv_plan* plan_kv, co
   BwdArgs a{};
   a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.dout = dout; a.dq = dq; a.dk = dk; a.dv = dv;
   a.dq_part = reinterpret_cast<float*>(w + ws.dq_part);
-  a.delta = reinterpret_cast<float*>(w + ws.delta);
+  a.qp = reinterpret_cast<uint16_t*>(w + ws.qp);
+  a.dop = reinterpret_cast<uint16_t*>(w + ws.dop);
+  a.lsep = reinterpret_cast<float*>(w + ws.lsep);
+  a.deltap = reinterpret_cast<float*>(w + ws.deltap);
+  a.endp = reinterpret_cast<int32_t*>(w + ws.endp);
   a.part_base = reinterpret_cast<int64_t*>(w + ws.part_base);
   a.q_st = p->q_stride_tok; a.q_sh = p->q_stride_head;
   a.kv_st = p->kv_stride_tok; a.kv_sh = p->kv_stride_head;

@@ -8,8 +8,10 @@
 //
 // Four launches on the caller's stream, none with atomics, so the result is
 // bitwise reproducible:
-//   1. preprocess: Delta per (query row, head), and the first partial row of
-//      every sequence (for the dQ partial layout).
+//   1. preprocess: the first partial row of every sequence (for the dQ
+//      partial layout), and copies of Q, dO, LSE (log2 units), Delta and the
+//      draft block's prefix end in packed row order, so that the query tiles
+//      of both main kernels are contiguous rows.
 //   2. key-owner kernel (persistent workgroups over BWD items = (sequence, KV
 //      head, key range)): 128 keys at a time (32 per wave) with their K, V
 //      operands and fp32 dK, dV accumulators in registers, walking the 64-row
@@ -41,27 +43,50 @@ constexpr int LDS_ROW = D + 8;   // bf16 per staged row (272 bytes: conflict-fre
 // 1. preprocess
 // ---------------------------------------------------------------------------
 
-__global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
-  // 16 lanes per (row, head), 8 bf16 each.
+// Packed copies for the two main kernels (16 lanes per (token, head), 8 bf16
+// each): Q and dO rows, LSE in log2 units, Delta = sum_x dO * O (from the
+// merged O in bf16) and the prefix end of the row's draft block, all at the
+// row's packed index.
+__global__ __launch_bounds__(256) void bwd_pack_kernel(BwdArgs a) {
   const int64_t idx = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
   const int ln = threadIdx.x & 15;
   const int64_t n = a.total_q * a.hq;
   if (idx >= n) return;  // whole 16-lane groups leave together
   const int64_t t = idx / a.hq;
   const int h = (int)(idx % a.hq);
+  int lo = 0, hi = a.n_seq;  // sequence of token t: q_off[lo] <= t < q_off[lo + 1]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (a.q_off[mid] <= t) lo = mid; else hi = mid;
+  }
+  const int64_t q0 = a.q_off[lo], mq = a.q_off[lo + 1] - q0;
+  const int64_t r = t - q0;
+  const int64_t b = r / a.block, i = r % a.block;
+  const int g = h / a.group, hl = h % a.group;
+  const int64_t P = q0 * a.hq + (int64_t)g * a.group * mq + (b * a.group + hl) * a.block + i;
+
   const uint16_t* O = static_cast<const uint16_t*>(a.o) + t * a.q_st + (int64_t)h * a.q_sh + ln * 8;
   const uint16_t* dO = static_cast<const uint16_t*>(a.dout) + t * a.q_st + (int64_t)h * a.q_sh + ln * 8;
+  const uint16_t* Qr = static_cast<const uint16_t*>(a.q) + t * a.q_st + (int64_t)h * a.q_sh + ln * 8;
   const uint4 ov = *reinterpret_cast<const uint4*>(O);
   const uint4 dv = *reinterpret_cast<const uint4*>(dO);
+  const uint4 qv = *reinterpret_cast<const uint4*>(Qr);
+  *reinterpret_cast<uint4*>(a.qp + P * D + ln * 8) = qv;
+  *reinterpret_cast<uint4*>(a.dop + P * D + ln * 8) = dv;
   const uint32_t ow[4] = {ov.x, ov.y, ov.z, ov.w}, dw[4] = {dv.x, dv.y, dv.z, dv.w};
   float sum = 0.f;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    sum = fmaf(__uint_as_float(ow[i] << 16), __uint_as_float(dw[i] << 16), sum);
-    sum = fmaf(__uint_as_float(ow[i] & 0xffff0000u), __uint_as_float(dw[i] & 0xffff0000u), sum);
+  for (int k = 0; k < 4; ++k) {
+    sum = fmaf(__uint_as_float(ow[k] << 16), __uint_as_float(dw[k] << 16), sum);
+    sum = fmaf(__uint_as_float(ow[k] & 0xffff0000u), __uint_as_float(dw[k] & 0xffff0000u), sum);
   }
   for (int o = 8; o > 0; o >>= 1) sum += __shfl_xor(sum, o, 16);
-  if (ln == 0) a.delta[idx] = sum;
+  if (ln == 0) {
+    const int n_ctx = (int)(a.kv_off[lo + 1] - a.kv_off[lo]);
+    a.deltap[P] = sum;
+    a.lsep[P] = a.lse[idx] * kLog2e;
+    a.endp[P] = min(a.anchor[q0 / a.block + b] + a.block, n_ctx);
+  }
 }
 
 // First partial row of every sequence: part_base[s] = sum_{s' < s} C_s' * hq * Mq_s'.
@@ -105,10 +130,8 @@ void bwd_kv_kernel(BwdArgs a) {
   const int lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hf = lane >> 5;
   const int gi = lane >> 4, li = lane & 15;
-  const uint16_t* Q = static_cast<const uint16_t*>(a.q);
   const uint16_t* K = static_cast<const uint16_t*>(a.k);
   const uint16_t* V = static_cast<const uint16_t*>(a.v);
-  const uint16_t* dO = static_cast<const uint16_t*>(a.dout);
   uint16_t* dK = static_cast<uint16_t*>(a.dk);
   uint16_t* dV = static_cast<uint16_t*>(a.dv);
   const int GB = a.group * a.block;
@@ -120,13 +143,16 @@ void bwd_kv_kernel(BwdArgs a) {
   for (;;) {
     const int64_t slot = claim_next(a.kv_worker_off, a.kv_claim, victim, visited, &s_claim, a.kv_steal);
     if (slot < 0) break;
-    const skv_item it = a.kv_items[slot];
+    skv_item it = a.kv_items[slot];
+    it.seq = uniform(it.seq); it.kv_head = uniform(it.kv_head); it.lo = uniform(it.lo); it.hi = uniform(it.hi);
     const int s = it.seq, g = it.kv_head;
-    const int64_t q0 = a.q_off[s];
-    const int64_t k0 = a.kv_off[s];
-    const int n_ctx = (int)(a.kv_off[s + 1] - k0);
+    const int64_t q0 = uniform(a.q_off[s]);
+    const int64_t mq = uniform(a.q_off[s + 1]) - q0;
+    const int64_t k0 = uniform(a.kv_off[s]);
+    const int n_ctx = (int)(uniform(a.kv_off[s + 1]) - k0);
     const int64_t blk0 = q0 / a.block;
-    const int n_blk = (int)((a.q_off[s + 1] - q0) / a.block);
+    const int n_blk = (int)(mq / a.block);
+    const int64_t pbase = q0 * a.hq + (int64_t)g * GB * n_blk;  // first packed row of (s, g)
     const uint16_t* Kseq = K + k0 * a.kv_st + (int64_t)g * a.kv_sh;
     const uint16_t* Vseq = V + k0 * a.kv_st + (int64_t)g * a.kv_sh;
 
@@ -143,42 +169,33 @@ void bwd_kv_kernel(BwdArgs a) {
       const int nq = (n_blk - b_first) * GB;
       const int ntq = (nq + QT - 1) / QT;
 
-      // Query tile loader: rows p = qt*64 + row of the visible suffix, packed
-      // block-major like the forward; padding rows read the last row and are masked.
+      // Query tile loader: rows qt*64 + row of the visible suffix, contiguous
+      // in the packed copies; padding rows read the last row and are masked.
+      const int64_t vis0 = pbase + (int64_t)b_first * GB;  // packed index of the suffix's first row
       auto load_q = [&](int qt) {
         QTileRegs r;
         const int row = tid >> 4;
-        const int64_t d8 = (tid & 15) * 8;
-        int64_t off[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int p = min(qt * QT + row + 16 * u, nq - 1);
-          const int pb = a.fd_block.div(p);
-          const int b = b_first + a.fd_group.div(pb);
-          const int h = g * a.group + (pb - a.fd_group.div(pb) * a.group);
-          const int64_t t = q0 + (int64_t)b * a.block + (p - pb * a.block);
-          off[u] = t * a.q_st + (int64_t)h * a.q_sh + d8;
-        }
-        r.q0 = *reinterpret_cast<const uint4*>(Q + off[0]);
-        r.q1 = *reinterpret_cast<const uint4*>(Q + off[1]);
-        r.q2 = *reinterpret_cast<const uint4*>(Q + off[2]);
-        r.q3 = *reinterpret_cast<const uint4*>(Q + off[3]);
-        r.o0 = *reinterpret_cast<const uint4*>(dO + off[0]);
-        r.o1 = *reinterpret_cast<const uint4*>(dO + off[1]);
-        r.o2 = *reinterpret_cast<const uint4*>(dO + off[2]);
-        r.o3 = *reinterpret_cast<const uint4*>(dO + off[3]);
+        const uint16_t* qb = a.qp + (vis0 + qt * QT) * D + (tid & 15) * 8;
+        const uint16_t* ob = a.dop + (vis0 + qt * QT) * D + (tid & 15) * 8;
+        const int last = nq - 1 - qt * QT;  // last valid row of the tile
+        const int r0 = min(row, last) * D, r1 = min(row + 16, last) * D;
+        const int r2 = min(row + 32, last) * D, r3 = min(row + 48, last) * D;
+        r.q0 = *reinterpret_cast<const uint4*>(qb + r0);
+        r.q1 = *reinterpret_cast<const uint4*>(qb + r1);
+        r.q2 = *reinterpret_cast<const uint4*>(qb + r2);
+        r.q3 = *reinterpret_cast<const uint4*>(qb + r3);
+        r.o0 = *reinterpret_cast<const uint4*>(ob + r0);
+        r.o1 = *reinterpret_cast<const uint4*>(ob + r1);
+        r.o2 = *reinterpret_cast<const uint4*>(ob + r2);
+        r.o3 = *reinterpret_cast<const uint4*>(ob + r3);
         r.lse = INFINITY; r.delta = 0.f; r.end = kb;
         if (tid < QT) {
           const int p = qt * QT + tid;
-          const int pc = min(p, nq - 1);
-          const int pb = a.fd_block.div(pc);
-          const int b = b_first + a.fd_group.div(pb);
-          const int h = g * a.group + (pb - a.fd_group.div(pb) * a.group);
-          const int64_t rr = (q0 + (int64_t)b * a.block + (pc - pb * a.block)) * a.hq + h;
-          const float lse = a.lse[rr];
-          const float del = a.delta[rr];
-          const int e = min(a.anchor[blk0 + b] + a.block, n_ctx);
-          if (p < nq) { r.lse = lse * kLog2e; r.delta = del; r.end = min(e, kend); }
+          const int64_t P = vis0 + min(p, nq - 1);
+          const float lse = a.lsep[P];
+          const float del = a.deltap[P];
+          const int e = a.endp[P];
+          if (p < nq) { r.lse = lse; r.delta = del; r.end = min(e, kend); }
         }
         return r;
       };
@@ -384,10 +401,8 @@ void bwd_dq_kernel(BwdArgs a) {
   const int lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hf = lane >> 5;
   const int gi = lane >> 4, li = lane & 15;
-  const uint16_t* Q = static_cast<const uint16_t*>(a.q);
   const uint16_t* K = static_cast<const uint16_t*>(a.k);
   const uint16_t* V = static_cast<const uint16_t*>(a.v);
-  const uint16_t* dO = static_cast<const uint16_t*>(a.dout);
   const int GB = a.group * a.block;
   const float c = a.scale_log2;
   const uint16_t* my_dO = sdO + (wave * 64 + l32) * LDS_ROW + hf * 8;  // this lane's row, nt = 0
@@ -398,13 +413,16 @@ void bwd_dq_kernel(BwdArgs a) {
   for (;;) {
     const int64_t slot = claim_next(a.q_worker_off, a.q_claim, victim, visited, &s_claim, a.q_steal);
     if (slot < 0) break;
-    const skv_item it = a.q_items[slot];
+    skv_item it = a.q_items[slot];
+    it.seq = uniform(it.seq); it.kv_head = uniform(it.kv_head); it.chunk = uniform(it.chunk);
+    it.lo = uniform(it.lo); it.hi = uniform(it.hi); it.part_base = uniform(it.part_base);
     const int s = it.seq;
-    const int64_t q0 = a.q_off[s];
-    const int64_t mq = a.q_off[s + 1] - q0;
-    const int64_t k0 = a.kv_off[s];
-    const int n_ctx = (int)(a.kv_off[s + 1] - k0);
-    const int64_t blk0 = q0 / a.block;
+    const int64_t q0 = uniform(a.q_off[s]);
+    const int64_t mq = uniform(a.q_off[s + 1]) - q0;
+    const int64_t k0 = uniform(a.kv_off[s]);
+    const int n_ctx = (int)(uniform(a.kv_off[s + 1]) - k0);
+    // packed index of the item's first row: (s, kv head) block, then draft block it.lo
+    const int64_t pitem = q0 * a.hq + (int64_t)it.kv_head * a.group * mq + (int64_t)it.lo * GB;
     const int klo = it.chunk * a.chunk;
     const int khi = min(klo + a.chunk, n_ctx);
     const int nrows = (it.hi - it.lo) * GB;
@@ -413,7 +431,7 @@ void bwd_dq_kernel(BwdArgs a) {
 
     for (int rt = 0; rt < nrows; rt += 256) {
       const int p_last = min(nrows, rt + 256) - 1;
-      const int wg_hi = max(klo, min(khi, min(a.anchor[blk0 + it.lo + a.fd_gb.div(p_last)] + a.block, n_ctx)));
+      const int wg_hi = max(klo, min(khi, a.endp[pitem + p_last]));
       const int ntiles = (wg_hi - klo + KT2 - 1) / KT2;
       if (ntiles == 0) continue;  // no row of the pass sees the chunk: no partial to write
 
@@ -434,25 +452,22 @@ void bwd_dq_kernel(BwdArgs a) {
         const int hl = a.fd_group.mod(a.fd_block.div(pc));
         const int64_t r = (int64_t)b * a.block + a.fd_block.mod(pc);
         const int h = it.kv_head * a.group + hl;
-        const int e = min(a.anchor[blk0 + b] + a.block, n_ctx);
+        const int64_t P = pitem + pc;
+        const int e = a.endp[P];
         vend[nt] = valid[nt] ? max(klo, min(khi, e)) : klo;
         prow[nt] = it.part_base + (int64_t)h * mq + r;
-        const int64_t qrow = (q0 + r) * a.q_st + (int64_t)h * a.q_sh + hf * 8;
-        lse2[nt] = a.lse[(q0 + r) * a.hq + h] * kLog2e;
-        del[nt] = a.delta[(q0 + r) * a.hq + h];
+        lse2[nt] = a.lsep[P];
+        del[nt] = a.deltap[P];
+        const uint16_t* qrow = a.qp + P * D + hf * 8;
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) qf[nt][ks] = load_bf16x8(Q + qrow + ks * 16);
+        for (int ks = 0; ks < 8; ++ks) qf[nt][ks] = load_bf16x8(qrow + ks * 16);
       }
       // dO of the pass's 256 rows: thread (row tid>>4 + 16u, 16-byte column tid&15)
       uint4 dox[16];
 #pragma unroll
       for (int u = 0; u < 16; ++u) {
         const int p = min(rt + (tid >> 4) + 16 * u, p_last);
-        const int pb = a.fd_block.div(p);
-        const int b = it.lo + a.fd_group.div(pb);
-        const int h = it.kv_head * a.group + (pb - a.fd_group.div(pb) * a.group);
-        const int64_t t = q0 + (int64_t)b * a.block + (p - pb * a.block);
-        dox[u] = *reinterpret_cast<const uint4*>(dO + t * a.q_st + (int64_t)h * a.q_sh + (tid & 15) * 8);
+        dox[u] = *reinterpret_cast<const uint4*>(a.dop + (pitem + p) * D + (tid & 15) * 8);
       }
 #pragma unroll
       for (int u = 0; u < 16; ++u)
@@ -592,8 +607,8 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, int kv_workers, int q_workers, hipS
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (rows > 0) {
-    TimedLaunch t(kBwdDelta, stream);
-    hipLaunchKernelGGL(bwd_pre_kernel, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, stream, a);
+    TimedLaunch t(kBwdPack, stream);
+    hipLaunchKernelGGL(bwd_pack_kernel, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   {

@@ -52,7 +52,13 @@ struct BwdArgs {
   void* dk;
   void* dv;
   float* dq_part;     // per-chunk dQ partials, the forward's partial layout, [rows][d] fp32
-  float* delta;       // [sum Mq][hq] fp32
+  // Packed row order: row P = q_off[s]*hq + g*G*Mq_s + (b*G + hl)*B + i holds
+  // token q_off[s] + b*B + i of query head g*G + hl.
+  uint16_t* qp;       // [sum Mq * hq][d] bf16 copy of Q
+  uint16_t* dop;      // [sum Mq * hq][d] bf16 copy of dO
+  float* lsep;        // LSE * log2(e)
+  float* deltap;      // Delta = sum_x dO * O
+  int32_t* endp;      // prefix end e_b of the row's draft block
   int64_t* part_base; // [n_seq + 1] first partial row of each sequence
   int64_t q_st, q_sh, kv_st, kv_sh;
   const int64_t* q_off;

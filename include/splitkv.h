@@ -229,7 +229,7 @@ int sparse_attn_bwd(const skv_problem* p, const skv_plan* plan_kv, const skv_pla
  * out[0 .. min(max_entries, *n_entries)) and resets the tallies; *n_entries
  * receives the number of kernels with at least one launch.  Kernel names:
  * "claim_reset", "partial_fwd_bf16", "partial_fwd_f32", "lse_merge",
- * "bwd_part_base", "bwd_delta", "bwd_kv", "bwd_dq", "bwd_finalize". */
+ * "bwd_part_base", "bwd_pack", "bwd_kv", "bwd_dq", "bwd_finalize". */
 typedef struct skv_kernel_time {
   const char* name;   /* static string */
   int64_t launches;
