@@ -325,7 +325,8 @@ def main():
         if with_bwd else None,
         "kernels": kernels,
         "plan": {"host_ms_per_step": round(1e3 * float(np.mean(plan_s)), 3) if plan_s else None,
-                 "fwd_items": path.fwd_plan.n_items, "fwd_imbalance": round(path.fwd_plan.imbalance, 5),
+                 "fwd_items": path.fwd_plan.n_items, "fwd_items_planned": path.fwd_plan.n_planned,
+                 "fwd_imbalance": round(path.fwd_plan.imbalance, 5),
                  "bwd_items": path.bwd_plan.n_items if with_bwd else None,
                  "bwd_imbalance": round(path.bwd_plan.imbalance, 5) if with_bwd else None},
         "roofline": roof,

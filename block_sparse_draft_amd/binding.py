@@ -78,7 +78,8 @@ def _load():
         "skv_item_table": (C.c_int, [P(skv_problem), I32, I32, VP, VP, VP, P(I64), P(I64)]),
         "lpt_plan": (C.c_int, [VP, I64, I32, VP, VP, VP, VP]),
         "skv_static_plan": (C.c_int, [VP, I64, I64, I32, VP, VP, VP]),
-        "skv_gather_items": (C.c_int, [VP, VP, I64, VP]),
+        "skv_gather_items": (C.c_int, [VP, I64, VP, I64, VP]),
+        "skv_drop_zero_cost": (C.c_int, [VP, I64, I32, VP, VP, VP, VP, P(I64)]),
         "sparse_attn_partial_fwd": (C.c_int, [P(skv_problem), P(skv_plan), VP, VP, VP, VP, VP, VP, VP]),
         "lse_merge": (C.c_int, [I32, I32, I64, I32, VP, VP, VP, VP, I64, I64, I32, VP, I64, VP]),
         "skv_bwd_workspace_bytes": (C.c_size_t, [P(skv_problem)]),
@@ -94,7 +95,7 @@ def _load():
 
 lib = _load()
 EXPORTED = ("skv_last_error", "skv_check_problem", "skv_partial_layout", "skv_item_table", "lpt_plan",
-            "skv_static_plan", "skv_gather_items", "sparse_attn_partial_fwd", "lse_merge",
+            "skv_static_plan", "skv_gather_items", "skv_drop_zero_cost", "sparse_attn_partial_fwd", "lse_merge",
             "skv_bwd_workspace_bytes", "sparse_attn_bwd", "skv_timing_enable", "skv_timing_collect")
 
 
@@ -169,8 +170,22 @@ def skv_gather_items(items: np.ndarray, order: np.ndarray) -> np.ndarray:
     items = np.ascontiguousarray(items, dtype=ITEM_DTYPE)
     order = np.ascontiguousarray(order, dtype=np.int64)
     out = np.empty(len(order), ITEM_DTYPE)
-    _check(lib.skv_gather_items(_ptr(items), _ptr(order), len(order), _ptr(out)))
+    _check(lib.skv_gather_items(_ptr(items), len(items), _ptr(order), len(order), _ptr(out)))
     return out
+
+
+def skv_drop_zero_cost(cost, order, worker_off):
+    """Plan lists without zero-cost items.  Returns (order, worker_off)."""
+    cost = np.ascontiguousarray(cost, dtype=np.int64)
+    order = np.ascontiguousarray(order, dtype=np.int64)
+    worker_off = np.ascontiguousarray(worker_off, dtype=np.int64)
+    nw = len(worker_off) - 1
+    o2 = np.empty(max(len(order), 1), np.int64)
+    w2 = np.empty(nw + 1, np.int64)
+    n = C.c_int64(0)
+    _check(lib.skv_drop_zero_cost(_ptr(cost), len(cost), nw, _ptr(order), _ptr(worker_off), _ptr(o2), _ptr(w2),
+                                  C.byref(n)))
+    return o2[:n.value].copy(), w2
 
 
 class Problem:

@@ -56,8 +56,14 @@ extern "C" int sparse_attn_partial_fwd(const skv_problem* p, const skv_plan* pla
   a.fd_block = FastDiv::make(a.block); a.fd_group = FastDiv::make(a.group); a.fd_gb = FastDiv::make(a.block * a.group);
   a.sm_scale = p->sm_scale;
   a.scale_log2 = p->sm_scale * kLog2e_host;
+  int64_t part_rows = 0;
+  for (int s = 0; s < p->n_seq; ++s) {
+    const SeqView v = seq_view(p, s);
+    part_rows += ceil_div(v.n, p->chunk) * p->hq * v.mq;
+  }
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e = launch_claim_reset(plan->d_claim, plan->n_workers, st);
+  if (e == hipSuccess) e = launch_fill_neg_inf(m_part, lse_part, part_rows, st);
   if (e != hipSuccess) return hip_status(e, "sparse_attn_partial_fwd launch");
   e = p->dtype == SKV_BF16 ? launch_fwd_bf16(a, plan->n_workers, st)
                                       : launch_fwd_f32(a, p->d, plan->n_workers, st);

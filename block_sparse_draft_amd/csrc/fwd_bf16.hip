@@ -328,11 +328,30 @@ __global__ void claim_reset_kernel(int32_t* claim, int n) {
   if (i < n) claim[i] = 0;
 }
 
+// m = lse = -inf for every partial row (rows of items left out of a plan).
+__global__ __launch_bounds__(256) void fill_neg_inf_kernel(float* m, float* lse, int64_t n) {
+  const int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+  const f32x4 v = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+  if (i + 4 <= n && ((reinterpret_cast<uintptr_t>(m) | reinterpret_cast<uintptr_t>(lse)) & 15) == 0) {
+    *reinterpret_cast<f32x4*>(m + i) = v;
+    *reinterpret_cast<f32x4*>(lse + i) = v;
+  } else {
+    for (int64_t j = i; j < min(i + 4, n); ++j) m[j] = lse[j] = -INFINITY;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_claim_reset(int32_t* claim, int n_workers, hipStream_t stream) {
   TimedLaunch t(kClaimReset, stream);
   hipLaunchKernelGGL(claim_reset_kernel, dim3((n_workers + 255) / 256), dim3(256), 0, stream, claim, n_workers);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_neg_inf(float* m, float* lse, int64_t n, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  TimedLaunch t(kFillPartials, stream);
+  hipLaunchKernelGGL(fill_neg_inf_kernel, dim3((unsigned)((n + 1023) / 1024)), dim3(256), 0, stream, m, lse, n);
   return hipGetLastError();
 }
 

@@ -224,12 +224,37 @@ extern "C" int skv_static_plan(const int64_t* tok_start, int64_t n, int64_t tota
   return write_csr(lists, order, worker_off);
 }
 
-extern "C" int skv_gather_items(const skv_item* items, const int64_t* order, int64_t n, skv_item* items_out) {
-  if (n < 0) return fail(SKV_EINVAL, "n < 0");
+extern "C" int skv_gather_items(const skv_item* items, int64_t n_items, const int64_t* order, int64_t n,
+                                skv_item* items_out) {
+  if (n < 0 || n_items < 0) return fail(SKV_EINVAL, "negative count");
   if (n > 0 && (!items || !order || !items_out)) return fail(SKV_EINVAL, "NULL argument");
   for (int64_t i = 0; i < n; ++i) {
-    if (order[i] < 0 || order[i] >= n) return fail(SKV_EINVAL, "order[%lld] out of range", (long long)i);
+    if (order[i] < 0 || order[i] >= n_items) return fail(SKV_EINVAL, "order[%lld] out of range", (long long)i);
     items_out[i] = items[order[i]];
   }
+  clear_error();
+  return SKV_OK;
+}
+
+extern "C" int skv_drop_zero_cost(const int64_t* cost, int64_t n, int32_t n_workers, const int64_t* order,
+                                  const int64_t* worker_off, int64_t* order_out, int64_t* worker_off_out,
+                                  int64_t* n_out) {
+  if (n < 0 || n_workers < 1) return fail(SKV_EINVAL, "bad counts n=%lld n_workers=%d", (long long)n, n_workers);
+  if (!worker_off || !worker_off_out || !n_out || (n > 0 && (!cost || !order || !order_out)))
+    return fail(SKV_EINVAL, "NULL argument");
+  if (worker_off[0] != 0 || worker_off[n_workers] != n) return fail(SKV_EINVAL, "worker_off does not span n items");
+  int64_t k = 0;
+  worker_off_out[0] = 0;
+  for (int32_t w = 0; w < n_workers; ++w) {
+    if (worker_off[w + 1] < worker_off[w]) return fail(SKV_EINVAL, "worker_off decreases at %d", w);
+    for (int64_t i = worker_off[w]; i < worker_off[w + 1]; ++i) {
+      const int64_t it = order[i];
+      if (it < 0 || it >= n) return fail(SKV_EINVAL, "order[%lld] out of range", (long long)i);
+      if (cost[it] != 0) order_out[k++] = it;
+    }
+    worker_off_out[w + 1] = k;
+  }
+  *n_out = k;
+  clear_error();
   return SKV_OK;
 }

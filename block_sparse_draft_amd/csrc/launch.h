@@ -80,6 +80,7 @@ struct BwdArgs {
 };
 
 hipError_t launch_claim_reset(int32_t* claim, int n_workers, hipStream_t stream);
+hipError_t launch_fill_neg_inf(float* m, float* lse, int64_t n, hipStream_t stream);
 hipError_t launch_fwd_bf16(const FwdArgs& a, int n_workers, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdArgs& a, int d, int n_workers, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, int d, hipStream_t stream);

@@ -12,7 +12,7 @@
 namespace skv {
 namespace {
 
-const char* const kNames[kNumKernels] = {"claim_reset", "partial_fwd_bf16", "partial_fwd_f32", "lse_merge",
+const char* const kNames[kNumKernels] = {"claim_reset", "fill_partials", "partial_fwd_bf16", "partial_fwd_f32", "lse_merge",
                                          "bwd_part_base", "bwd_pack", "bwd_kv", "bwd_dq", "bwd_finalize"};
 
 struct Pending {

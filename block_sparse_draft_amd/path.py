@@ -62,20 +62,24 @@ class _PlanSlots:
             load = np.bincount(assign, weights=cost, minlength=self.n_workers).astype(np.int64)
         else:
             raise ValueError(self.policy)
+        if self.kind == B.SKV_ITEM_FWD:
+            # empty forward items only mark rows -inf, which the forward call does for all rows
+            order, off = B.skv_drop_zero_cost(cost, order, off)
         gathered = B.skv_gather_items(items, order).view(np.uint8)
         self.plan_s = time.perf_counter() - t0
         slot = self.slots[self.next]
         self.next ^= 1
         if slot["used"]:
             slot["event"].synchronize()   # its previous upload has left the pinned buffer
-        slot["h_items"].numpy()[:len(items) * 32] = gathered
+        slot["h_items"].numpy()[:len(gathered)] = gathered
         slot["h_off"].numpy()[:] = off
         slot["d_items"].copy_(slot["h_items"], non_blocking=True)
         slot["d_off"].copy_(slot["h_off"], non_blocking=True)
         slot["event"].record()
         slot["used"] = True
         self.cost, self.load = cost, load
-        self.c = B.skv_plan(self.kind, self.n_workers, len(items), slot["d_items"].data_ptr(),
+        self.n_planned = len(order)
+        self.c = B.skv_plan(self.kind, self.n_workers, len(order), slot["d_items"].data_ptr(),
                             slot["d_off"].data_ptr(), self.claim.data_ptr(), self.flags, 0,
                             None if self.ticks is None else self.ticks.data_ptr())
         return self.c

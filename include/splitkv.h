@@ -165,8 +165,22 @@ int lpt_plan(const int64_t* cost, int64_t n, int32_t n_workers, int32_t* assign,
 int skv_static_plan(const int64_t* tok_start, int64_t n, int64_t total_tok, int32_t n_workers,
                     int32_t* assign, int64_t* order, int64_t* worker_off);
 
-/* items_out[i] = items[order[i]] for i < n (host gather into plan order). */
-int skv_gather_items(const skv_item* items, const int64_t* order, int64_t n, skv_item* items_out);
+/* items_out[i] = items[order[i]] for i < n (host gather into plan order);
+ * every order[i] must lie in [0, n_items). */
+int skv_gather_items(const skv_item* items, int64_t n_items, const int64_t* order, int64_t n, skv_item* items_out);
+
+/* Drop zero-cost items from a plan's worker lists (host, pure).  A forward
+ * item of zero cost has no row that sees any key of its chunk: its only
+ * output is m_part = lse_part = -inf for its rows, which
+ * sparse_attn_partial_fwd writes for every partial row before it runs the
+ * plan.  Left in the lists they all land on one worker under LPT (they do not
+ * change any load), which then runs thousands of empty items.  Inputs are
+ * lpt_plan / skv_static_plan outputs (order [n], worker_off [n_workers+1]);
+ * writes order_out [n] (first *n_out used) and worker_off_out
+ * [n_workers+1], keeping the order within each list.  Backward plans must
+ * keep their zero-cost items (they write the zero dK, dV of unseen keys). */
+int skv_drop_zero_cost(const int64_t* cost, int64_t n, int32_t n_workers, const int64_t* order,
+                       const int64_t* worker_off, int64_t* order_out, int64_t* worker_off_out, int64_t* n_out);
 
 /* Forward partials, one per (sequence, KV chunk).  For every query row r of
  * sequence s, query head h and chunk c with visible keys
@@ -178,7 +192,9 @@ int skv_gather_items(const skv_item* items, const int64_t* order, int64_t n, skv
  * o_part rows are d floats.  Rows with J empty get m_part = lse_part = -inf
  * and their o_part row is not written.  Fully masked 64-key tiles are never
  * read.  `plan` must be a FWD plan over skv_item_table items of this problem
- * covering every (seq, kv_head, chunk, range) exactly once; it is launched
+ * covering every (seq, kv_head, chunk, range) of nonzero cost exactly once
+ * (zero-cost items may be left out, see skv_drop_zero_cost): the call first
+ * sets m_part and lse_part of every partial row to -inf, then runs the plan
  * with plan->n_workers workgroups.  Results are bitwise deterministic. */
 int sparse_attn_partial_fwd(const skv_problem* p, const skv_plan* plan, const void* q, const void* k,
                             const void* v, float* o_part, float* m_part, float* lse_part, void* stream);
@@ -228,7 +244,7 @@ int sparse_attn_bwd(const skv_problem* p, const skv_plan* plan_kv, const skv_pla
  * the number of launches and their summed event-to-event time into
  * out[0 .. min(max_entries, *n_entries)) and resets the tallies; *n_entries
  * receives the number of kernels with at least one launch.  Kernel names:
- * "claim_reset", "partial_fwd_bf16", "partial_fwd_f32", "lse_merge",
+ * "claim_reset", "fill_partials", "partial_fwd_bf16", "partial_fwd_f32", "lse_merge",
  * "bwd_part_base", "bwd_pack", "bwd_kv", "bwd_dq", "bwd_finalize". */
 typedef struct skv_kernel_time {
   const char* name;   /* static string */

@@ -230,3 +230,28 @@ def test_plan_struct_layout():
     """skv_plan as the header lays it out on LP64: 56 bytes, d_ticks last."""
     assert C.sizeof(B.skv_plan) == 56
     assert B.skv_plan.flags.offset == 40 and B.skv_plan.d_ticks.offset == 48
+
+
+def test_drop_zero_cost_matches_filtering():
+    """skv_drop_zero_cost keeps each worker's nonzero-cost items in order."""
+    rng = np.random.default_rng(7)
+    for W in (1, 3, 16):
+        cost = rng.integers(0, 4, size=200).astype(np.int64) * rng.integers(0, 2, size=200)
+        _, order, off, _ = B.lpt_plan(cost, W)
+        o2, w2 = B.skv_drop_zero_cost(cost, order, off)
+        assert w2[0] == 0 and w2[-1] == len(o2) == int((cost != 0).sum())
+        for w in range(W):
+            lst = order[off[w]:off[w + 1]]
+            assert np.array_equal(o2[w2[w]:w2[w + 1]], lst[cost[lst] != 0])
+    # a c5-shaped forward table: LPT alone gives one worker every zero-cost item
+    w = make("c5", seed=0, with_do=False)
+    p = _problem_from(w)
+    items, cost, tok, total = p.item_table(B.SKV_ITEM_FWD, 8)
+    _, order, off, _ = B.lpt_plan(cost, 256)
+    counts = np.diff(off)
+    assert counts.max() > 1000
+    o2, w2 = B.skv_drop_zero_cost(cost, order, off)
+    assert np.diff(w2).max() < 100
+    bad = off.copy(); bad[-1] += 1
+    with pytest.raises(B.SkvError):
+        B.skv_drop_zero_cost(cost, order, bad)
