@@ -12,14 +12,14 @@
 //      partial layout), and copies of Q, dO, LSE (log2 units), Delta and the
 //      draft block's prefix end in packed row order, so that the query tiles
 //      of both main kernels are contiguous rows.
-//   2. key-owner kernel (persistent workgroups over BWD items = (sequence, KV
-//      head, key range)): 128 keys at a time (32 per wave) with their K, V
-//      operands and fp32 dK, dV accumulators in registers, walking the 64-row
-//      query tiles that see those keys (anchors are sorted, so those rows are
-//      a suffix of the draft blocks); the next tile's Q, dO, LSE, Delta load
-//      while the current one is computed.  S = Q K^T, dP = dO V^T (A from
-//      LDS), P and dS in registers, dV += P^T dO and dK += dS^T Q (B read
-//      transposed from LDS).
+//   2. key-owner kernel (persistent workgroups of 8 waves, two per SIMD, over
+//      BWD items = (sequence, KV head, key range)): 256 keys at a time, 32 per
+//      wave, with the keys' K staged in LDS, their V operands and fp32 dK, dV
+//      accumulators in registers, walking the 32-row query tiles that see
+//      those keys (anchors are sorted, so those rows are a suffix of the draft
+//      blocks); the next tile's Q, dO, LSE, Delta load while the current one
+//      is computed.  S = Q K^T, dP = dO V^T (A from LDS), P and dS in
+//      registers, dV += P^T dO and dK += dS^T Q (B read transposed from LDS).
 //   3. query-owner kernel over the forward's items (sequence, KV head, chunk,
 //      draft blocks), structured like the forward: 64 rows per wave with Q
 //      in registers and dO in LDS, K/V tiles of the chunk through two LDS
@@ -35,8 +35,6 @@ namespace skv {
 namespace {
 
 constexpr int D = 128;
-constexpr int KT = 128;          // keys per key-owner workgroup tile (32 per wave)
-constexpr int QT = 64;           // query rows per query tile
 constexpr int LDS_ROW = D + 8;   // bf16 per staged row (272 bytes: conflict-free 16-byte reads)
 
 // ---------------------------------------------------------------------------
@@ -105,25 +103,32 @@ __global__ void part_base_kernel(BwdArgs a) {
 // 2. key-owner kernel: dK, dV
 // ---------------------------------------------------------------------------
 
-// Staging registers of one query tile (64 rows): each thread moves 4 x 16 bytes
-// of Q and of dO; threads 0..63 also carry their row's LSE, Delta and prefix end.
+// Staging registers of one query tile (32 rows): each of the 512 threads moves
+// 16 bytes of Q and of dO; threads 0..31 also carry their row's LSE, Delta and
+// prefix end.
 struct QTileRegs {
-  uint4 q0, q1, q2, q3, o0, o1, o2, o3;
+  uint4 q, o;
   float lse, delta;
   int end;
 };
 
+constexpr int KV_WAVES = 8;            // two per SIMD
+constexpr int KV_THREADS = 64 * KV_WAVES;
+constexpr int KV_KEYS = 32 * KV_WAVES; // keys per workgroup pass: 32 per wave
+constexpr int QT = 32;                // query rows per tile
+
 struct QTileMeta {
-  float lse[QT];     // LSE of each row, log2 units (+inf for padding rows: P = 0)
+  float lse[QT];    // LSE of each row, log2 units (+inf for padding rows: P = 0)
   float delta[QT];
-  int end[QT];       // visible keys of the row inside this key tile: [kb, end)
+  int end[QT];      // prefix end e_b of the row (keys at or past it are masked)
 };
 
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(KV_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_kv_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t sQ[2][QT * LDS_ROW];
   __shared__ __attribute__((aligned(16))) uint16_t sdO[2][QT * LDS_ROW];
   __shared__ __attribute__((aligned(16))) QTileMeta sMeta[2];
+  __shared__ __attribute__((aligned(16))) uint16_t sK[KV_KEYS * LDS_ROW];
   __shared__ int s_claim;
 
   const int tid = threadIdx.x;
@@ -156,8 +161,8 @@ void bwd_kv_kernel(BwdArgs a) {
     const uint16_t* Kseq = K + k0 * a.kv_st + (int64_t)g * a.kv_sh;
     const uint16_t* Vseq = V + k0 * a.kv_st + (int64_t)g * a.kv_sh;
 
-    for (int kb = it.lo; kb < it.hi; kb += KT) {
-      const int kend = min(it.hi, kb + KT);
+    for (int kb = it.lo; kb < it.hi; kb += KV_KEYS) {
+      const int kend = min(it.hi, kb + KV_KEYS);
       // Blocks whose prefix ends at or before kb see none of these keys.
       int b_first = 0;
       for (int b0 = 0; b0 < n_blk; b0 += 64) {
@@ -169,25 +174,15 @@ void bwd_kv_kernel(BwdArgs a) {
       const int nq = (n_blk - b_first) * GB;
       const int ntq = (nq + QT - 1) / QT;
 
-      // Query tile loader: rows qt*64 + row of the visible suffix, contiguous
+      // Query tile loader: rows qt*32 + row of the visible suffix, contiguous
       // in the packed copies; padding rows read the last row and are masked.
       const int64_t vis0 = pbase + (int64_t)b_first * GB;  // packed index of the suffix's first row
       auto load_q = [&](int qt) {
         QTileRegs r;
-        const int row = tid >> 4;
-        const uint16_t* qb = a.qp + (vis0 + qt * QT) * D + (tid & 15) * 8;
-        const uint16_t* ob = a.dop + (vis0 + qt * QT) * D + (tid & 15) * 8;
-        const int last = nq - 1 - qt * QT;  // last valid row of the tile
-        const int r0 = min(row, last) * D, r1 = min(row + 16, last) * D;
-        const int r2 = min(row + 32, last) * D, r3 = min(row + 48, last) * D;
-        r.q0 = *reinterpret_cast<const uint4*>(qb + r0);
-        r.q1 = *reinterpret_cast<const uint4*>(qb + r1);
-        r.q2 = *reinterpret_cast<const uint4*>(qb + r2);
-        r.q3 = *reinterpret_cast<const uint4*>(qb + r3);
-        r.o0 = *reinterpret_cast<const uint4*>(ob + r0);
-        r.o1 = *reinterpret_cast<const uint4*>(ob + r1);
-        r.o2 = *reinterpret_cast<const uint4*>(ob + r2);
-        r.o3 = *reinterpret_cast<const uint4*>(ob + r3);
+        const int row = min(tid >> 4, nq - 1 - qt * QT);
+        const int64_t off = (vis0 + qt * QT + row) * D + (tid & 15) * 8;
+        r.q = *reinterpret_cast<const uint4*>(a.qp + off);
+        r.o = *reinterpret_cast<const uint4*>(a.dop + off);
         r.lse = INFINITY; r.delta = 0.f; r.end = kb;
         if (tid < QT) {
           const int p = qt * QT + tid;
@@ -195,23 +190,14 @@ void bwd_kv_kernel(BwdArgs a) {
           const float lse = a.lsep[P];
           const float del = a.deltap[P];
           const int e = a.endp[P];
-          if (p < nq) { r.lse = lse; r.delta = del; r.end = min(e, kend); }
+          if (p < nq) { r.lse = lse; r.delta = del; r.end = e; }
         }
         return r;
       };
       auto store_q = [&](const QTileRegs& r, int buf) {
         const int o = (tid >> 4) * LDS_ROW + (tid & 15) * 8;
-        constexpr int R16 = 16 * LDS_ROW;
-        uint16_t* q = sQ[buf];
-        uint16_t* d = sdO[buf];
-        *reinterpret_cast<uint4*>(q + o) = r.q0;
-        *reinterpret_cast<uint4*>(q + o + R16) = r.q1;
-        *reinterpret_cast<uint4*>(q + o + 2 * R16) = r.q2;
-        *reinterpret_cast<uint4*>(q + o + 3 * R16) = r.q3;
-        *reinterpret_cast<uint4*>(d + o) = r.o0;
-        *reinterpret_cast<uint4*>(d + o + R16) = r.o1;
-        *reinterpret_cast<uint4*>(d + o + 2 * R16) = r.o2;
-        *reinterpret_cast<uint4*>(d + o + 3 * R16) = r.o3;
+        *reinterpret_cast<uint4*>(sQ[buf] + o) = r.q;
+        *reinterpret_cast<uint4*>(sdO[buf] + o) = r.o;
         if (tid < QT) {
           sMeta[buf].lse[tid] = r.lse;
           sMeta[buf].delta[tid] = r.delta;
@@ -221,28 +207,36 @@ void bwd_kv_kernel(BwdArgs a) {
 
       // This wave's 32 keys as MFMA B operands (k = head dim); keys past the
       // context are clamped to its last key and masked.
-      const int key_w = kb + wave * 32 + l32;
-      bf16x8 kreg[8], vreg[8];
+      const int kw0 = kb + wave * 32;           // first key of this wave
+      const int key_w = kw0 + l32;
+      bf16x8 vreg[8];
       {
         const int kc = min(key_w, n_ctx - 1);
-        const uint16_t* kp = Kseq + (int64_t)kc * a.kv_st + hf * 8;
         const uint16_t* vp = Vseq + (int64_t)kc * a.kv_st + hf * 8;
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-          kreg[ks] = load_bf16x8(kp + ks * 16);
-          vreg[ks] = load_bf16x8(vp + ks * 16);
+        for (int ks = 0; ks < 8; ++ks) vreg[ks] = load_bf16x8(vp + ks * 16);
+      }
+      __syncthreads();  // every wave is done with the previous pass's K
+      {
+        // 256 keys x 16 chunks of 16 bytes: thread -> key tid/2 .. in 8 steps
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int idx = tid + u * KV_THREADS;        // 0 .. 4095
+          const int key = idx >> 4, ch = idx & 15;
+          const int kc = min(kb + key, n_ctx - 1);
+          *reinterpret_cast<uint4*>(sK + key * LDS_ROW + ch * 8) =
+              *reinterpret_cast<const uint4*>(Kseq + (int64_t)kc * a.kv_st + ch * 8);
         }
       }
       f32x16 dk_acc[4], dv_acc[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) dk_acc[i] = dv_acc[i] = f32x16{};
+      const bool wave_live = kw0 < kend;        // the wave owns at least one key of the item
 
       if (ntq > 0) {
         QTileRegs R = load_q(0);
         __syncthreads();  // previous users of the query buffers are done
         store_q(R, 0);
-        // Drain every load before the prefetch starts, so that inside the loop
-        // only the prefetch is in flight and the MFMA phase never waits on it.
         __builtin_amdgcn_s_waitcnt(0);
         if (ntq > 1) R = load_q(1);
 
@@ -252,75 +246,69 @@ void bwd_kv_kernel(BwdArgs a) {
             store_q(R, buf);                       // tile qt, loaded during tile qt-1
             if (qt + 1 < ntq) R = load_q(qt + 1);  // in flight during this tile
           }
-          // Two buffers suffice: the buffer written above was last read before
-          // the previous iteration's barrier.
           __syncthreads();
+          if (!wave_live) continue;
           const uint16_t* bq = sQ[buf];
           const uint16_t* bo = sdO[buf];
           const QTileMeta& M = sMeta[buf];
+          // 32-bit LDS addresses of this lane's transposed reads; the empty asm
+          // keeps the per-read offsets as immediates.
+          uint32_t qt0 = lds_addr(bq + (4 * hf + (li >> 2)) * LDS_ROW + 16 * (gi & 1) + 4 * (li & 3));
+          uint32_t ot0 = lds_addr(bo + (4 * hf + (li >> 2)) * LDS_ROW + 16 * (gi & 1) + 4 * (li & 3));
+          asm volatile("" : "+v"(qt0), "+v"(ot0));
 
-          // ---- S = Q K^T and dP = dO V^T for 64 rows x this wave's 32 keys ----
-          f32x16 sacc[2], pacc[2];
-          sacc[0] = sacc[1] = pacc[0] = pacc[1] = f32x16{};
+          // ---- S = Q K^T and dP = dO V^T for 32 rows x this wave's 32 keys ----
+          f32x16 sacc = f32x16{}, pacc = f32x16{};
 #pragma unroll
           for (int ks = 0; ks < 8; ++ks) {
-#pragma unroll
-            for (int mt = 0; mt < 2; ++mt) {
-              const bf16x8 qa = lds_load_bf16x8(bq + (mt * 32 + l32) * LDS_ROW + ks * 16 + hf * 8);
-              const bf16x8 oa = lds_load_bf16x8(bo + (mt * 32 + l32) * LDS_ROW + ks * 16 + hf * 8);
-              sacc[mt] = mfma32x32x16(qa, kreg[ks], sacc[mt]);
-              pacc[mt] = mfma32x32x16(oa, vreg[ks], pacc[mt]);
-            }
+            if (ks & 1) asm volatile("" ::: "memory");  // bounds how far the compiler hoists the reads
+            const bf16x8 qa = lds_load_bf16x8(bq + l32 * LDS_ROW + ks * 16 + hf * 8);
+            const bf16x8 oa = lds_load_bf16x8(bo + l32 * LDS_ROW + ks * 16 + hf * 8);
+            const bf16x8 kf = lds_load_bf16x8(sK + (wave * 32 + l32) * LDS_ROW + ks * 16 + hf * 8);
+            sacc = mfma32x32x16(qa, kf, sacc);
+            pacc = mfma32x32x16(oa, vreg[ks], pacc);
           }
           // ---- P = exp2(s*c - LSE2) on visible entries, dS = P (dP - Delta) ----
-          // lane holds key key_w, rows mt*32 + 8i + 4hf + j (element 4i + j).
-          // Rows are sorted by prefix end, so if the tile's first row sees all
-          // 128 keys (and no row is padding) no entry needs masking.
-          const bool full = M.end[0] >= kb + KT && qt * QT + QT <= nq;
+          // lane holds key key_w, rows 8i + 4hf + j (element 4i + j).  Rows are
+          // sorted by prefix end: if the tile's first row sees all of this
+          // wave's keys (and no row is padding) no entry needs masking.
+          const bool full = M.end[0] >= kw0 + 32 && qt * QT + QT <= nq;
           if (!full) {
 #pragma unroll
-            for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                const int4 end4 = *reinterpret_cast<const int4*>(&M.end[mt * 32 + 8 * i + 4 * hf]);
-                const int ends[4] = {end4.x, end4.y, end4.z, end4.w};
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                  if (key_w >= ends[j]) sacc[mt][4 * i + j] = -INFINITY;
-              }
-          }
-#pragma unroll
-          for (int mt = 0; mt < 2; ++mt) {
-#pragma unroll
             for (int i = 0; i < 4; ++i) {
-              const int r0 = mt * 32 + 8 * i + 4 * hf;
-              const f32x4 lse4 = *reinterpret_cast<const f32x4*>(&M.lse[r0]);
-              const f32x4 del4 = *reinterpret_cast<const f32x4*>(&M.delta[r0]);
+              const int4 end4 = *reinterpret_cast<const int4*>(&M.end[8 * i + 4 * hf]);
+              const int ends[4] = {end4.x, end4.y, end4.z, end4.w};
 #pragma unroll
-              for (int j = 0; j < 4; ++j) {
-                const int e = 4 * i + j;
-                const float p = fast_exp2(__builtin_fmaf(sacc[mt][e], c, -lse4[j]));
-                sacc[mt][e] = p;
-                pacc[mt][e] = p * (pacc[mt][e] - del4[j]);
-              }
+              for (int j = 0; j < 4; ++j)
+                if (key_w >= ends[j]) sacc[4 * i + j] = -INFINITY;
             }
           }
           // ---- dV += P^T dO, dK += dS^T Q (A from registers, B transposed from LDS) ----
 #pragma unroll
-          for (int kstep = 0; kstep < 4; ++kstep) {
-            const int mt = kstep >> 1, qh = (kstep & 1) * 8;
-            const f32x16& ps = sacc[mt];
-            const f32x16& ds = pacc[mt];
-            const bf16x8 pa = to_bf16x8(ps[qh], ps[qh + 1], ps[qh + 2], ps[qh + 3], ps[qh + 4], ps[qh + 5],
-                                        ps[qh + 6], ps[qh + 7]);
-            const bf16x8 da = to_bf16x8(ds[qh], ds[qh + 1], ds[qh + 2], ds[qh + 3], ds[qh + 4], ds[qh + 5],
-                                        ds[qh + 6], ds[qh + 7]);
-            const int row0 = kstep * 16 + 4 * hf + (li >> 2);
+          for (int kstep = 0; kstep < 2; ++kstep) {
+            const int qh = kstep * 8;
+            float pv[8], dv8[8];
+#pragma unroll
+            for (int ii = 0; ii < 2; ++ii) {
+              const int i = (qh >> 2) + ii;
+              const int r0 = 8 * i + 4 * hf;
+              const f32x4 lse4 = *reinterpret_cast<const f32x4*>(&M.lse[r0]);
+              const f32x4 del4 = *reinterpret_cast<const f32x4*>(&M.delta[r0]);
+#pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                const float p = fast_exp2(__builtin_fmaf(sacc[4 * i + j], c, -lse4[j]));
+                pv[4 * ii + j] = p;
+                dv8[4 * ii + j] = p * (pacc[4 * i + j] - del4[j]);
+              }
+            }
+            const bf16x8 pa = to_bf16x8(pv[0], pv[1], pv[2], pv[3], pv[4], pv[5], pv[6], pv[7]);
+            const bf16x8 da = to_bf16x8(dv8[0], dv8[1], dv8[2], dv8[3], dv8[4], dv8[5], dv8[6], dv8[7]);
 #pragma unroll
             for (int nd = 0; nd < 4; ++nd) {
-              const int col = nd * 32 + 16 * (gi & 1) + 4 * (li & 3);
-              const bf16x8 ob = lds_tr_pair(bo + row0 * LDS_ROW + col, bo + (row0 + 8) * LDS_ROW + col);
-              const bf16x8 qb = lds_tr_pair(bq + row0 * LDS_ROW + col, bq + (row0 + 8) * LDS_ROW + col);
+              asm volatile("" ::: "memory");
+              const uint32_t so = 2u * (kstep * 16 * LDS_ROW + nd * 32);
+              const bf16x8 ob = lds_tr_pair(ot0 + so, ot0 + so + 2u * 8 * LDS_ROW);
+              const bf16x8 qb = lds_tr_pair(qt0 + so, qt0 + so + 2u * 8 * LDS_ROW);
               dv_acc[nd] = mfma32x32x16(pa, ob, dv_acc[nd]);
               dk_acc[nd] = mfma32x32x16(da, qb, dk_acc[nd]);
             }
@@ -328,12 +316,12 @@ void bwd_kv_kernel(BwdArgs a) {
         }
       }
 
-      // ---- write dK (scaled) and dV for the keys of this tile inside the item ----
+      // ---- write dK (scaled) and dV for this wave's keys inside the item ----
 #pragma unroll
       for (int nd = 0; nd < 4; ++nd)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const int key = kb + wave * 32 + (e >> 2) * 8 + 4 * hf + (e & 3);
+          const int key = kw0 + (e >> 2) * 8 + 4 * hf + (e & 3);
           if (key < kend) {
             const int64_t off = (k0 + key) * a.kv_st + (int64_t)g * a.kv_sh + nd * 32 + l32;
             dK[off] = f32_to_bf16_bits(a.sm_scale * dk_acc[nd][e]);
@@ -613,7 +601,7 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, int kv_workers, int q_workers, hipS
   }
   {
     TimedLaunch t(kBwdKv, stream);
-    hipLaunchKernelGGL(bwd_kv_kernel, dim3(kv_workers), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(bwd_kv_kernel, dim3(kv_workers), dim3(KV_THREADS), 0, stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   {
