@@ -199,24 +199,26 @@ def plan_compare(w, q, k, v, do, grads, dt, dev, K: int, warmup: int, bwd_granul
     from block_sparse_draft_amd import SplitKVAttention
     c = w.cfg
     out = []
-    for policy in ("static", "lpt"):
-        for steal in (False, True):
-            path = SplitKVAttention(w.q_off, w.kv_off, w.anchors, c.block, c.hq, c.hkv, c.d, c.chunk, w.sm_scale,
-                                    dt, dev, policy=policy, bwd_granule=bwd_granule, with_bwd=with_bwd,
-                                    steal=steal, ticks=True)
-            wall, ph, kt, _ = run_steps(path, q, k, v, do, grads, K, warmup, False, with_bwd)
-            rec = {"policy": policy, "steal": steal, "ms_per_step": round(wall / K * 1e3, 4),
-                   "fwd_ms": round(float(np.mean(ph["fwd"])), 4),
-                   "bwd_ms": round(float(np.mean(ph["bwd"])), 4) if with_bwd else None,
-                   "fwd_cost_imbalance": round(path.fwd_plan.imbalance, 5),
-                   "fwd_measured_imbalance": round(imbalance(path.fwd_plan.ticks.cpu().numpy()), 5)}
-            if with_bwd:
-                rec.update({"bwd_kv_cost_imbalance": round(path.bwd_plan.imbalance, 5),
-                            "bwd_kv_measured_imbalance": round(imbalance(path.bwd_plan.ticks.cpu().numpy()), 5),
-                            "bwd_dq_measured_imbalance": round(imbalance(path.dq_plan.ticks.cpu().numpy()), 5)})
-            out.append(rec)
-            del path
-            torch.cuda.empty_cache()
+    # one chunk per forward item in the four static/LPT rows; the last row adds chunk runs
+    for policy, steal, runs in (("static", False, None), ("static", True, None), ("lpt", False, None),
+                                ("lpt", True, None), ("lpt", True, 4.0)):
+        path = SplitKVAttention(w.q_off, w.kv_off, w.anchors, c.block, c.hq, c.hkv, c.d, c.chunk, w.sm_scale,
+                                dt, dev, policy=policy, bwd_granule=bwd_granule, with_bwd=with_bwd,
+                                steal=steal, ticks=True, fwd_runs_per_worker=runs)
+        wall, ph, kt, _ = run_steps(path, q, k, v, do, grads, K, warmup, False, with_bwd)
+        rec = {"policy": policy, "steal": steal, "fwd_runs_per_worker": runs,
+               "ms_per_step": round(wall / K * 1e3, 4),
+               "fwd_ms": round(float(np.mean(ph["fwd"])), 4),
+               "bwd_ms": round(float(np.mean(ph["bwd"])), 4) if with_bwd else None,
+               "fwd_cost_imbalance": round(path.fwd_plan.imbalance, 5),
+               "fwd_measured_imbalance": round(imbalance(path.fwd_plan.ticks.cpu().numpy()), 5)}
+        if with_bwd:
+            rec.update({"bwd_kv_cost_imbalance": round(path.bwd_plan.imbalance, 5),
+                        "bwd_kv_measured_imbalance": round(imbalance(path.bwd_plan.ticks.cpu().numpy()), 5),
+                        "bwd_dq_measured_imbalance": round(imbalance(path.dq_plan.ticks.cpu().numpy()), 5)})
+        out.append(rec)
+        del path
+        torch.cuda.empty_cache()
     return out
 
 
@@ -233,6 +235,9 @@ def main():
     ap.add_argument("--no-replan", action="store_true", help="plan once outside the timed region")
     ap.add_argument("--no-steal", action="store_true", help="workgroups run only their own plan lists")
     ap.add_argument("--plan-compare", action="store_true")
+    ap.add_argument("--runs-per-worker", type=float, default=4.0,
+                    help="forward items cover runs of consecutive chunks of the same rows (one partial per run), "
+                         "about this many runs per workgroup; 0 = one chunk per item (LPT only)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB")
     args = ap.parse_args()
 
@@ -272,7 +277,7 @@ def main():
 
     path = SplitKVAttention(w.q_off, w.kv_off, w.anchors, c.block, c.hq, c.hkv, c.d, c.chunk, w.sm_scale, dt, dev,
                             policy=args.policy, bwd_granule=args.bwd_granule, with_bwd=with_bwd,
-                            steal=not args.no_steal)
+                            steal=not args.no_steal, fwd_runs_per_worker=args.runs_per_worker or None)
     K = args.steps
     wall, ph, kt, plan_s = run_steps(path, q, k, v, do, grads, K, args.warmup, not args.no_replan, with_bwd)
 
@@ -318,7 +323,8 @@ def main():
         "config": {"workload": f"{c.name}: {WORKLOAD_TEXT.get(c.name, c.note)}", "seed": args.seed,
                    "n_ctx": [int(x) for x in w.n_ctx], "unmasked_pairs": int(pairs), "policy": args.policy,
                    "steal": not args.no_steal, "n_workers": path.n_workers, "fwd_granule_blocks": path.fwd_granule,
-                   "bwd_granule_keys": path.bwd_granule if with_bwd else None},
+                   "bwd_granule_keys": path.bwd_granule if with_bwd else None,
+                   "fwd_runs_per_worker": path.fwd_runs_per_worker},
         "pct_of_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "fwd": {"ms": round(fwd_ms, 4), "tflops": round(fwd_tf, 2), "frac": round(fwd_tf / PEAK_BF16_TFLOPS, 4)},
         "merge": {"ms": round(mrg_ms, 4), "launches": c.n_seq, "bytes": mbytes, "gbs": round(merge_gbs, 1),
@@ -328,6 +334,7 @@ def main():
         "kernels": kernels,
         "plan": {"host_ms_per_step": round(1e3 * float(np.mean(plan_s)), 3) if plan_s else None,
                  "fwd_items": path.fwd_plan.n_items, "fwd_items_planned": path.fwd_plan.n_planned,
+                 "fwd_partial_rows_written": int(torch.isfinite(path.lse_part).sum().item()),
                  "fwd_imbalance": round(path.fwd_plan.imbalance, 5),
                  "bwd_items": path.bwd_plan.n_items if with_bwd else None,
                  "bwd_imbalance": round(path.bwd_plan.imbalance, 5) if with_bwd else None},

@@ -43,12 +43,13 @@ class skv_problem(C.Structure):
 
 class skv_item(C.Structure):
     _fields_ = [("seq", C.c_int32), ("kv_head", C.c_int32), ("chunk", C.c_int32), ("range", C.c_int32),
-                ("part_base", C.c_int64), ("lo", C.c_int32), ("hi", C.c_int32)]
+                ("part_base", C.c_int64), ("lo", C.c_int32), ("hi", C.c_int32),
+                ("n_chunk", C.c_int32), ("reserved", C.c_int32)]
 
 
 ITEM_DTYPE = np.dtype([("seq", "<i4"), ("kv_head", "<i4"), ("chunk", "<i4"), ("range", "<i4"),
-                       ("part_base", "<i8"), ("lo", "<i4"), ("hi", "<i4")])
-assert ITEM_DTYPE.itemsize == C.sizeof(skv_item) == 32
+                       ("part_base", "<i8"), ("lo", "<i4"), ("hi", "<i4"), ("n_chunk", "<i4"), ("reserved", "<i4")])
+assert ITEM_DTYPE.itemsize == C.sizeof(skv_item) == 40
 
 
 class skv_plan(C.Structure):
@@ -80,6 +81,7 @@ def _load():
         "skv_static_plan": (C.c_int, [VP, I64, I64, I32, VP, VP, VP]),
         "skv_gather_items": (C.c_int, [VP, I64, VP, I64, VP]),
         "skv_drop_zero_cost": (C.c_int, [VP, I64, I32, VP, VP, VP, VP, P(I64)]),
+        "skv_coarsen_fwd_items": (C.c_int, [VP, VP, I64, I64, VP, VP, P(I64)]),
         "sparse_attn_partial_fwd": (C.c_int, [P(skv_problem), P(skv_plan), VP, VP, VP, VP, VP, VP, VP]),
         "lse_merge": (C.c_int, [I32, I32, I64, I32, VP, VP, VP, VP, I64, I64, I32, VP, I64, VP]),
         "skv_bwd_workspace_bytes": (C.c_size_t, [P(skv_problem)]),
@@ -95,7 +97,8 @@ def _load():
 
 lib = _load()
 EXPORTED = ("skv_last_error", "skv_check_problem", "skv_partial_layout", "skv_item_table", "lpt_plan",
-            "skv_static_plan", "skv_gather_items", "skv_drop_zero_cost", "sparse_attn_partial_fwd", "lse_merge",
+            "skv_static_plan", "skv_gather_items", "skv_drop_zero_cost", "skv_coarsen_fwd_items",
+            "sparse_attn_partial_fwd", "lse_merge",
             "skv_bwd_workspace_bytes", "sparse_attn_bwd", "skv_timing_enable", "skv_timing_collect")
 
 
@@ -186,6 +189,19 @@ def skv_drop_zero_cost(cost, order, worker_off):
     _check(lib.skv_drop_zero_cost(_ptr(cost), len(cost), nw, _ptr(order), _ptr(worker_off), _ptr(o2), _ptr(w2),
                                   C.byref(n)))
     return o2[:n.value].copy(), w2
+
+
+def skv_coarsen_fwd_items(items, cost, target: int):
+    """Runs of consecutive chunks of the same rows as single forward items.
+    Returns (items ITEM_DTYPE, cost int64)."""
+    items = np.ascontiguousarray(items, dtype=ITEM_DTYPE)
+    cost = np.ascontiguousarray(cost, dtype=np.int64)
+    n = len(cost)
+    it2 = np.empty(max(n, 1), ITEM_DTYPE)
+    c2 = np.empty(max(n, 1), np.int64)
+    m = C.c_int64(0)
+    _check(lib.skv_coarsen_fwd_items(_ptr(items), _ptr(cost), n, int(target), _ptr(it2), _ptr(c2), C.byref(m)))
+    return it2[:m.value].copy(), c2[:m.value].copy()
 
 
 class Problem:

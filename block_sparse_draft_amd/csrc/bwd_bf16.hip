@@ -411,12 +411,17 @@ void bwd_dq_kernel(BwdArgs a) {
     const int n_ctx = (int)(uniform(a.kv_off[s + 1]) - k0);
     // packed index of the item's first row: (s, kv head) block, then draft block it.lo
     const int64_t pitem = q0 * a.hq + (int64_t)it.kv_head * a.group * mq + (int64_t)it.lo * GB;
-    const int klo = it.chunk * a.chunk;
-    const int khi = min(klo + a.chunk, n_ctx);
     const int nrows = (it.hi - it.lo) * GB;
     const uint16_t* Kseq = K + k0 * a.kv_st + (int64_t)it.kv_head * a.kv_sh;
     const uint16_t* Vseq = V + k0 * a.kv_st + (int64_t)it.kv_head * a.kv_sh;
+    const int n_chunk = max(1, uniform(it.n_chunk));
 
+    // one dQ partial per chunk of the item (an item of several chunks writes
+    // each of them, exactly as the single-chunk items would)
+    for (int cc = 0; cc < n_chunk; ++cc) {
+    const int klo = (it.chunk + cc) * a.chunk;
+    const int khi = min(klo + a.chunk, n_ctx);
+    const int64_t part_base = it.part_base + (int64_t)cc * a.hq * mq;
     for (int rt = 0; rt < nrows; rt += 256) {
       const int p_last = min(nrows, rt + 256) - 1;
       const int wg_hi = max(klo, min(khi, a.endp[pitem + p_last]));
@@ -443,7 +448,7 @@ void bwd_dq_kernel(BwdArgs a) {
         const int64_t P = pitem + pc;
         const int e = a.endp[P];
         vend[nt] = valid[nt] ? max(klo, min(khi, e)) : klo;
-        prow[nt] = it.part_base + (int64_t)h * mq + r;
+        prow[nt] = part_base + (int64_t)h * mq + r;
         lse2[nt] = a.lsep[P];
         del[nt] = a.deltap[P];
         const uint16_t* qrow = a.qp + P * D + hf * 8;
@@ -548,6 +553,7 @@ void bwd_dq_kernel(BwdArgs a) {
           }
       }
     }
+    }  // chunks of the item
   }
   record_ticks(a.q_ticks, me, t_start);
 }

@@ -146,14 +146,16 @@ void fwd_bf16_kernel(FwdArgs a) {
     skv_item it = a.items[slot];
     it.seq = uniform(it.seq); it.kv_head = uniform(it.kv_head); it.chunk = uniform(it.chunk);
     it.lo = uniform(it.lo); it.hi = uniform(it.hi); it.part_base = uniform(it.part_base);
+    it.n_chunk = uniform(it.n_chunk);
     const int s = it.seq;
     const int64_t q0 = uniform(a.q_off[s]);
     const int64_t mq = uniform(a.q_off[s + 1]) - q0;
     const int64_t k0 = uniform(a.kv_off[s]);
     const int n_ctx = (int)(uniform(a.kv_off[s + 1]) - k0);
     const int64_t blk0 = q0 / a.block;
+    // keys of the item's chunks: [chunk*L, (chunk + n_chunk)*L) inside the context
     const int klo = it.chunk * a.chunk;
-    const int khi = min(klo + a.chunk, n_ctx);
+    const int khi = (int)min((int64_t)(it.chunk + max(1, it.n_chunk)) * a.chunk, (int64_t)n_ctx);
     const int nrows = (it.hi - it.lo) * GB;
     const uint16_t* Kseq = K + k0 * a.kv_st + (int64_t)it.kv_head * a.kv_sh;
     const uint16_t* Vseq = V + k0 * a.kv_st + (int64_t)it.kv_head * a.kv_sh;

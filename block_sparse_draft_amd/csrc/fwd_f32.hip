@@ -28,8 +28,9 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdArgs a) {
     const int64_t k0 = a.kv_off[s];
     const int n_ctx = (int)(a.kv_off[s + 1] - k0);
     const int64_t blk0 = q0 / a.block;
+    // keys of the item's chunks: [chunk*L, (chunk + n_chunk)*L) inside the context
     const int klo = it.chunk * a.chunk;
-    const int khi = min(klo + a.chunk, n_ctx);
+    const int khi = (int)min((int64_t)(it.chunk + max(1, it.n_chunk)) * a.chunk, (int64_t)n_ctx);
     const int nrows = (it.hi - it.lo) * GB;
     for (int p = threadIdx.x; p < nrows; p += blockDim.x) {
       const int b = it.lo + p / GB;

@@ -12,6 +12,7 @@
 #include <cstdio>
 #include <queue>
 #include <string>
+#include <tuple>
 #include <vector>
 
 #include "internal.h"
@@ -136,7 +137,8 @@ extern "C" int skv_item_table(const skv_problem* p, int32_t kind, int32_t granul
               cost[n] = G * sum;
             }
             if (tok_start) tok_start[n] = tok;
-            if (items) items[n] = skv_item{s, g, (int32_t)c, (int32_t)r, base + c * p->hq * v.mq, (int32_t)b0, (int32_t)b1};
+            if (items)
+              items[n] = skv_item{s, g, (int32_t)c, (int32_t)r, base + c * p->hq * v.mq, (int32_t)b0, (int32_t)b1, 1, 0};
             ++n;
           }
         } else {
@@ -150,7 +152,7 @@ extern "C" int skv_item_table(const skv_problem* p, int32_t kind, int32_t granul
               cost[n] = G * sum;
             }
             if (tok_start) tok_start[n] = tok + (klo - lo);
-            if (items) items[n] = skv_item{s, g, (int32_t)c, (int32_t)r, 0, (int32_t)klo, (int32_t)khi};
+            if (items) items[n] = skv_item{s, g, (int32_t)c, (int32_t)r, 0, (int32_t)klo, (int32_t)khi, 1, 0};
             ++n;
           }
         }
@@ -256,5 +258,53 @@ extern "C" int skv_drop_zero_cost(const int64_t* cost, int64_t n, int32_t n_work
   }
   *n_out = k;
   clear_error();
+  return SKV_OK;
+}
+
+// Runs of consecutive chunks of the same rows become one forward item.
+extern "C" int skv_coarsen_fwd_items(const skv_item* items, const int64_t* cost, int64_t n, int64_t target,
+                                     skv_item* items_out, int64_t* cost_out, int64_t* n_out) {
+  if (n < 0 || target < 1) return fail(SKV_EINVAL, "n = %lld, target = %lld", (long long)n, (long long)target);
+  if (n > 0 && (!items || !cost || !items_out || !cost_out)) return fail(SKV_EINVAL, "NULL array");
+  if (!n_out) return fail(SKV_EINVAL, "n_out is NULL");
+  for (int64_t i = 0; i < n; ++i)
+    if (items[i].n_chunk != 1 || cost[i] < 0)
+      return fail(SKV_EINVAL, "item %lld: n_chunk %d, cost %lld (single-chunk items with cost >= 0 expected)",
+                  (long long)i, items[i].n_chunk, (long long)cost[i]);
+  // group order: (seq, kv_head, lo, hi, chunk), ties by input index
+  std::vector<int64_t> idx(n);
+  for (int64_t i = 0; i < n; ++i) idx[i] = i;
+  auto key = [&](int64_t i) {
+    const skv_item& t = items[i];
+    return std::make_tuple(t.seq, t.kv_head, t.lo, t.hi, t.chunk, i);
+  };
+  std::sort(idx.begin(), idx.end(), [&](int64_t x, int64_t y) { return key(x) < key(y); });
+  struct Run { int64_t first; int32_t len; int64_t cost; };
+  std::vector<Run> runs;
+  bool open = false;
+  for (int64_t j = 0; j < n; ++j) {
+    const int64_t i = idx[j];
+    const skv_item& t = items[i];
+    bool join = false;
+    if (open && cost[i] > 0) {
+      const skv_item& f = items[runs.back().first];
+      join = f.seq == t.seq && f.kv_head == t.kv_head && f.lo == t.lo && f.hi == t.hi &&
+             t.chunk == f.chunk + runs.back().len && runs.back().cost < target;
+    }
+    if (join) {
+      runs.back().len += 1;
+      runs.back().cost += cost[i];
+    } else {
+      runs.push_back(Run{i, 1, cost[i]});
+    }
+    open = cost[i] > 0;  // a zero-cost item stands alone
+  }
+  std::sort(runs.begin(), runs.end(), [](const Run& x, const Run& y) { return x.first < y.first; });
+  for (size_t r = 0; r < runs.size(); ++r) {
+    items_out[r] = items[runs[r].first];
+    items_out[r].n_chunk = runs[r].len;
+    cost_out[r] = runs[r].cost;
+  }
+  *n_out = (int64_t)runs.size();
   return SKV_OK;
 }

@@ -26,9 +26,12 @@ class _PlanSlots:
     previous step's kernels may still read the other pair."""
 
     def __init__(self, problem: B.Problem, kind: int, granule: int, n_workers: int, policy: str,
-                 steal: bool = True, ticks: bool = False):
+                 steal: bool = True, ticks: bool = False, runs_per_worker: Optional[float] = None):
         import torch
         self.problem, self.kind, self.granule, self.n_workers, self.policy = problem, kind, granule, n_workers, policy
+        # forward only: chunks of the same rows merged into runs of about
+        # total cost / (n_workers * runs_per_worker) (None: one chunk per item)
+        self.runs_per_worker = runs_per_worker
         self.flags = 0 if steal else B.SKV_PLAN_NO_STEAL
         n = len(problem.item_table(kind, granule)[1])
         dev = problem.device
@@ -36,9 +39,9 @@ class _PlanSlots:
         self.slots = []
         for _ in range(2):
             self.slots.append({
-                "h_items": torch.empty(max(n, 1) * 32, dtype=torch.uint8, pin_memory=True),
+                "h_items": torch.empty(max(n, 1) * B.ITEM_DTYPE.itemsize, dtype=torch.uint8, pin_memory=True),
                 "h_off": torch.empty(n_workers + 1, dtype=torch.int64, pin_memory=True),
-                "d_items": torch.empty(max(n, 1) * 32, dtype=torch.uint8, device=dev),
+                "d_items": torch.empty(max(n, 1) * B.ITEM_DTYPE.itemsize, dtype=torch.uint8, device=dev),
                 "d_off": torch.empty(n_workers + 1, dtype=torch.int64, device=dev),
                 "event": torch.cuda.Event(), "used": False})
         self.claim = torch.zeros(n_workers, dtype=torch.int32, device=dev)  # reset by the library per call
@@ -48,6 +51,7 @@ class _PlanSlots:
         self.plan_s = 0.0
         self.c = None
         self.load = self.cost = None
+        self.table = None
 
     def replan(self):
         """Realized costs -> LPT (or static) plan -> async upload.  Returns the skv_plan.
@@ -55,6 +59,12 @@ class _PlanSlots:
         import time
         t0 = time.perf_counter()
         items, cost, tok, total = self.problem.item_table(self.kind, self.granule)
+        if self.runs_per_worker and self.kind == B.SKV_ITEM_FWD:
+            if self.policy != "lpt":
+                raise ValueError("chunk runs are planned with LPT only")
+            target = max(1, int(np.ceil(cost.sum() / (self.n_workers * self.runs_per_worker))))
+            items, cost = B.skv_coarsen_fwd_items(items, cost, target)
+        self.table = (items, cost)  # the items planned (chunk runs when asked for)
         if self.policy == "lpt":
             _, order, off, load = B.lpt_plan(cost, self.n_workers)
         elif self.policy == "static":
@@ -101,7 +111,8 @@ class SplitKVAttention:
     def __init__(self, q_off, kv_off, anchors, block: int, hq: int, hkv: int, d: int, chunk: int,
                  sm_scale: float, dtype, device, n_workers: Optional[int] = None,
                  fwd_granule: Optional[int] = None, bwd_granule: int = 256, policy: str = "lpt",
-                 with_bwd: bool = True, steal: bool = True, ticks: bool = False):
+                 with_bwd: bool = True, steal: bool = True, ticks: bool = False,
+                 fwd_runs_per_worker: Optional[float] = 4.0):
         import torch
         self.device = torch.device(device)
         self.dtype = dtype
@@ -114,7 +125,12 @@ class SplitKVAttention:
         self.fwd_granule = fwd_granule or max(1, 256 // (G * block))
         self.bwd_granule = bwd_granule
         kw = dict(steal=steal, ticks=ticks)
-        self.fwd_plan = _PlanSlots(self.problem, B.SKV_ITEM_FWD, self.fwd_granule, self.n_workers, policy, **kw)
+        # Forward items cover runs of consecutive chunks of the same rows, about
+        # fwd_runs_per_worker per workgroup, each with one partial (LPT plans
+        # only; None or a static plan: one chunk per item, one partial per chunk).
+        self.fwd_runs_per_worker = fwd_runs_per_worker if policy == "lpt" else None
+        self.fwd_plan = _PlanSlots(self.problem, B.SKV_ITEM_FWD, self.fwd_granule, self.n_workers, policy, **kw,
+                                   runs_per_worker=self.fwd_runs_per_worker)
         self.bwd_plan = (_PlanSlots(self.problem, B.SKV_ITEM_BWD, self.bwd_granule, self.n_workers, policy, **kw)
                          if with_bwd else None)
         # dQ runs over the forward's items; its own slots give it separate claim cursors

@@ -83,16 +83,21 @@ typedef struct skv_problem {
   int64_t kv_stride_tok, kv_stride_head; /* elements; head_dim is contiguous */
 } skv_problem;
 
-/* One work item, 32 bytes.  Built on the host by skv_item_table.
+/* One work item, 40 bytes.  Built on the host by skv_item_table (and
+ * skv_coarsen_fwd_items).
  * FWD: (seq, kv_head, chunk, range) covers draft blocks [lo, hi) of the
- *      sequence, all hq/hkv query heads of kv_head, against chunk `chunk`;
- *      part_base is the first partial row of (seq, chunk).
+ *      sequence, all hq/hkv query heads of kv_head, against the n_chunk
+ *      consecutive chunks chunk .. chunk + n_chunk - 1 (one contiguous key
+ *      range); part_base is the first partial row of (seq, chunk), where the
+ *      item writes the one partial of all its chunks.
  * BWD: covers context keys [lo, hi) of the sequence (inside chunk `chunk`)
- *      for kv_head; part_base is unused (0). */
+ *      for kv_head; part_base is unused (0); n_chunk is 1.
+ * skv_item_table sets n_chunk = 1; kernels treat n_chunk < 1 as 1. */
 typedef struct skv_item {
   int32_t seq, kv_head, chunk, range;
   int64_t part_base;
   int32_t lo, hi;
+  int32_t n_chunk, reserved;
 } skv_item;
 
 /* A plan as the kernels read it: items grouped by persistent workgroup.
@@ -182,6 +187,23 @@ int skv_gather_items(const skv_item* items, int64_t n_items, const int64_t* orde
 int skv_drop_zero_cost(const int64_t* cost, int64_t n, int32_t n_workers, const int64_t* order,
                        const int64_t* worker_off, int64_t* order_out, int64_t* worker_off_out, int64_t* n_out);
 
+/* Local merge of chunks before the exchange (host, pure).  The pages' ranks
+ * each aggregate the attention results of the KV they hold before the
+ * query-sized exchange (Split-KV article, "Split-KV's Core Mechanism"); here a
+ * forward item may likewise cover several consecutive chunks of the same rows
+ * and emit a single partial for them, so rows get fewer partials to write and
+ * merge.  Input: single-chunk FWD items (n_chunk == 1) with their costs, e.g.
+ * skv_item_table output or a subset of it.  Items with equal (seq, kv_head,
+ * lo, hi) form a group; in ascending chunk order each group is cut into runs:
+ * a zero-cost item is emitted alone, and an item joins the open run iff its
+ * chunk follows the run's last chunk and the run's cost is still below
+ * `target` (>= 1).  Each run becomes one item (the first item's fields,
+ * n_chunk = run length) whose cost is the sum.  Runs are written in the
+ * order of their first item in the input.  items_out and cost_out hold n
+ * entries; *n_out receives the count.  target = 1 leaves the table as is. */
+int skv_coarsen_fwd_items(const skv_item* items, const int64_t* cost, int64_t n, int64_t target,
+                          skv_item* items_out, int64_t* cost_out, int64_t* n_out);
+
 /* Forward partials, one per (sequence, KV chunk).  For every query row r of
  * sequence s, query head h and chunk c with visible keys
  * J = {j in [c*L, min((c+1)*L, N_s)) : j < e_b}:
@@ -195,7 +217,10 @@ int skv_drop_zero_cost(const int64_t* cost, int64_t n, int32_t n_workers, const 
  * covering every (seq, kv_head, chunk, range) of nonzero cost exactly once
  * (zero-cost items may be left out, see skv_drop_zero_cost): the call first
  * sets m_part and lse_part of every partial row to -inf, then runs the plan
- * with plan->n_workers workgroups.  Results are bitwise deterministic. */
+ * with plan->n_workers workgroups.  Results are bitwise deterministic.
+ * With items of several chunks (skv_coarsen_fwd_items) the partial of such an
+ * item covers the keys of all its chunks and sits in its first chunk's rows;
+ * the other chunks' rows stay -inf, and lse_merge gives the same result. */
 int sparse_attn_partial_fwd(const skv_problem* p, const skv_plan* plan, const void* q, const void* k,
                             const void* v, float* o_part, float* m_part, float* lse_part, void* stream);
 

@@ -25,5 +25,5 @@ from .attention import (  # noqa: F401
 )
 from .plan import (  # noqa: F401
     item_table, lpt, static_assign, csr_from_assign, loads_from_assign, imbalance,
-    brute_force_makespan, graham_bound,
+    brute_force_makespan, graham_bound, coarsen_runs,
 )

@@ -29,6 +29,14 @@ Readings of what the pages leave open:
     item starting at token offset x of that stream goes to worker
     floor(x * W / total).  All block ranges of one unit share its start.
   * Imbalance: max worker load / mean worker load - 1.
+  * Local merge before the exchange: the pages' ranks each aggregate the
+    attention results of the KV they hold before the query-sized exchange
+    ([P1] "Split-KV's Core Mechanism").  Here forward items of the same rows
+    (s, g, r) and consecutive chunks are merged into runs, each with one
+    partial.  Rule: per (s, g, r) in ascending chunk order, a zero-cost item
+    stays alone; an item joins the open run iff its chunk follows the run's
+    last chunk and the run's cost is still below the target; runs are listed
+    in the order of their first item.
 """
 from __future__ import annotations
 
@@ -160,3 +168,36 @@ def brute_force_makespan(cost, n_workers: int) -> int:
 def graham_bound(n_workers: int) -> float:
     """Graham's worst-case ratio of LPT to the optimum on m machines."""
     return 4.0 / 3.0 - 1.0 / (3.0 * n_workers)
+
+
+def coarsen_runs(desc, cost, target: int):
+    """Merge forward items into runs of consecutive chunks of the same rows.
+
+    ``desc`` rows are (s, g, c, r) as ``item_table`` returns them.  Returns
+    (first int64 [m] = item id of each run's first chunk, length int64 [m],
+    cost int64 [m]), runs in ascending order of ``first``.
+    """
+    if target < 1:
+        raise ValueError("target must be >= 1")
+    desc = np.asarray(desc)
+    cost = np.asarray(cost, dtype=np.int64)
+    groups = {}
+    for i in range(len(cost)):
+        s, g, c, r = (int(x) for x in desc[i])
+        groups.setdefault((s, g, r), []).append((c, i))
+    runs = []  # [first, length, cost, last chunk]
+    for key in groups:
+        open_run = None
+        for c, i in sorted(groups[key]):
+            w = int(cost[i])
+            if w > 0 and open_run is not None and c == open_run[3] + 1 and open_run[2] < target:
+                open_run[1] += 1
+                open_run[2] += w
+                open_run[3] = c
+                continue
+            run = [i, 1, w, c]
+            runs.append(run)
+            open_run = run if w > 0 else None
+    runs.sort(key=lambda x: x[0])
+    return (np.asarray([x[0] for x in runs], dtype=np.int64), np.asarray([x[1] for x in runs], dtype=np.int64),
+            np.asarray([x[2] for x in runs], dtype=np.int64))

@@ -30,6 +30,7 @@ def make_path(w, dev, **kw):
     from block_sparse_draft_amd import SplitKVAttention
     c = w.cfg
     dt = torch.bfloat16 if w.is_bf16 else torch.float32
+    kw.setdefault("fwd_runs_per_worker", None)  # one partial per chunk unless a test asks for runs
     return SplitKVAttention(w.q_off, w.kv_off, w.anchors, c.block, c.hq, c.hkv, c.d, c.chunk, w.sm_scale, dt, dev,
                             with_bwd=kw.pop("with_bwd", c.bwd and w.is_bf16), **kw)
 

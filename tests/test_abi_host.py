@@ -244,7 +244,7 @@ def test_drop_zero_cost_matches_filtering():
             lst = order[off[w]:off[w + 1]]
             assert np.array_equal(o2[w2[w]:w2[w + 1]], lst[cost[lst] != 0])
     # a c5-shaped forward table: LPT alone gives one worker every zero-cost item
-    w = make("c5", seed=0, with_do=False)
+    w = _meta_only("c5", {})
     p = _problem_from(w)
     items, cost, tok, total = p.item_table(B.SKV_ITEM_FWD, 8)
     _, order, off, _ = B.lpt_plan(cost, 256)
@@ -255,3 +255,37 @@ def test_drop_zero_cost_matches_filtering():
     bad = off.copy(); bad[-1] += 1
     with pytest.raises(B.SkvError):
         B.skv_drop_zero_cost(cost, order, bad)
+
+
+@pytest.mark.parametrize("cfg,granule", [("c3", 4), ("c4", 4), ("c5", 8)])
+@pytest.mark.parametrize("target", [1, 97, 2000, 1 << 40])
+def test_coarsen_fwd_items_matches_oracle(cfg, granule, target):
+    """skv_coarsen_fwd_items forms exactly the oracle's runs (bit-exact)."""
+    w = _meta_only(cfg, {})
+    p = _problem_from(w)
+    items, cost, _, _ = p.item_table(B.SKV_ITEM_FWD, granule)
+    assert np.all(items["n_chunk"] == 1)
+    it2, c2 = B.skv_coarsen_fwd_items(items, cost, target)
+    desc, ocost, _, _ = _oracle_table(w, "fwd", granule)
+    first, length, rcost = oracle.coarsen_runs(desc, ocost, target)
+    assert np.array_equal(c2, rcost)
+    assert np.array_equal(it2["n_chunk"], length)
+    ref = items[first]
+    for f in ("seq", "kv_head", "chunk", "range", "part_base", "lo", "hi"):
+        assert np.array_equal(it2[f], ref[f]), f
+
+
+def test_coarsen_fwd_items_rejects_bad_input():
+    w = make("c2", seed=0, n_ctx=4096, n_anchor=4, with_do=False)
+    p = _problem_from(w)
+    items, cost, _, _ = p.item_table(B.SKV_ITEM_FWD, 1)
+    with pytest.raises(B.SkvError):
+        B.skv_coarsen_fwd_items(items, cost, 0)          # target below 1
+    it2, c2 = B.skv_coarsen_fwd_items(items, cost, 1 << 40)
+    if (it2["n_chunk"] > 1).any():
+        with pytest.raises(B.SkvError):
+            B.skv_coarsen_fwd_items(it2, c2, 10)         # already coarsened
+    bad = cost.copy(); bad[0] = -1
+    with pytest.raises(B.SkvError):
+        B.skv_coarsen_fwd_items(items, bad, 10)
+    assert B.skv_coarsen_fwd_items(items[:0], cost[:0], 5)[0].shape == (0,)

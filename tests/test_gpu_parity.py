@@ -100,6 +100,43 @@ def test_bf16_forward_small(case):
     _check_merged(path, w, O, L)
 
 
+@pytest.mark.parametrize("case,runs_per_worker", [("c4_small", 1), ("c3_small", 2), ("c5_small", 1),
+                                                  ("c2_small", 0.5)])
+def test_bf16_forward_chunk_runs(case, runs_per_worker):
+    """Forward items that cover runs of consecutive chunks of the same rows
+    (one partial per run, in the run's first chunk): the merged O and LSE match
+    the oracle, each run's partial is the oracle's merge of its chunks'
+    partials, and the run's other chunk rows stay -inf."""
+    cfg, over = SMALL_BF16[case]
+    w = make(cfg, seed=7, with_do=False, **over)
+    path = make_path(w, DEV, with_bwd=False, n_workers=8, fwd_runs_per_worker=runs_per_worker)
+    q, k, v = _upload(w)
+    path.forward(q, k, v)
+    torch.cuda.synchronize()
+    O, L = oracle.attention_workload(w)
+    _check_merged(path, w, O, L)
+    items, cost = path.fwd_plan.table
+    assert (items["n_chunk"] > 1).any()
+    G, B = w.cfg.hq // w.cfg.hkv, w.cfg.block
+    parts = {s: oracle.partials_workload(w, s) for s in range(w.cfg.n_seq)}
+    views = {s: [to_np64(t) for t in path.partial_view(s)] for s in range(w.cfg.n_seq)}
+    for it, c in zip(items, cost):
+        if c == 0:
+            continue
+        s, g, c0, n = int(it["seq"]), int(it["kv_head"]), int(it["chunk"]), int(it["n_chunk"])
+        rows = slice(int(it["lo"]) * B, int(it["hi"]) * B)
+        hs = slice(g * G, (g + 1) * G)
+        op, mp, lp = (x[c0:c0 + n, hs, rows] for x in parts[s])
+        ro, rl = oracle.lse_merge(op, mp, lp)            # [rows, G, D], [rows, G]
+        go, gm, gl = (x[:, hs, rows] for x in views[s])
+        assert_lse(f"run s{s} g{g} c{c0}+{n} lse", gl[c0].T, rl, BF16_LSE_REL)
+        vis = np.isfinite(rl)
+        with np.errstate(invalid="ignore", over="ignore"):
+            gn = go[c0] * np.exp(np.where(vis.T, gm[c0] - gl[c0], 0.0))[..., None]
+        assert_close(f"run s{s} g{g} c{c0}+{n} o", gn.transpose(1, 0, 2)[vis], ro[vis], BF16_ABS, BF16_FROB)
+        assert np.all(gl[c0 + 1:c0 + n] == -np.inf) and np.all(gm[c0 + 1:c0 + n] == -np.inf)
+
+
 def test_bf16_forward_edge_anchors():
     """Anchors at 0, at N-1 (clipped block), duplicates, and a context whose
     length is not a multiple of the tile."""
@@ -180,7 +217,7 @@ def test_full_size_fwd_bwd_sampled(cfg, kv_heads, seqs):
     """Full configuration on the GPU, compared with the oracle on one KV head
     (and one sequence for the 4-sequence config)."""
     w = make(cfg, seed=0)
-    path = make_path(w, DEV)
+    path = make_path(w, DEV, fwd_runs_per_worker=4)  # the driver's default plan (chunk runs)
     q, k, v = _upload(w)
     got = _bwd(w, path, q, k, v)
     G = w.cfg.hq // w.cfg.hkv

@@ -128,3 +128,69 @@ def test_lpt_beats_static_under_skewed_anchors():
     assert oracle.imbalance(lpt_load) < 0.05 < oracle.imbalance(st_load)
     order, off = oracle.csr_from_assign(oracle.static_assign(tok, total, W), W)
     assert sorted(order.tolist()) == list(range(len(cost))) and off[-1] == len(cost)
+
+
+# ---- local merge of consecutive chunks (runs) ----
+
+def test_coarsen_runs_worked_example():
+    # Two row ranges (r = 0, 1) of one (s, g), chunks 0..3, numbered row-major
+    # (c, r): ids 0..7.  Costs fall with the chunk as prefixes end.
+    desc = [(0, 0, c, r) for c in range(4) for r in range(2)]
+    cost = [5, 7, 4, 7, 3, 0, 0, 0]
+    first, length, rcost = oracle.coarsen_runs(desc, cost, 8)
+    # r = 0: chunks 0+1 (5 + 4 = 9 reaches 8, closes), chunk 2 (3) alone (group ends
+    #        with chunk 3 of cost 0, which stays alone);
+    # r = 1: chunks 0+1 (7 < 8, then 14), chunk 2 (0) alone, chunk 3 (0) alone.
+    assert first.tolist() == [0, 1, 4, 5, 6, 7]
+    assert length.tolist() == [2, 2, 1, 1, 1, 1]
+    assert rcost.tolist() == [9, 14, 3, 0, 0, 0]
+    # target 1: no run grows past one chunk
+    f1, l1, c1 = oracle.coarsen_runs(desc, cost, 1)
+    assert f1.tolist() == list(range(8)) and l1.tolist() == [1] * 8 and c1.tolist() == cost
+
+
+def _run_members(desc, first, length):
+    idx = {tuple(int(x) for x in d): i for i, d in enumerate(desc)}
+    out = []
+    for f, n in zip(first, length):
+        s, g, c, r = (int(x) for x in desc[f])
+        out.append([idx[(s, g, c + k, r)] for k in range(int(n))])
+    return out
+
+
+@pytest.mark.parametrize("target", [1, 40, 500, 10 ** 12])
+def test_coarsen_runs_properties(target):
+    rng = np.random.default_rng(11)
+    n_ctx = [5000, 1500, 9000]
+    anchors = [np.sort(rng.integers(0, n, size=12)) for n in n_ctx]
+    desc, cost, _, _ = oracle.item_table(n_ctx, anchors, 16, 4, 2, 256, "fwd", 3)
+    first, length, rcost = oracle.coarsen_runs(desc, cost, target)
+    members = _run_members(desc, first, length)
+    # a partition of the items into runs of consecutive chunks, costs preserved
+    flat = sorted(i for m in members for i in m)
+    assert flat == list(range(len(cost)))
+    for m, c in zip(members, rcost):
+        assert c == cost[m].sum()
+        assert m[0] == min(m)
+    assert np.all(np.diff(first) > 0)
+    # zero-cost items stand alone; a run is cut below the target only where its
+    # group's next chunk is missing or costs nothing
+    nxt = {}
+    for i, d in enumerate(desc):
+        nxt[(int(d[0]), int(d[1]), int(d[2]) - 1, int(d[3]))] = i
+    for m, c in zip(members, rcost):
+        if any(cost[i] == 0 for i in m):
+            assert len(m) == 1
+            continue
+        s, g, cl, r = (int(x) for x in desc[m[-1]])
+        j = nxt.get((s, g, cl, r))
+        if j is not None and cost[j] > 0:
+            assert c >= target
+        # no run keeps growing once it has reached the target
+        assert c - cost[m[-1]] < target
+    if target == 1:
+        assert len(first) == len(cost)
+    if target == 10 ** 12:
+        # one run per (s, g, r) over its nonzero chunks (they start at chunk 0)
+        n_groups = len({(int(d[0]), int(d[1]), int(d[3])) for d, c in zip(desc, cost) if c > 0})
+        assert len(first) == n_groups + int((cost == 0).sum())
