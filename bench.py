@@ -62,7 +62,7 @@ def merge_bytes(path, d: int) -> int:
     return rows * 8 + visible * d * 4 + out_rows * (d * out_el + 4)
 
 
-def cpu_baseline(w, budget_s: float = 12.0):
+def cpu_baseline(w, budget_s: float = 12.0, mask: str = "prefix"):
     """Time the float64 oracle (forward + backward) on (sequence, KV head) slices
     of the workload until ~budget_s of CPU work; report unmasked TFLOP/s on the
     same 14*d-per-triple convention."""
@@ -78,7 +78,20 @@ def cpu_baseline(w, budget_s: float = 12.0):
     for s in range(c.n_seq):
         for g in range(c.hkv):
             t0 = time.perf_counter()
-            if c.bwd and w.do is not None:
+            if mask == "own_block":
+                qs = slice(int(w.q_off[s]), int(w.q_off[s + 1]))
+                ks = slice(int(w.kv_off[s]), int(w.kv_off[s + 1]))
+                args = [w.as_f64(n, rows=qs if n in ("q", "k_own", "v_own") else ks)
+                        for n in ("q", "k", "v", "k_own", "v_own")]
+                if c.bwd and w.do is not None:
+                    oracle.attention_own_bwd(*args, w.seq_anchors(s), c.block, w.sm_scale,
+                                             w.as_f64("do", rows=qs), kv_heads=[g])
+                    per_pair = 14 * c.d
+                else:
+                    oracle.attention_own(*args, w.seq_anchors(s), c.block, w.sm_scale,
+                                         heads=range(g * G, (g + 1) * G))
+                    per_pair = 4 * c.d
+            elif c.bwd and w.do is not None:
                 oracle.bwd_workload(w, kv_heads=[g], seqs=[s])
                 per_pair = 14 * c.d
             else:
@@ -88,7 +101,10 @@ def cpu_baseline(w, budget_s: float = 12.0):
                 oracle.attention(q, k, v, w.seq_anchors(s), c.block, w.sm_scale, heads=range(g * G, (g + 1) * G))
                 per_pair = 4 * c.d
             t += time.perf_counter() - t0
-            e = np.minimum(w.seq_anchors(s).astype(np.int64) + c.block, int(w.n_ctx[s]))
+            if mask == "own_block":
+                e = np.minimum(w.seq_anchors(s).astype(np.int64), int(w.n_ctx[s])) + c.block
+            else:
+                e = np.minimum(w.seq_anchors(s).astype(np.int64) + c.block, int(w.n_ctx[s]))
             flops += float(e.sum()) * c.block * G * per_pair
             done.append((s, g))
             if t >= budget_s:
@@ -146,7 +162,7 @@ def hbm_traffic(kernel: str, config: str):
         return None
 
 
-def run_steps(path, q, k, v, do, grads, K: int, warmup: int, replan: bool, with_bwd: bool):
+def run_steps(path, q, k, v, do, grads, K: int, warmup: int, replan: bool, with_bwd: bool, own=None):
     """Warm up, then time K steps.  Returns wall seconds, per-phase event ms
     (lists) and the library's per-kernel event times."""
     import torch
@@ -159,12 +175,15 @@ def run_steps(path, q, k, v, do, grads, K: int, warmup: int, replan: bool, with_
             path.replan()
             plan_s.append(path.plan_s)
         if e: e[0].record()
-        path.partial_fwd(q, k, v)
+        if own is None:
+            path.partial_fwd(q, k, v)
+        else:
+            path.partial_fwd(q, k, v, k_own=own[0], v_own=own[1])
         if e: e[1].record()
         path.merge()
         if e: e[2].record()
         if with_bwd:
-            path.backward(q, k, v, do, *grads)
+            path.backward(q, k, v, do, *grads, own=own)
         if e: e[3].record()
 
     for _ in range(warmup):
@@ -235,6 +254,8 @@ def main():
     ap.add_argument("--no-replan", action="store_true", help="plan once outside the timed region")
     ap.add_argument("--no-steal", action="store_true", help="workgroups run only their own plan lists")
     ap.add_argument("--plan-compare", action="store_true")
+    ap.add_argument("--mask", default="prefix", choices=["prefix", "own_block"],
+                    help="own_block: context prefix [0, a_b) plus each block's own keys (seeded k_own, v_own)")
     ap.add_argument("--runs-per-worker", type=float, default=4.0,
                     help="forward items cover runs of consecutive chunks of the same rows (one partial per run), "
                          "about this many runs per workgroup; 0 = one chunk per item (LPT only)")
@@ -248,10 +269,12 @@ def main():
 
     import torch
     from block_sparse_draft_amd import SplitKVAttention, unmasked_pairs
-    from synthetic import make
+    from synthetic import add_own_block, make
 
     dev = torch.device("cuda:0")
     w = make(args.config, seed=args.seed)
+    if args.mask == "own_block":
+        add_own_block(w)
     c = w.cfg
     dt = torch.bfloat16 if w.is_bf16 else torch.float32
 
@@ -265,6 +288,10 @@ def main():
     with_bwd = c.bwd and w.is_bf16
     do = up("do") if with_bwd else None
     grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)) if with_bwd else None
+    own = None
+    if args.mask == "own_block":
+        ko, vo = up("k_own"), up("v_own")
+        own = (ko, vo, torch.empty_like(ko), torch.empty_like(vo)) if with_bwd else (ko, vo, None, None)
 
     if args.copy_calibration > 0:
         # one plain device-to-device copy of known size, for scaling HBM byte counters
@@ -277,14 +304,17 @@ def main():
 
     path = SplitKVAttention(w.q_off, w.kv_off, w.anchors, c.block, c.hq, c.hkv, c.d, c.chunk, w.sm_scale, dt, dev,
                             policy=args.policy, bwd_granule=args.bwd_granule, with_bwd=with_bwd,
-                            steal=not args.no_steal, fwd_runs_per_worker=args.runs_per_worker or None)
+                            steal=not args.no_steal, fwd_runs_per_worker=args.runs_per_worker or None,
+                            mask=args.mask)
     K = args.steps
-    wall, ph, kt, plan_s = run_steps(path, q, k, v, do, grads, K, args.warmup, not args.no_replan, with_bwd)
+    wall, ph, kt, plan_s = run_steps(path, q, k, v, do, grads, K, args.warmup, not args.no_replan, with_bwd, own)
 
     fwd_ms = float(np.mean(ph["fwd"]))
     mrg_ms = float(np.mean(ph["merge"]))
     bwd_ms = float(np.mean(ph["bwd"]))
-    pairs = unmasked_pairs(w.q_off, w.kv_off, w.anchors, c.block, c.hq)
+    pairs = unmasked_pairs(w.q_off, w.kv_off, w.anchors, c.block, c.hq, mask=args.mask)
+    # triples the context kernels handle (the own-block keys go to own_fwd / own_bwd)
+    ctx_pairs = pairs - (int(w.q_off[-1]) * c.hq * c.block if args.mask == "own_block" else 0)
     fwd_flops = 4.0 * c.d * pairs
     bwd_flops = 10.0 * c.d * pairs if with_bwd else 0.0
     ms_per_step = wall / K * 1e3
@@ -299,21 +329,21 @@ def main():
         avg = tot / max(n_launch, 1)
         rec = {"launches_per_step": n_launch / K, "avg_ms": round(avg, 4)}
         if name in KERNEL_FLOPS_D:
-            alg = KERNEL_FLOPS_D[name] * c.d * pairs
+            alg = KERNEL_FLOPS_D[name] * c.d * ctx_pairs
             rec["alg_tflops"] = round(alg / (avg * 1e-3) / 1e12, 2)
-            rec["exec_tflops"] = round(KERNEL_EXEC_FLOPS_D[name] * c.d * pairs / (avg * 1e-3) / 1e12, 2)
+            rec["exec_tflops"] = round(KERNEL_EXEC_FLOPS_D[name] * c.d * ctx_pairs / (avg * 1e-3) / 1e12, 2)
         if name == "lse_merge":
             rec["gbs"] = round(mbytes / (tot / K * 1e-3) / 1e9, 1)
         kernels[name] = rec
     compute = {n: kt[n][1] for n in KERNEL_FLOPS_D if n in kt}
     dom = max(compute, key=compute.get)
     dom_avg = kt[dom][1] / kt[dom][0]
-    dom_flops = KERNEL_FLOPS_D[dom] * c.d * pairs
+    dom_flops = KERNEL_FLOPS_D[dom] * c.d * ctx_pairs
     achieved = dom_flops / (dom_avg * 1e-3) / 1e12
     roof = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS
             if w.is_bf16 else 157.3, "unit": "TFLOP/s",
             "frac": round(achieved / (PEAK_BF16_TFLOPS if w.is_bf16 else 157.3), 4),
-            "traffic": hbm_traffic(dom, c.name),
+            "traffic": hbm_traffic(dom, c.name) if args.mask == "prefix" else None,
             "alg_flops_per_launch": dom_flops, "avg_launch_ms": round(dom_avg, 4)}
     out = {
         "metric": "unmasked-FLOP TFLOP/s fwd+bwd, % of bf16 MFMA peak; merge GB/s",
@@ -324,7 +354,7 @@ def main():
                    "n_ctx": [int(x) for x in w.n_ctx], "unmasked_pairs": int(pairs), "policy": args.policy,
                    "steal": not args.no_steal, "n_workers": path.n_workers, "fwd_granule_blocks": path.fwd_granule,
                    "bwd_granule_keys": path.bwd_granule if with_bwd else None,
-                   "fwd_runs_per_worker": path.fwd_runs_per_worker},
+                   "fwd_runs_per_worker": path.fwd_runs_per_worker, "mask": args.mask},
         "pct_of_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "fwd": {"ms": round(fwd_ms, 4), "tflops": round(fwd_tf, 2), "frac": round(fwd_tf / PEAK_BF16_TFLOPS, 4)},
         "merge": {"ms": round(mrg_ms, 4), "launches": c.n_seq, "bytes": mbytes, "gbs": round(merge_gbs, 1),
@@ -346,7 +376,7 @@ def main():
         out["plan_compare"] = plan_compare(w, q, k, v, do, grads, dt, dev, max(3, K // 2), 2, args.bwd_granule,
                                            with_bwd)
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w)
+        out["cpu_baseline"] = cpu_baseline(w, mask=args.mask)
     print(json.dumps(out), flush=True)
 
 

@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsplitkv.
 
 SKV_OK, SKV_EINVAL, SKV_EDTYPE, SKV_ESHAPE, SKV_EHIP, SKV_EWORKSPACE, SKV_EPLAN = 0, -1, -2, -3, -4, -5, -6
 SKV_F32, SKV_BF16 = 0, 1
+SKV_MASK_PREFIX, SKV_MASK_OWN_BLOCK = 0, 1
 SKV_ITEM_FWD, SKV_ITEM_BWD = 0, 1
 SKV_TILE = 64
 SKV_PLAN_NO_STEAL = 1
@@ -35,10 +36,16 @@ class SkvError(RuntimeError):
 class skv_problem(C.Structure):
     _fields_ = [("n_seq", C.c_int32), ("block", C.c_int32), ("hq", C.c_int32), ("hkv", C.c_int32),
                 ("d", C.c_int32), ("chunk", C.c_int32), ("dtype", C.c_int32), ("sm_scale", C.c_float),
+                ("mask", C.c_int32), ("reserved", C.c_int32),
                 ("h_q_off", C.c_void_p), ("d_q_off", C.c_void_p), ("h_kv_off", C.c_void_p), ("d_kv_off", C.c_void_p),
                 ("h_anchor", C.c_void_p), ("d_anchor", C.c_void_p),
                 ("q_stride_tok", C.c_int64), ("q_stride_head", C.c_int64),
                 ("kv_stride_tok", C.c_int64), ("kv_stride_head", C.c_int64)]
+
+
+class skv_own_block(C.Structure):
+    _fields_ = [("k", C.c_void_p), ("v", C.c_void_p), ("dk", C.c_void_p), ("dv", C.c_void_p),
+                ("stride_tok", C.c_int64), ("stride_head", C.c_int64)]
 
 
 class skv_item(C.Structure):
@@ -85,7 +92,9 @@ def _load():
         "sparse_attn_partial_fwd": (C.c_int, [P(skv_problem), P(skv_plan), VP, VP, VP, VP, VP, VP, VP]),
         "lse_merge": (C.c_int, [I32, I32, I64, I32, VP, VP, VP, VP, I64, I64, I32, VP, I64, VP]),
         "skv_bwd_workspace_bytes": (C.c_size_t, [P(skv_problem)]),
-        "sparse_attn_bwd": (C.c_int, [P(skv_problem), P(skv_plan), P(skv_plan)] + [VP] * 10 + [C.c_size_t, VP]),
+        "sparse_attn_bwd": (C.c_int, [P(skv_problem), P(skv_plan), P(skv_plan)] + [VP] * 10 +
+                            [C.c_size_t, P(skv_own_block), VP]),
+        "sparse_attn_own_fwd": (C.c_int, [P(skv_problem), VP, VP, VP, I64, I64, VP, VP, VP, VP]),
         "skv_timing_enable": (C.c_int, [I32]),
         "skv_timing_collect": (C.c_int, [P(skv_kernel_time), I32, P(I32)]),
     }
@@ -99,7 +108,8 @@ lib = _load()
 EXPORTED = ("skv_last_error", "skv_check_problem", "skv_partial_layout", "skv_item_table", "lpt_plan",
             "skv_static_plan", "skv_gather_items", "skv_drop_zero_cost", "skv_coarsen_fwd_items",
             "sparse_attn_partial_fwd", "lse_merge",
-            "skv_bwd_workspace_bytes", "sparse_attn_bwd", "skv_timing_enable", "skv_timing_collect")
+            "skv_bwd_workspace_bytes", "sparse_attn_bwd", "sparse_attn_own_fwd", "skv_timing_enable",
+            "skv_timing_collect")
 
 
 def last_error() -> str:
@@ -213,13 +223,13 @@ class Problem:
     """
 
     def __init__(self, q_off, kv_off, anchors, block: int, hq: int, hkv: int, d: int, chunk: int,
-                 dtype: int, sm_scale: float, q_strides=None, kv_strides=None, device=None):
+                 dtype: int, sm_scale: float, q_strides=None, kv_strides=None, device=None, mask: int = 0):
         self.h_q_off = np.ascontiguousarray(q_off, dtype=np.int64)
         self.h_kv_off = np.ascontiguousarray(kv_off, dtype=np.int64)
         self.h_anchor = np.ascontiguousarray(anchors, dtype=np.int32)
         self.n_seq = len(self.h_q_off) - 1
         self.block, self.hq, self.hkv, self.d, self.chunk = block, hq, hkv, d, chunk
-        self.dtype, self.sm_scale = dtype, sm_scale
+        self.dtype, self.sm_scale, self.mask = dtype, sm_scale, mask
         self.q_strides = q_strides or (hq * d, d)
         self.kv_strides = kv_strides or (hkv * d, d)
         self.device = device
@@ -229,7 +239,7 @@ class Problem:
             self.d_q_off = torch.from_numpy(self.h_q_off).to(device)
             self.d_kv_off = torch.from_numpy(self.h_kv_off).to(device)
             self.d_anchor = torch.from_numpy(self.h_anchor).to(device)
-        self.c = skv_problem(self.n_seq, block, hq, hkv, d, chunk, dtype, sm_scale,
+        self.c = skv_problem(self.n_seq, block, hq, hkv, d, chunk, dtype, sm_scale, mask, 0,
                              _ptr(self.h_q_off), _ptr(self.d_q_off), _ptr(self.h_kv_off), _ptr(self.d_kv_off),
                              _ptr(self.h_anchor), _ptr(self.d_anchor),
                              self.q_strides[0], self.q_strides[1], self.kv_strides[0], self.kv_strides[1])
@@ -318,9 +328,32 @@ def lse_merge(n_part: int, hq: int, mq: int, d: int, o_part, m_part, lse_part, o
                          _ptr(lse_out) + lse_offset * 4, lse_stride_tok, _stream(stream)))
 
 
-def sparse_attn_bwd(problem: Problem, plan_kv, plan_q, q, k, v, o, lse, dout, dq, dk, dv, workspace, stream=None):
-    """plan_kv: BWD plan (key ranges); plan_q: FWD plan (forward items, for dQ)."""
+def _own_strides(t):
+    return (t.stride(0), t.stride(1)) if hasattr(t, "stride") and callable(t.stride) else (
+        t.strides[0] // t.itemsize, t.strides[1] // t.itemsize)
+
+
+def sparse_attn_own_fwd(problem: Problem, q, k_own, v_own, o_part, m_part, lse_part, stream=None):
+    """Own-block partial of every row (own-block mask), after sparse_attn_partial_fwd."""
+    st, sh = _own_strides(k_own)
+    if _own_strides(v_own) != (st, sh):
+        raise ValueError("k_own and v_own need the same strides")
+    _check(lib.sparse_attn_own_fwd(C.byref(problem.c), _ptr(q), _ptr(k_own), _ptr(v_own), st, sh, _ptr(o_part),
+                                   _ptr(m_part), _ptr(lse_part), _stream(stream)))
+
+
+def sparse_attn_bwd(problem: Problem, plan_kv, plan_q, q, k, v, o, lse, dout, dq, dk, dv, workspace, stream=None,
+                    own=None):
+    """plan_kv: BWD plan (key ranges); plan_q: FWD plan (forward items, for dQ).
+    own = (k_own, v_own, dk_own, dv_own) under the own-block mask, else None."""
     nbytes = workspace.numel() * workspace.element_size()
+    ob = None
+    if own is not None:
+        ko, vo, dko, dvo = own
+        st, sh = _own_strides(ko)
+        if any(_own_strides(t) != (st, sh) for t in (vo, dko, dvo)):
+            raise ValueError("own-block tensors need the same strides")
+        ob = C.byref(skv_own_block(_ptr(ko), _ptr(vo), _ptr(dko), _ptr(dvo), st, sh))
     _check(lib.sparse_attn_bwd(C.byref(problem.c), C.byref(plan_kv.c), C.byref(plan_q.c), _ptr(q), _ptr(k), _ptr(v),
                                _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), nbytes,
-                               _stream(stream)))
+                               ob, _stream(stream)))

@@ -20,7 +20,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libsplitkv.so")
-SOURCES = ["host.cpp", "timing.cpp", "api.hip", "fwd_bf16.hip", "fwd_f32.hip", "merge.hip", "bwd_bf16.hip"]
+SOURCES = ["host.cpp", "timing.cpp", "api.hip", "fwd_bf16.hip", "fwd_f32.hip", "merge.hip", "bwd_bf16.hip", "own.hip"]
 ARCH = "gfx950"
 
 

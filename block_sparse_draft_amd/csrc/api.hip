@@ -54,12 +54,13 @@ extern "C" int sparse_attn_partial_fwd(const skv_problem* p, const skv_plan* pla
   a.o_part = o_part; a.m_part = m_part; a.lse_part = lse_part;
   a.block = p->block; a.group = p->hq / p->hkv; a.hq = p->hq; a.chunk = p->chunk;
   a.fd_block = FastDiv::make(a.block); a.fd_group = FastDiv::make(a.group); a.fd_gb = FastDiv::make(a.block * a.group);
+  a.end_shift = end_shift(p);
   a.sm_scale = p->sm_scale;
   a.scale_log2 = p->sm_scale * kLog2e_host;
   int64_t part_rows = 0;
   for (int s = 0; s < p->n_seq; ++s) {
     const SeqView v = seq_view(p, s);
-    part_rows += ceil_div(v.n, p->chunk) * p->hq * v.mq;
+    part_rows += n_partials(p, v.n) * p->hq * v.mq;
   }
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e = launch_claim_reset(plan->d_claim, plan->n_workers, st);
@@ -68,6 +69,48 @@ extern "C" int sparse_attn_partial_fwd(const skv_problem* p, const skv_plan* pla
   e = p->dtype == SKV_BF16 ? launch_fwd_bf16(a, plan->n_workers, st)
                                       : launch_fwd_f32(a, p->d, plan->n_workers, st);
   return hip_status(e, "sparse_attn_partial_fwd launch");
+}
+
+// Own-block limits: the own keys and values of a block, and the P / dS tile of
+// its rows against them, are staged in LDS.
+static int check_own_shape(const skv_problem* p) {
+  if (p->mask != SKV_MASK_OWN_BLOCK) return fail(SKV_EINVAL, "the problem does not use the own-block mask");
+  if (p->block > 64) return fail(SKV_ESHAPE, "own-block mask: block = %d > 64", p->block);
+  if ((int64_t)(p->hq / p->hkv) * p->block * p->block > 8192)
+    return fail(SKV_ESHAPE, "own-block mask: (hq/hkv) * block^2 = %lld > 8192",
+                (long long)(p->hq / p->hkv) * p->block * p->block);
+  return SKV_OK;
+}
+
+static int check_own_strides(const skv_problem* p, int64_t st, int64_t sh) {
+  const int64_t vec = p->dtype == SKV_BF16 ? 8 : 4;
+  if (sh < p->d || st < (int64_t)p->hkv * sh || st % vec || sh % vec)
+    return fail(SKV_ESHAPE, "own-block strides (%lld, %lld) must be 16-byte multiples with tok >= hkv*head >= hkv*d",
+                (long long)st, (long long)sh);
+  return SKV_OK;
+}
+
+extern "C" int sparse_attn_own_fwd(const skv_problem* p, const void* q, const void* k_own, const void* v_own,
+                                   int64_t own_stride_tok, int64_t own_stride_head, float* o_part, float* m_part,
+                                   float* lse_part, void* stream) {
+  int rc = skv_check_problem(p);
+  if (rc) return rc;
+  if ((rc = check_device_problem(p))) return rc;
+  if ((rc = check_own_shape(p))) return rc;
+  if ((rc = check_own_strides(p, own_stride_tok, own_stride_head))) return rc;
+  if (!q || !k_own || !v_own || !o_part || !m_part || !lse_part) return fail(SKV_EINVAL, "tensor pointer is NULL");
+  if (!aligned16(q) || !aligned16(k_own) || !aligned16(v_own) || !aligned16(o_part))
+    return fail(SKV_ESHAPE, "q, k_own, v_own and o_part must be 16-byte aligned");
+  OwnFwdArgs a{};
+  a.q = q; a.k_own = k_own; a.v_own = v_own;
+  a.q_st = p->q_stride_tok; a.q_sh = p->q_stride_head; a.own_st = own_stride_tok; a.own_sh = own_stride_head;
+  a.q_off = p->d_q_off; a.kv_off = p->d_kv_off;
+  a.o_part = o_part; a.m_part = m_part; a.lse_part = lse_part;
+  a.n_seq = p->n_seq; a.block = p->block; a.group = p->hq / p->hkv; a.hq = p->hq; a.hkv = p->hkv;
+  a.chunk = p->chunk; a.sm_scale = p->sm_scale;
+  const int64_t n_blocks = p->h_q_off[p->n_seq] / p->block;
+  return hip_status(launch_own_fwd(a, p->dtype, p->d, n_blocks, static_cast<hipStream_t>(stream)),
+                    "sparse_attn_own_fwd launch");
 }
 
 extern "C" int lse_merge(int32_t n_part, int32_t hq, int64_t mq, int32_t d, const float* o_part, const float* m_part,
@@ -107,7 +150,7 @@ static BwdWorkspace bwd_workspace(const skv_problem* p) {
   int64_t rows = 0;
   for (int s = 0; s < p->n_seq; ++s) {
     const SeqView v = seq_view(p, s);
-    rows += ceil_div(v.n, p->chunk) * p->hq * v.mq;
+    rows += n_partials(p, v.n) * p->hq * v.mq;
   }
   const size_t prow = (size_t)p->h_q_off[p->n_seq] * (size_t)p->hq;  // packed rows
   BwdWorkspace w;
@@ -129,7 +172,8 @@ extern "C" size_t skv_bwd_workspace_bytes(const skv_problem* p) {
 
 extern "C" int sparse_attn_bwd(const skv_problem* p, const skv_plan* plan_kv, const skv_plan* plan_q, const void* q,
                                const void* k, const void* v, const void* o, const float* lse, const void* dout,
-                               void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, void* stream) {
+                               void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                               const skv_own_block* own, void* stream) {
   int rc = skv_check_problem(p);
   if (rc) return rc;
   if (p->dtype != SKV_BF16) return fail(SKV_EDTYPE, "sparse_attn_bwd supports bf16 only");
@@ -142,6 +186,16 @@ extern "C" int sparse_attn_bwd(const skv_problem* p, const skv_plan* plan_kv, co
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return fail(SKV_EINVAL, "tensor pointer is NULL");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) || !aligned16(dq))
     return fail(SKV_ESHAPE, "q, k, v, o, dout and dq must be 16-byte aligned");
+  if (p->mask == SKV_MASK_OWN_BLOCK) {
+    if ((rc = check_own_shape(p))) return rc;
+    if (!own || !own->k || !own->v || !own->dk || !own->dv)
+      return fail(SKV_EINVAL, "the own-block mask needs own-block keys, values and gradient outputs");
+    if ((rc = check_own_strides(p, own->stride_tok, own->stride_head))) return rc;
+    if (!aligned16(own->k) || !aligned16(own->v) || !aligned16(own->dk) || !aligned16(own->dv))
+      return fail(SKV_ESHAPE, "own-block tensors must be 16-byte aligned");
+  } else if (own) {
+    return fail(SKV_EINVAL, "own-block tensors given for the prefix mask");
+  }
   const BwdWorkspace ws = bwd_workspace(p);
   if (!workspace || workspace_bytes < ws.total)
     return fail(SKV_EWORKSPACE, "workspace of %zu bytes needed, %zu given", ws.total, workspace_bytes);
@@ -166,6 +220,12 @@ extern "C" int sparse_attn_bwd(const skv_problem* p, const skv_plan* plan_kv, co
   a.total_q = p->h_q_off[p->n_seq];
   a.n_seq = p->n_seq; a.block = p->block; a.group = p->hq / p->hkv; a.hq = p->hq; a.hkv = p->hkv;
   a.chunk = p->chunk;
+  a.end_shift = end_shift(p);
+  a.own = p->mask == SKV_MASK_OWN_BLOCK;
+  if (own) {
+    a.k_own = own->k; a.v_own = own->v; a.dk_own = own->dk; a.dv_own = own->dv;
+    a.own_st = own->stride_tok; a.own_sh = own->stride_head;
+  }
   a.fd_block = FastDiv::make(a.block); a.fd_group = FastDiv::make(a.group); a.fd_gb = FastDiv::make(a.block * a.group);
   a.sm_scale = p->sm_scale; a.scale_log2 = p->sm_scale * kLog2e_host;
   hipStream_t st = static_cast<hipStream_t>(stream);

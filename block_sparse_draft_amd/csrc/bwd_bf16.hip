@@ -83,18 +83,19 @@ __global__ __launch_bounds__(256) void bwd_pack_kernel(BwdArgs a) {
     const int n_ctx = (int)(a.kv_off[lo + 1] - a.kv_off[lo]);
     a.deltap[P] = sum;
     a.lsep[P] = a.lse[idx] * kLog2e;
-    a.endp[P] = min(a.anchor[q0 / a.block + b] + a.block, n_ctx);
+    a.endp[P] = min(a.anchor[q0 / a.block + b] + a.end_shift, n_ctx);
   }
 }
 
-// First partial row of every sequence: part_base[s] = sum_{s' < s} C_s' * hq * Mq_s'.
+// First partial row of every sequence: part_base[s] = sum_{s' < s} P_s' * hq * Mq_s',
+// P_s = C_s partials, plus the own-block partial under the own-block mask.
 __global__ void part_base_kernel(BwdArgs a) {
   if (threadIdx.x != 0 || blockIdx.x != 0) return;
   int64_t base = 0;
   for (int s = 0; s < a.n_seq; ++s) {
     a.part_base[s] = base;
     const int64_t n = a.kv_off[s + 1] - a.kv_off[s];
-    base += (n + a.chunk - 1) / a.chunk * a.hq * (a.q_off[s + 1] - a.q_off[s]);
+    base += ((n + a.chunk - 1) / a.chunk + a.own) * a.hq * (a.q_off[s + 1] - a.q_off[s]);
   }
   a.part_base[a.n_seq] = base;
 }
@@ -168,7 +169,7 @@ void bwd_kv_kernel(BwdArgs a) {
       for (int b0 = 0; b0 < n_blk; b0 += 64) {
         const int b = b0 + lane;
         bool blind = false;
-        if (b < n_blk) blind = min(a.anchor[blk0 + b] + a.block, n_ctx) <= kb;
+        if (b < n_blk) blind = min(a.anchor[blk0 + b] + a.end_shift, n_ctx) <= kb;
         b_first += __popcll(__ballot(blind));
       }
       const int nq = (n_blk - b_first) * GB;
@@ -578,12 +579,16 @@ __global__ __launch_bounds__(256) void bwd_finalize_kernel(BwdArgs a) {
   const int64_t q0 = a.q_off[s], mq = a.q_off[s + 1] - q0;
   const int64_t r = t - q0;
   const int n_ctx = (int)(a.kv_off[s + 1] - a.kv_off[s]);
-  const int e = min(a.anchor[(q0 + r) / a.block] + a.block, n_ctx);
+  const int e = min(a.anchor[(q0 + r) / a.block] + a.end_shift, n_ctx);
   const int nc = (e + a.chunk - 1) / a.chunk;  // chunks the row sees
   const float* src = a.dq_part + (a.part_base[s] + (int64_t)h * mq + r) * D + ln * 4;
   const int64_t cstride = (int64_t)a.hq * mq * D;
   f32x4 sum = {0.f, 0.f, 0.f, 0.f};
   for (int cc = 0; cc < nc; ++cc) sum += *reinterpret_cast<const f32x4*>(src + cc * cstride);
+  if (a.own) {  // the own-block partial follows the sequence's chunks
+    const int n_chunk = (n_ctx + a.chunk - 1) / a.chunk;
+    sum += *reinterpret_cast<const f32x4*>(src + n_chunk * cstride);
+  }
   uint2 pk;
   pk.x = (uint32_t)f32_to_bf16_bits(a.sm_scale * sum[0]) | ((uint32_t)f32_to_bf16_bits(a.sm_scale * sum[1]) << 16);
   pk.y = (uint32_t)f32_to_bf16_bits(a.sm_scale * sum[2]) | ((uint32_t)f32_to_bf16_bits(a.sm_scale * sum[3]) << 16);
@@ -615,6 +620,7 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, int kv_workers, int q_workers, hipS
     hipLaunchKernelGGL(bwd_dq_kernel, dim3(q_workers), dim3(256), 0, stream, a);
     if ((e = hipGetLastError()) != hipSuccess || rows == 0) return e;
   }
+  if (a.own && (e = launch_own_bwd(a, a.total_q / a.block, stream)) != hipSuccess) return e;
   TimedLaunch t(kBwdFinalize, stream);
   hipLaunchKernelGGL(bwd_finalize_kernel, dim3((unsigned)((rows + 7) / 8)), dim3(256), 0, stream, a);
   return hipGetLastError();

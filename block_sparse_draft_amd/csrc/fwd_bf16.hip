@@ -163,7 +163,7 @@ void fwd_bf16_kernel(FwdArgs a) {
     for (int rt = 0; rt < nrows; rt += ROWS) {
       // Anchors are sorted, so the last row of the pass has the largest prefix end.
       const int p_last = min(nrows, rt + ROWS) - 1;
-      const int wg_hi = max(klo, min(khi, min(a.anchor[blk0 + it.lo + a.fd_gb.div(p_last)] + a.block, n_ctx)));
+      const int wg_hi = max(klo, min(khi, min(a.anchor[blk0 + it.lo + a.fd_gb.div(p_last)] + a.end_shift, n_ctx)));
       const int ntiles = (wg_hi - klo + KT - 1) / KT;
 
       // ---- start the K/V pipeline around the loads of this lane's Q row ----
@@ -179,7 +179,7 @@ void fwd_bf16_kernel(FwdArgs a) {
       const int hl = a.fd_group.mod(a.fd_block.div(pc));
       const int64_t r = (int64_t)b * a.block + a.fd_block.mod(pc);
       const int h = it.kv_head * a.group + hl;
-      const int e = min(a.anchor[blk0 + b] + a.block, n_ctx);
+      const int e = min(a.anchor[blk0 + b] + a.end_shift, n_ctx);
       const int vend = valid ? max(klo, min(khi, e)) : klo;  // visible keys of the row: [klo, vend)
       const int64_t prow = it.part_base + (int64_t)h * mq + r;
       bf16x8 qf[8];

@@ -36,7 +36,7 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdArgs a) {
       const int b = it.lo + p / GB;
       const int hl = (p / a.block) % a.group;
       const int i = p % a.block;
-      const int e = min(a.anchor[blk0 + b] + a.block, n_ctx);
+      const int e = min(a.anchor[blk0 + b] + a.end_shift, n_ctx);
       const int vend = min(khi, e);
       const int h = it.kv_head * a.group + hl;
       const int64_t r = (int64_t)b * a.block + i;

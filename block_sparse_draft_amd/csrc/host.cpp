@@ -49,6 +49,7 @@ extern "C" int skv_check_problem(const skv_problem* p) {
   if (p->hq % p->hkv) return fail(SKV_ESHAPE, "hq = %d is not a multiple of hkv = %d", p->hq, p->hkv);
   if ((int64_t)p->block * (p->hq / p->hkv) > (1 << 20)) return fail(SKV_ESHAPE, "block * hq/hkv exceeds 2^20");
   if (p->dtype != SKV_F32 && p->dtype != SKV_BF16) return fail(SKV_EDTYPE, "unknown dtype %d", p->dtype);
+  if (p->mask != SKV_MASK_PREFIX && p->mask != SKV_MASK_OWN_BLOCK) return fail(SKV_EINVAL, "unknown mask %d", p->mask);
   if (p->dtype == SKV_BF16 && p->d != 128) return fail(SKV_ESHAPE, "bf16 supports head_dim 128, got %d", p->d);
   if (p->dtype == SKV_F32 && p->d != 64 && p->d != 128)
     return fail(SKV_ESHAPE, "f32 supports head_dim 64 or 128, got %d", p->d);
@@ -91,7 +92,7 @@ extern "C" int skv_partial_layout(const skv_problem* p, int64_t* part_base, int3
   int64_t base = 0;
   for (int s = 0; s < p->n_seq; ++s) {
     const SeqView v = seq_view(p, s);
-    const int64_t c = ceil_div(v.n, p->chunk);
+    const int64_t c = n_partials(p, v.n);
     if (part_base) part_base[s] = base;
     if (n_chunk) n_chunk[s] = (int32_t)c;
     base += c * p->hq * v.mq;
@@ -122,7 +123,8 @@ extern "C" int skv_item_table(const skv_problem* p, int32_t kind, int32_t granul
     const SeqView v = seq_view(p, s);
     const int64_t C = ceil_div(v.n, p->chunk);
     ends.resize(v.n_blk);
-    for (int64_t b = 0; b < v.n_blk; ++b) ends[b] = std::min<int64_t>((int64_t)p->h_anchor[v.blk0 + b] + p->block, v.n);
+    for (int64_t b = 0; b < v.n_blk; ++b)
+      ends[b] = std::min<int64_t>((int64_t)p->h_anchor[v.blk0 + b] + end_shift(p), v.n);
     for (int g = 0; g < p->hkv; ++g) {
       for (int64_t c = 0; c < C; ++c) {
         const int64_t lo = c * p->chunk, hi = std::min<int64_t>(lo + p->chunk, v.n);
@@ -159,7 +161,7 @@ extern "C" int skv_item_table(const skv_problem* p, int32_t kind, int32_t granul
         tok += hi - lo;
       }
     }
-    base += C * p->hq * v.mq;
+    base += n_partials(p, v.n) * p->hq * v.mq;  // chunks, then the own-block partial if any
   }
   if (n_items) *n_items = n;
   if (total_tok) *total_tok = tok;

@@ -15,6 +15,14 @@ constexpr float kLog2e_host = 1.4426950408889634f;
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Partials of a sequence with n context keys: its chunks, plus the own-block
+// partial under SKV_MASK_OWN_BLOCK.
+inline int64_t n_partials(const skv_problem* p, int64_t n) {
+  return ceil_div(n, p->chunk) + (p->mask == SKV_MASK_OWN_BLOCK ? 1 : 0);
+}
+// e_b = min(a_b + shift, N): shift is block under the prefix mask, 0 under the own-block mask.
+inline int32_t end_shift(const skv_problem* p) { return p->mask == SKV_MASK_OWN_BLOCK ? 0 : p->block; }
+
 // Per-sequence view of a validated problem (host copies).
 struct SeqView {
   int64_t q0, mq, k0, n, blk0, n_blk;

@@ -26,9 +26,25 @@ struct FwdArgs {
   float* m_part;
   float* lse_part;
   int32_t block, group, hq, chunk;
+  int32_t end_shift;  // e_b = min(a_b + end_shift, N): block (prefix mask) or 0 (own-block mask)
   FastDiv fd_block, fd_group, fd_gb;  // division by block, hq/hkv and their product
   float sm_scale;
   float scale_log2;  // sm_scale * log2(e)
+};
+
+// Own-block partial (own-block mask): one workgroup per (draft block, KV head).
+struct OwnFwdArgs {
+  const void* q;
+  const void* k_own;
+  const void* v_own;
+  int64_t q_st, q_sh, own_st, own_sh;  // element strides
+  const int64_t* q_off;
+  const int64_t* kv_off;
+  float* o_part;
+  float* m_part;
+  float* lse_part;
+  int32_t n_seq, block, group, hq, hkv, chunk;
+  float sm_scale;
 };
 
 struct MergeArgs {
@@ -75,6 +91,13 @@ struct BwdArgs {
   int32_t kv_steal, q_steal;
   int64_t total_q;  // sum Mq
   int32_t n_seq, block, group, hq, hkv, chunk;
+  int32_t end_shift;  // e_b = min(a_b + end_shift, N): block (prefix mask) or 0 (own-block mask)
+  int32_t own;        // own-block mask: one more dQ partial per sequence (index C_s)
+  const void* k_own;  // own-block keys / values and their gradients, [sum Mq][hkv][d]
+  const void* v_own;
+  void* dk_own;
+  void* dv_own;
+  int64_t own_st, own_sh;
   FastDiv fd_block, fd_group, fd_gb;  // division by block, hq/hkv and their product
   float sm_scale, scale_log2;
 };
@@ -85,5 +108,7 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, int n_workers, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdArgs& a, int d, int n_workers, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, int d, hipStream_t stream);
 hipError_t launch_bwd_bf16(const BwdArgs& a, int kv_workers, int q_workers, hipStream_t stream);
+hipError_t launch_own_fwd(const OwnFwdArgs& a, int dtype, int d, int64_t n_blocks, hipStream_t stream);
+hipError_t launch_own_bwd(const BwdArgs& a, int64_t n_blocks, hipStream_t stream);
 
 }  // namespace skv

@@ -5,7 +5,8 @@
 namespace skv {
 
 enum KernelId {
-  kClaimReset, kFillPartials, kFwdBf16, kFwdF32, kMerge, kBwdPartBase, kBwdPack, kBwdKv, kBwdDq, kBwdFinalize, kNumKernels
+  kClaimReset, kFillPartials, kFwdBf16, kFwdF32, kMerge, kBwdPartBase, kBwdPack, kBwdKv, kBwdDq, kBwdFinalize,
+  kOwnFwd, kOwnBwd, kNumKernels
 };
 
 // Brackets the launches made during its lifetime with two events on `stream`

@@ -112,13 +112,20 @@ class SplitKVAttention:
                  sm_scale: float, dtype, device, n_workers: Optional[int] = None,
                  fwd_granule: Optional[int] = None, bwd_granule: int = 256, policy: str = "lpt",
                  with_bwd: bool = True, steal: bool = True, ticks: bool = False,
-                 fwd_runs_per_worker: Optional[float] = 4.0):
+                 fwd_runs_per_worker: Optional[float] = 4.0, mask: str = "prefix"):
         import torch
         self.device = torch.device(device)
         self.dtype = dtype
         self.skv_dtype = B.SKV_BF16 if dtype == torch.bfloat16 else B.SKV_F32
+        if mask not in ("prefix", "own_block"):
+            raise ValueError(mask)
+        # "own_block": each draft block also sees its own tokens' keys (k_own,
+        # v_own [sum Mq, hkv, d]), one more partial per row; the context prefix
+        # then ends at the anchor
+        self.mask = mask
         self.problem = B.Problem(q_off, kv_off, anchors, block, hq, hkv, d, chunk, self.skv_dtype, sm_scale,
-                                 device=self.device)
+                                 device=self.device,
+                                 mask=B.SKV_MASK_OWN_BLOCK if mask == "own_block" else B.SKV_MASK_PREFIX)
         self.problem.check()
         self.n_workers = n_workers or default_workers(self.device)
         G = hq // hkv
@@ -160,9 +167,13 @@ class SplitKVAttention:
             self.dq_plan.replan()
             self.plan_s += self.bwd_plan.plan_s + self.dq_plan.plan_s
 
-    def partial_fwd(self, q, k, v, stream=None):
+    def partial_fwd(self, q, k, v, stream=None, k_own=None, v_own=None):
         B.sparse_attn_partial_fwd(self.problem, self.fwd_plan, q, k, v, self.o_part, self.m_part, self.lse_part,
                                   stream)
+        if self.mask == "own_block":
+            if k_own is None or v_own is None:
+                raise ValueError("the own-block mask needs k_own and v_own")
+            B.sparse_attn_own_fwd(self.problem, q, k_own, v_own, self.o_part, self.m_part, self.lse_part, stream)
 
     def merge(self, stream=None):
         p = self.problem
@@ -174,16 +185,19 @@ class SplitKVAttention:
                         p.hq * p.d, p.d, out_dtype, self.lse, p.hq, stream,
                         part_offset=int(self.part_base[s]), out_offset=q0, lse_offset=q0 * p.hq)
 
-    def forward(self, q, k, v, stream=None):
-        """Partials of every KV chunk, then their exact merge.  Returns (O, LSE)."""
-        self.partial_fwd(q, k, v, stream)
+    def forward(self, q, k, v, stream=None, k_own=None, v_own=None):
+        """Partials of every KV chunk (and of the own block), then their exact merge.  Returns (O, LSE)."""
+        self.partial_fwd(q, k, v, stream, k_own, v_own)
         self.merge(stream)
         return self.o, self.lse
 
-    def backward(self, q, k, v, dout, dq, dk, dv, stream=None):
-        """dQ, dK, dV from the merged O and LSE of the last forward."""
+    def backward(self, q, k, v, dout, dq, dk, dv, stream=None, own=None):
+        """dQ, dK, dV from the merged O and LSE of the last forward.  Under the
+        own-block mask ``own`` = (k_own, v_own, dk_own, dv_own)."""
+        if (self.mask == "own_block") != (own is not None):
+            raise ValueError("own-block tensors go with the own-block mask")
         B.sparse_attn_bwd(self.problem, self.bwd_plan, self.dq_plan, q, k, v, self.o, self.lse, dout, dq, dk, dv,
-                          self.workspace, stream)
+                          self.workspace, stream, own=own)
         return dq, dk, dv
 
     # -- views ---------------------------------------------------------------
@@ -198,12 +212,17 @@ class SplitKVAttention:
                 self.lse_part[b:b + n].view(c, p.hq, mq))
 
 
-def unmasked_pairs(q_off, kv_off, anchors, block: int, hq: int) -> int:
-    """Token-exact number of visible (query head, query row, key) triples."""
+def unmasked_pairs(q_off, kv_off, anchors, block: int, hq: int, mask: str = "prefix") -> int:
+    """Token-exact number of visible (query head, query row, key) triples
+    (under the own-block mask: the context prefix [0, min(a_b, N)) plus the
+    block's own keys)."""
     total = 0
+    shift = block if mask == "prefix" else 0
     for s in range(len(q_off) - 1):
         n = int(kv_off[s + 1] - kv_off[s])
         b0, b1 = int(q_off[s]) // block, int(q_off[s + 1]) // block
-        e = np.minimum(np.asarray(anchors[b0:b1], dtype=np.int64) + block, n)
+        e = np.minimum(np.asarray(anchors[b0:b1], dtype=np.int64) + shift, n)
+        if mask != "prefix":
+            e = e + block
         total += int(e.sum()) * block
     return total * hq

@@ -12,9 +12,17 @@
  * log-sum-exp.  Work items are placed on persistent workgroups by a
  * cost-aware longest-processing-time-first (LPT) planner ("LPT Scheduling").
  *
- * Mask reading: draft block b of a sequence is anchored at context position
- * a_b and its `block` query rows see the context prefix [0, e_b) with
- * e_b = min(a_b + block, N_s).  Anchors are sorted ascending per sequence.
+ * Mask reading (skv_problem.mask): draft block b of a sequence is anchored
+ * at context position a_b.
+ *  - SKV_MASK_PREFIX (default): its `block` query rows see the context
+ *    prefix [0, e_b) with e_b = min(a_b + block, N_s) (the block's own tokens
+ *    are context positions a_b .. a_b + block - 1).
+ *  - SKV_MASK_OWN_BLOCK: its rows see the context prefix [0, e_b) with
+ *    e_b = min(a_b, N_s), plus all `block` keys of the block's own draft
+ *    tokens, a query-sized K/V segment passed separately (k_own, v_own:
+ *    [sum_s Mq_s, hkv, d], row t = draft token t).  Its contribution is one
+ *    more partial per sequence (sparse_attn_own_fwd), merged like the rest.
+ * Anchors are sorted ascending per sequence.
  *
  * Conventions shared by every call:
  *  - All device pointers are caller-owned; the library never allocates,
@@ -67,6 +75,8 @@ enum { SKV_TILE = 64 }; /* key-tile granularity of mask skipping and of the cost
  * draft blocks) and context tokens [kv_off[s], kv_off[s+1]).  Its draft block
  * b (0-based within s) is anchor[q_off[s]/block + b].  Every pointer pair holds
  * the same values in host memory (h_*) and device memory (d_*). */
+typedef enum { SKV_MASK_PREFIX = 0, SKV_MASK_OWN_BLOCK = 1 } skv_mask;
+
 typedef struct skv_problem {
   int32_t n_seq;
   int32_t block;          /* B: draft tokens per anchor, >= 1 */
@@ -76,6 +86,8 @@ typedef struct skv_problem {
   int32_t chunk;          /* L: KV chunk length, positive multiple of SKV_TILE */
   int32_t dtype;          /* skv_dtype of Q, K, V, O, dO, dQ, dK, dV */
   float sm_scale;         /* logit scale, finite and > 0 (usually 1/sqrt(d)) */
+  int32_t mask;           /* skv_mask: SKV_MASK_PREFIX (0) or SKV_MASK_OWN_BLOCK */
+  int32_t reserved;       /* 0 */
   const int64_t *h_q_off, *d_q_off;    /* [n_seq+1], multiples of block, non-decreasing */
   const int64_t *h_kv_off, *d_kv_off;  /* [n_seq+1], non-decreasing */
   const int32_t *h_anchor, *d_anchor;  /* [q_off[n_seq]/block], >= 0, sorted per sequence */
@@ -135,10 +147,11 @@ const char* skv_last_error(void);
 int skv_check_problem(const skv_problem* p);
 
 /* Partial layout of sparse_attn_partial_fwd.  Sequence s has
- * n_chunk[s] = ceil(N_s / chunk) partials; partial (s, c) owns rows
- * part_base[s] + c*hq*Mq_s + h*Mq_s + r  (h = query head, r = query row in s).
- * part_base has n_seq+1 entries; part_base[n_seq] is the total number of
- * partial rows.  Either output may be NULL. */
+ * n_chunk[s] = C_s = ceil(N_s / chunk) context partials, plus one (index C_s,
+ * written by sparse_attn_own_fwd) under SKV_MASK_OWN_BLOCK; partial (s, c)
+ * owns rows part_base[s] + c*hq*Mq_s + h*Mq_s + r  (h = query head, r = query
+ * row in s).  part_base has n_seq+1 entries; part_base[n_seq] is the total
+ * number of partial rows.  Either output may be NULL. */
 int skv_partial_layout(const skv_problem* p, int64_t* part_base, int32_t* n_chunk);
 
 /* Work items of a problem, in enumeration order (seq, kv_head, chunk, range),
@@ -234,14 +247,29 @@ int sparse_attn_partial_fwd(const skv_problem* p, const skv_plan* plan, const vo
  * lse_c = -inf gets O = 0 and LSE = -inf.  O is written in out_dtype at
  * o_out + r*o_stride_tok + h*o_stride_head (+ x); LSE at lse_out[r*lse_stride_tok + h].
  * n_part may be 0.  Bitwise deterministic. */
+/* The own-block partial of every draft row (SKV_MASK_OWN_BLOCK only): for
+ * row r of block b, query head h and the block's own keys J (its `block`
+ * draft tokens, KV head h / (hq/hkv)), the same m_part / o_part / lse_part
+ * formulas as above, written at partial index C_s of the sequence
+ * (skv_partial_layout).  k_own, v_own: [sum Mq, hkv, d] in the problem dtype,
+ * element (t, g, x) at t*own_stride_tok + g*own_stride_head + x (strides
+ * 16-byte multiples).  Call after sparse_attn_partial_fwd on the same stream
+ * (that call first sets every partial row to -inf).  Own-block limits:
+ * block <= 64 and (hq/hkv) * block * block <= 8192 (SKV_ESHAPE otherwise).
+ * Bitwise deterministic. */
+int sparse_attn_own_fwd(const skv_problem* p, const void* q, const void* k_own, const void* v_own,
+                        int64_t own_stride_tok, int64_t own_stride_head, float* o_part, float* m_part,
+                        float* lse_part, void* stream);
+
 int lse_merge(int32_t n_part, int32_t hq, int64_t mq, int32_t d, const float* o_part, const float* m_part,
               const float* lse_part, void* o_out, int64_t o_stride_tok, int64_t o_stride_head, int32_t out_dtype,
               float* lse_out, int64_t lse_stride_tok, void* stream);
 
 /* Bytes of device workspace sparse_attn_bwd needs (256-byte aligned pieces):
- * fp32 dQ partials in the layout of skv_partial_layout ([rows][d]), fp32
- * Delta [sum Mq][hq], and n_seq+1 int64 partial offsets.  0 for an invalid
- * problem. */
+ * fp32 dQ partials in the layout of skv_partial_layout ([rows][d]); bf16
+ * copies of Q and dO and fp32 LSE, Delta and int32 prefix ends in the
+ * backward's packed row order; n_seq+1 int64 partial offsets.  0 for an
+ * invalid problem. */
 size_t skv_bwd_workspace_bytes(const skv_problem* p);
 
 /* Backward of O with respect to Q, K, V, reusing the merged LSE.
@@ -255,10 +283,25 @@ size_t skv_bwd_workspace_bytes(const skv_problem* p);
  * plan_q is a FWD plan over the forward's items (each writes the dQ partial of
  * its chunk, summed per row afterwards).  The two plans need distinct claim
  * arrays.  No atomics: the result is bitwise reproducible.
- * Only SKV_BF16 with d = 128 is supported. */
+ * Only SKV_BF16 with d = 128 is supported.
+ * Under SKV_MASK_OWN_BLOCK `own` is required: its keys and values enter P and
+ * dS like the context keys each row sees, their gradients
+ * dk_own = sm_scale * sum dS q and dv_own = sum P dO (summed over the block's
+ * rows and the query heads of each KV head) are written to own->dk, own->dv
+ * (k_own layout, fully written), and their share of dQ joins the sum.  NULL
+ * otherwise. */
+typedef struct skv_own_block {
+  const void* k;              /* [sum Mq, hkv, d] own-block keys (problem dtype) */
+  const void* v;              /* own-block values, same layout */
+  void* dk;                   /* outputs, same layout */
+  void* dv;
+  int64_t stride_tok, stride_head;  /* elements, 16-byte multiples, stride_head >= d */
+} skv_own_block;
+
 int sparse_attn_bwd(const skv_problem* p, const skv_plan* plan_kv, const skv_plan* plan_q, const void* q,
                     const void* k, const void* v, const void* o, const float* lse, const void* dout, void* dq,
-                    void* dk, void* dv, void* workspace, size_t workspace_bytes, void* stream);
+                    void* dk, void* dv, void* workspace, size_t workspace_bytes, const skv_own_block* own,
+                    void* stream);
 
 /* ---- Instrumentation (host) ----
  * Per-kernel timing with HIP events, off by default.  While enabled, every
@@ -270,7 +313,7 @@ int sparse_attn_bwd(const skv_problem* p, const skv_plan* plan_kv, const skv_pla
  * out[0 .. min(max_entries, *n_entries)) and resets the tallies; *n_entries
  * receives the number of kernels with at least one launch.  Kernel names:
  * "claim_reset", "fill_partials", "partial_fwd_bf16", "partial_fwd_f32", "lse_merge",
- * "bwd_part_base", "bwd_pack", "bwd_kv", "bwd_dq", "bwd_finalize". */
+ * "bwd_part_base", "bwd_pack", "bwd_kv", "bwd_dq", "bwd_finalize", "own_fwd", "own_bwd". */
 typedef struct skv_kernel_time {
   const char* name;   /* static string */
   int64_t launches;

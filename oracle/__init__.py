@@ -23,6 +23,9 @@ from .attention import (  # noqa: F401
     block_ends, visible_mask, attention, chunk_partials, lse_merge, attention_bwd,
     attention_workload, partials_workload, bwd_workload,
 )
+from .own_block import (  # noqa: F401
+    context_ends, attention_own, own_partial, attention_own_bwd, attention_own_workload, bwd_own_workload,
+)
 from .plan import (  # noqa: F401
     item_table, lpt, static_assign, csr_from_assign, loads_from_assign, imbalance,
     brute_force_makespan, graham_bound, coarsen_runs,

@@ -27,7 +27,7 @@ from typing import Optional, Sequence
 
 import numpy as np
 
-STREAM_LEN, STREAM_ANCHOR, STREAM_Q, STREAM_K, STREAM_V, STREAM_DO = range(6)
+STREAM_LEN, STREAM_ANCHOR, STREAM_Q, STREAM_K, STREAM_V, STREAM_DO, STREAM_K_OWN, STREAM_V_OWN = range(8)
 _SLAB = 1 << 24  # values drawn per call, keeps peak host memory bounded
 
 
@@ -78,6 +78,10 @@ class Workload:
     do: Optional[np.ndarray]
     sm_scale: float
     seed: int
+    # own-block keys and values, [sum Mq, Hkv, D] (row t holds draft token t's
+    # key): present only for the own-block mask variant, see add_own_block
+    k_own: Optional[np.ndarray] = None
+    v_own: Optional[np.ndarray] = None
 
     @property
     def is_bf16(self) -> bool:
@@ -192,3 +196,32 @@ def _assemble(cfg: Config, n_ctx: np.ndarray, anchors: np.ndarray, seed: int, wi
     v = _normal(_rng(seed, cfg.cid, STREAM_V), (tk, cfg.hkv, cfg.d), cfg.dtype)
     do = _normal(_rng(seed, cfg.cid, STREAM_DO), (tq, cfg.hq, cfg.d), cfg.dtype) if with_do else None
     return Workload(cfg, n_ctx, anchors, q_off, kv_off, q, k, v, do, 1.0 / math.sqrt(cfg.d), seed)
+
+
+def add_own_block(w: Workload, from_context: bool = False) -> Workload:
+    """Attach own-block keys and values [sum Mq, Hkv, D] to a workload.
+
+    Default: seeded N(0, 1) draws (own streams, bf16-rounded for bf16).  With
+    ``from_context`` the rows of draft block b are copies of the context rows
+    [a_b, a_b + B) of its sequence (every anchor must satisfy a_b + B <= N_s),
+    the case in which the own-block mask reproduces the prefix mask.
+    """
+    c = w.cfg
+    tq = int(w.q_off[-1])
+    if not from_context:
+        w.k_own = _normal(_rng(w.seed, c.cid, STREAM_K_OWN), (tq, c.hkv, c.d), c.dtype)
+        w.v_own = _normal(_rng(w.seed, c.cid, STREAM_V_OWN), (tq, c.hkv, c.d), c.dtype)
+        return w
+    k_own = np.empty((tq, c.hkv, c.d), dtype=w.k.dtype)
+    v_own = np.empty_like(k_own)
+    for s in range(c.n_seq):
+        k0, n = int(w.kv_off[s]), int(w.n_ctx[s])
+        for bi, a in enumerate(w.seq_anchors(s)):
+            a = int(a)
+            if a + c.block > n:
+                raise ValueError("anchor + block runs past the context")
+            t0 = int(w.q_off[s]) + bi * c.block
+            k_own[t0:t0 + c.block] = w.k[k0 + a:k0 + a + c.block]
+            v_own[t0:t0 + c.block] = w.v[k0 + a:k0 + a + c.block]
+    w.k_own, w.v_own = k_own, v_own
+    return w

@@ -182,7 +182,7 @@ def test_device_calls_reject_bad_arguments_before_touching_the_gpu():
                                        None)
     assert rc == B.SKV_ESHAPE
     # bwd: fp32 problems are rejected, workspace is checked
-    rc = B.lib.sparse_attn_bwd(C.byref(p.c), C.byref(bplan), C.byref(plan), *([fake] * 10), 1 << 30, None)
+    rc = B.lib.sparse_attn_bwd(C.byref(p.c), C.byref(bplan), C.byref(plan), *([fake] * 10), 1 << 30, None, None)
     assert rc == B.SKV_EDTYPE
     wb = make("c2", seed=0, n_ctx=256, n_anchor=2)
     pb = _problem_from(wb)
@@ -192,15 +192,15 @@ def test_device_calls_reject_bad_arguments_before_touching_the_gpu():
     # (1024 rows x 128 bf16 each); packed LSE, Delta, prefix end (1024 x 4 bytes each); 2 offsets
     assert need == 32 * 32 * 128 * 4 + 2 * 1024 * 128 * 2 + 3 * 1024 * 4 + 256
     qplan = B.skv_plan(B.SKV_ITEM_FWD, 4, 1, 16, 16, 32)
-    rc = B.lib.sparse_attn_bwd(C.byref(pb.c), C.byref(bplan), C.byref(qplan), *([fake] * 10), need - 1, None)
+    rc = B.lib.sparse_attn_bwd(C.byref(pb.c), C.byref(bplan), C.byref(qplan), *([fake] * 10), need - 1, None, None)
     assert rc == B.SKV_EWORKSPACE
-    rc = B.lib.sparse_attn_bwd(C.byref(pb.c), C.byref(bplan), C.byref(bplan), *([fake] * 10), need, None)
+    rc = B.lib.sparse_attn_bwd(C.byref(pb.c), C.byref(bplan), C.byref(bplan), *([fake] * 10), need, None, None)
     assert rc == B.SKV_EPLAN                       # second plan must be a forward plan
-    rc = B.lib.sparse_attn_bwd(C.byref(pb.c), C.byref(bplan), C.byref(plan), *([fake] * 10), need, None)
+    rc = B.lib.sparse_attn_bwd(C.byref(pb.c), C.byref(bplan), C.byref(plan), *([fake] * 10), need, None, None)
     assert rc == B.SKV_EPLAN                       # shared claim cursors are rejected
     tk = B.skv_plan(B.SKV_ITEM_BWD, 4, 1, 16, 16, 48, 0, 0, 64)
     tq = B.skv_plan(B.SKV_ITEM_FWD, 4, 1, 16, 16, 32, 0, 0, 64)
-    rc = B.lib.sparse_attn_bwd(C.byref(pb.c), C.byref(tk), C.byref(tq), *([fake] * 10), need, None)
+    rc = B.lib.sparse_attn_bwd(C.byref(pb.c), C.byref(tk), C.byref(tq), *([fake] * 10), need, None, None)
     assert rc == B.SKV_EPLAN and "ticks" in B.last_error()   # shared ticks arrays are rejected
     badflags = B.skv_plan(B.SKV_ITEM_FWD, 4, 1, 16, 16, 16, 2, 0, None)
     rc = B.lib.sparse_attn_partial_fwd(C.byref(p.c), C.byref(badflags), fake, fake, fake, fake, fake, fake, None)
@@ -289,3 +289,52 @@ def test_coarsen_fwd_items_rejects_bad_input():
     with pytest.raises(B.SkvError):
         B.skv_coarsen_fwd_items(items, bad, 10)
     assert B.skv_coarsen_fwd_items(items[:0], cost[:0], 5)[0].shape == (0,)
+
+
+def test_own_block_mask_host_side():
+    """Own-block mask: the context prefix ends at the anchor (the prefix mask's
+    cost with anchors moved back by B), one more partial per sequence, and the
+    own-block calls reject bad shapes and missing tensors before any launch."""
+    w = make("c2", seed=0, n_ctx=3000, n_anchor=8, hq=8, hkv=2, chunk=1024, with_do=False)
+    p = B.Problem(w.q_off, w.kv_off, w.anchors, w.cfg.block, w.cfg.hq, w.cfg.hkv, w.cfg.d, w.cfg.chunk, B.SKV_BF16,
+                  w.sm_scale, mask=B.SKV_MASK_OWN_BLOCK)
+    p.check()
+    items, cost, tok, total = p.item_table(B.SKV_ITEM_FWD, 1)
+    anchors = [w.seq_anchors(s).astype(np.int64) - w.cfg.block for s in range(w.cfg.n_seq)]
+    desc, ocost, _, _ = oracle.item_table(list(w.n_ctx), anchors, w.cfg.block, w.cfg.hq, w.cfg.hkv, w.cfg.chunk,
+                                          "fwd", 1)
+    assert np.array_equal(cost, ocost)
+    base, nchunk = p.partial_layout()
+    assert nchunk.tolist() == [3 + 1]
+    assert base[-1] == 4 * w.cfg.hq * int(w.q_off[-1])
+    assert np.array_equal(items["part_base"][items["chunk"] == 2], np.full((items["chunk"] == 2).sum(),
+                                                                           2 * w.cfg.hq * int(w.q_off[-1])))
+    fake = C.c_void_p(4096)
+    pd = _problem_from(w)
+    pd.c.d_q_off = pd.c.d_kv_off = pd.c.d_anchor = 4096
+    # prefix-mask problem: the own-block forward is refused
+    assert B.lib.sparse_attn_own_fwd(C.byref(pd.c), fake, fake, fake, 256, 128, fake, fake, fake, None) == B.SKV_EINVAL
+    pd.c.mask = B.SKV_MASK_OWN_BLOCK
+    assert B.lib.sparse_attn_own_fwd(C.byref(pd.c), fake, fake, fake, 100, 128, fake, fake, fake, None) == B.SKV_ESHAPE
+    assert B.lib.sparse_attn_own_fwd(C.byref(pd.c), fake, None, fake, 256, 128, fake, fake, fake, None) == B.SKV_EINVAL
+    pd.c.mask = 7
+    assert B.lib.skv_check_problem(C.byref(pd.c)) == B.SKV_EINVAL
+    pd.c.mask = B.SKV_MASK_OWN_BLOCK
+    pd.c.block, pd.c.hq = 64, 8     # (hq/hkv) * block^2 = 4 * 4096 > 8192
+    assert B.lib.sparse_attn_own_fwd(C.byref(pd.c), fake, fake, fake, 256, 128, fake, fake, fake, None) in (
+        B.SKV_ESHAPE, B.SKV_EINVAL)
+    # backward: the own-block mask needs its tensors
+    pb = _problem_from(w)
+    pb.c.d_q_off = pb.c.d_kv_off = pb.c.d_anchor = 4096
+    pb.c.mask = B.SKV_MASK_OWN_BLOCK
+    need = B.lib.skv_bwd_workspace_bytes(C.byref(pb.c))
+    bplan = B.skv_plan(B.SKV_ITEM_BWD, 4, 1, 16, 16, 48)
+    qplan = B.skv_plan(B.SKV_ITEM_FWD, 4, 1, 16, 16, 32)
+    rc = B.lib.sparse_attn_bwd(C.byref(pb.c), C.byref(bplan), C.byref(qplan), *([fake] * 10), need, None, None)
+    assert rc == B.SKV_EINVAL
+    own = B.skv_own_block(4096, 4096, 4096, 4096, 256, 128)
+    pb.c.mask = B.SKV_MASK_PREFIX
+    need2 = B.lib.skv_bwd_workspace_bytes(C.byref(pb.c))
+    assert need2 < need                                       # one partial fewer per sequence
+    rc = B.lib.sparse_attn_bwd(C.byref(pb.c), C.byref(bplan), C.byref(qplan), *([fake] * 10), need, C.byref(own), None)
+    assert rc == B.SKV_EINVAL                                 # own-block tensors with the prefix mask

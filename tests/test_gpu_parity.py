@@ -10,7 +10,7 @@ import torch
 import oracle
 from helpers import (BF16_ABS, BF16_FROB, BF16_LSE_REL, F32_ABS, assert_close, assert_lse, make_path, to_device,
                      to_np64)
-from synthetic import make, make_custom
+from synthetic import add_own_block, make, make_custom
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -335,3 +335,102 @@ def test_backward_bitwise_deterministic_across_plans_and_stealing():
                 t = plan.ticks.cpu().numpy()
                 busy = np.diff(plan.slots[(plan.next + 1) % 2]["h_off"].numpy()) > 0
                 assert (t >= 0).all() and (t[busy] > 0).all()
+
+
+# ---------------------------------------------------------------------------
+# own-block mask variant: context prefix [0, a_b) plus the block's own keys
+# ---------------------------------------------------------------------------
+
+OWN_CASES = {
+    "c3_small": ("c3", dict(n_ctx_range=(500, 2500), n_anchor=6, hq=8, hkv=2, chunk=512)),
+    "c5_small": ("c5", dict(n_ctx=4100, n_anchor=12, hq=4, hkv=4, chunk=1024)),   # G = 1, 32-token blocks
+    "c4_small": ("c4", dict(n_ctx=8192, n_anchor=8, hq=4, hkv=1, chunk=256)),     # G = 4, many chunks
+}
+
+
+def _own_upload(w):
+    return to_device(w, "k_own", DEV), to_device(w, "v_own", DEV)
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_c1_fp32_own_block_forward(seed):
+    """The fp32 tiny config under the own-block reading of its mask."""
+    w = add_own_block(make("c1", seed=seed))
+    path = make_path(w, DEV, mask="own_block")
+    q, k, v = _upload(w)
+    ko, vo = _own_upload(w)
+    path.forward(q, k, v, k_own=ko, v_own=vo)
+    torch.cuda.synchronize()
+    O, L = oracle.attention_own_workload(w)
+    assert np.isfinite(to_np64(path.lse)).all()
+    _check_merged(path, w, O, L, abs_tol=F32_ABS, frob_tol=None, lse_tol=F32_ABS)
+    # the own-block partial of each sequence sits after its chunks
+    for s in range(w.cfg.n_seq):
+        qs = slice(int(w.q_off[s]), int(w.q_off[s + 1]))
+        o, m, lse = oracle.own_partial(w.as_f64("q", rows=qs), w.as_f64("k_own", rows=qs), w.as_f64("v_own", rows=qs),
+                                       w.cfg.block, w.sm_scale, w.cfg.hkv)
+        go, gm, gl = [to_np64(t)[-1] for t in path.partial_view(s)]
+        assert_lse(f"seq{s} own lse", gl, lse, F32_ABS)
+        assert_close(f"seq{s} own o", go * np.exp(gm - gl)[..., None], o * np.exp(m - lse)[..., None], F32_ABS)
+
+
+@pytest.mark.parametrize("case", sorted(OWN_CASES))
+def test_bf16_own_block_forward_and_backward(case):
+    cfg, over = OWN_CASES[case]
+    w = add_own_block(make(cfg, seed=13, with_do=True, **over))
+    path = make_path(w, DEV, with_bwd=True, bwd_granule=192, mask="own_block", fwd_runs_per_worker=2)
+    q, k, v = _upload(w)
+    ko, vo = _own_upload(w)
+    do = to_device(w, "do", DEV)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dko, dvo = torch.empty_like(ko), torch.empty_like(vo)
+    path.forward(q, k, v, k_own=ko, v_own=vo)
+    path.backward(q, k, v, do, dq, dk, dv, own=(ko, vo, dko, dvo))
+    torch.cuda.synchronize()
+    O, L = oracle.attention_own_workload(w)
+    _check_merged(path, w, O, L)
+    rq, rk, rv, rko, rvo = oracle.bwd_own_workload(w)
+    assert_close("dQ", to_np64(dq), rq, BF16_ABS, BF16_FROB)
+    assert_close("dK", to_np64(dk), rk, BF16_ABS, BF16_FROB)
+    assert_close("dV", to_np64(dv), rv, BF16_ABS, BF16_FROB)
+    assert_close("dK_own", to_np64(dko), rko, BF16_ABS, BF16_FROB)
+    assert_close("dV_own", to_np64(dvo), rvo, BF16_ABS, BF16_FROB)
+
+
+def test_bf16_own_block_matches_prefix_mask_when_own_keys_are_context_keys():
+    """Own keys copied from the context at [a_b, a_b + B): the own-block path
+    reproduces the prefix-mask path's O, LSE and dQ (up to rounding), and its
+    dK_own / dV_own scattered back complete the prefix path's dK / dV."""
+    w = make_custom([1000, 700], [[0, 40, 41, 500], [3, 64, 300, 684]], block=16, hq=8, hkv=2, d=128,
+                    dtype="bf16", chunk=128, seed=21, with_do=True)
+    w = add_own_block(w, from_context=True)
+    q, k, v = _upload(w)
+    ko, vo = _own_upload(w)
+    do = to_device(w, "do", DEV)
+    res = {}
+    for mask in ("prefix", "own_block"):
+        path = make_path(w, DEV, with_bwd=True, mask=mask)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        dko, dvo = torch.empty_like(ko), torch.empty_like(vo)
+        if mask == "prefix":
+            path.forward(q, k, v)
+            path.backward(q, k, v, do, dq, dk, dv)
+        else:
+            path.forward(q, k, v, k_own=ko, v_own=vo)
+            path.backward(q, k, v, do, dq, dk, dv, own=(ko, vo, dko, dvo))
+        torch.cuda.synchronize()
+        res[mask] = [to_np64(t) for t in (path.o, path.lse, dq, dk, dv, dko, dvo)]
+    a, b = res["prefix"], res["own_block"]
+    assert_close("O", b[0], a[0], BF16_ABS, BF16_FROB)
+    assert_lse("LSE", b[1], a[1], BF16_LSE_REL)
+    assert_close("dQ", b[2], a[2], BF16_ABS, BF16_FROB)
+    dk_sum, dv_sum = b[3].copy(), b[4].copy()
+    B = w.cfg.block
+    for s in range(w.cfg.n_seq):
+        k0, t0 = int(w.kv_off[s]), int(w.q_off[s])
+        for bi, an in enumerate(w.seq_anchors(s)):
+            rows = slice(t0 + bi * B, t0 + (bi + 1) * B)
+            dk_sum[k0 + an:k0 + an + B] += b[5][rows]
+            dv_sum[k0 + an:k0 + an + B] += b[6][rows]
+    assert_close("dK", dk_sum, a[3], 2 * BF16_ABS, BF16_FROB)
+    assert_close("dV", dv_sum, a[4], 2 * BF16_ABS, BF16_FROB)
