@@ -144,7 +144,7 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // order (sequence, KV head, packed row p = (b*G + hl)*B + i), which is the
 // order both backward kernels walk; the first partial row of each sequence.
 struct BwdWorkspace {
-  size_t dq_part, qp, dop, lsep, deltap, endp, part_base, total;
+  size_t dq_part, dq_run, qp, dop, lsep, deltap, endp, part_base, total;
 };
 static BwdWorkspace bwd_workspace(const skv_problem* p) {
   int64_t rows = 0;
@@ -155,7 +155,8 @@ static BwdWorkspace bwd_workspace(const skv_problem* p) {
   const size_t prow = (size_t)p->h_q_off[p->n_seq] * (size_t)p->hq;  // packed rows
   BwdWorkspace w;
   w.dq_part = 0;
-  w.qp = align256((size_t)rows * (size_t)p->d * sizeof(float));
+  w.dq_run = align256((size_t)rows * (size_t)p->d * sizeof(float));
+  w.qp = w.dq_run + align256((size_t)rows * sizeof(int32_t));
   w.dop = w.qp + align256(prow * (size_t)p->d * 2);
   w.lsep = w.dop + align256(prow * (size_t)p->d * 2);
   w.deltap = w.lsep + align256(prow * sizeof(float));
@@ -204,6 +205,7 @@ extern "C" int sparse_attn_bwd(const skv_problem* p, const skv_plan* plan_kv, co
   BwdArgs a{};
   a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.dout = dout; a.dq = dq; a.dk = dk; a.dv = dv;
   a.dq_part = reinterpret_cast<float*>(w + ws.dq_part);
+  a.dq_run = reinterpret_cast<int32_t*>(w + ws.dq_run);
   a.qp = reinterpret_cast<uint16_t*>(w + ws.qp);
   a.dop = reinterpret_cast<uint16_t*>(w + ws.dop);
   a.lsep = reinterpret_cast<float*>(w + ws.lsep);

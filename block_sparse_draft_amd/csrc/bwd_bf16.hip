@@ -415,14 +415,12 @@ void bwd_dq_kernel(BwdArgs a) {
     const int nrows = (it.hi - it.lo) * GB;
     const uint16_t* Kseq = K + k0 * a.kv_st + (int64_t)it.kv_head * a.kv_sh;
     const uint16_t* Vseq = V + k0 * a.kv_st + (int64_t)it.kv_head * a.kv_sh;
+    // keys of the item's chunks (a run of consecutive chunks: one dQ partial
+    // for all of them, in the first chunk's rows, with the run length beside it)
     const int n_chunk = max(1, uniform(it.n_chunk));
-
-    // one dQ partial per chunk of the item (an item of several chunks writes
-    // each of them, exactly as the single-chunk items would)
-    for (int cc = 0; cc < n_chunk; ++cc) {
-    const int klo = (it.chunk + cc) * a.chunk;
-    const int khi = min(klo + a.chunk, n_ctx);
-    const int64_t part_base = it.part_base + (int64_t)cc * a.hq * mq;
+    const int klo = it.chunk * a.chunk;
+    const int khi = (int)min((int64_t)(it.chunk + n_chunk) * a.chunk, (int64_t)n_ctx);
+    const int64_t part_base = it.part_base;
     for (int rt = 0; rt < nrows; rt += 256) {
       const int p_last = min(nrows, rt + 256) - 1;
       const int wg_hi = max(klo, min(khi, a.endp[pitem + p_last]));
@@ -539,10 +537,11 @@ void bwd_dq_kernel(BwdArgs a) {
         }
       }
 
-      // ---- the chunk's dQ partial (unscaled) for rows that see the chunk ----
+      // ---- the item's dQ partial (unscaled) for rows that see its keys ----
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
         if (!valid[nt] || vend[nt] <= klo) continue;
+        if (hf == 0) a.dq_run[prow[nt]] = n_chunk;
         float* op = a.dq_part + prow[nt] * D + hf * 4;
 #pragma unroll
         for (int md = 0; md < 4; ++md)
@@ -554,13 +553,12 @@ void bwd_dq_kernel(BwdArgs a) {
           }
       }
     }
-    }  // chunks of the item
   }
   record_ticks(a.q_ticks, me, t_start);
 }
 
 // ---------------------------------------------------------------------------
-// 4. finalize: dQ = scale * sum of visible chunk partials
+// 4. finalize: dQ = scale * sum of the row's dQ partials
 // ---------------------------------------------------------------------------
 
 __global__ __launch_bounds__(256) void bwd_finalize_kernel(BwdArgs a) {
@@ -581,10 +579,17 @@ __global__ __launch_bounds__(256) void bwd_finalize_kernel(BwdArgs a) {
   const int n_ctx = (int)(a.kv_off[s + 1] - a.kv_off[s]);
   const int e = min(a.anchor[(q0 + r) / a.block] + a.end_shift, n_ctx);
   const int nc = (e + a.chunk - 1) / a.chunk;  // chunks the row sees
-  const float* src = a.dq_part + (a.part_base[s] + (int64_t)h * mq + r) * D + ln * 4;
+  const int64_t prow0 = a.part_base[s] + (int64_t)h * mq + r;
+  const float* src = a.dq_part + prow0 * D + ln * 4;
   const int64_t cstride = (int64_t)a.hq * mq * D;
   f32x4 sum = {0.f, 0.f, 0.f, 0.f};
-  for (int cc = 0; cc < nc; ++cc) sum += *reinterpret_cast<const f32x4*>(src + cc * cstride);
+  // The chunks the row sees are covered by runs in order; each run's partial
+  // sits in its first chunk's rows with the run length beside it (>= 1, so
+  // the walk always ends).
+  for (int cc = 0; cc < nc;) {
+    sum += *reinterpret_cast<const f32x4*>(src + cc * cstride);
+    cc += max(1, a.dq_run[prow0 + (int64_t)cc * a.hq * mq]);
+  }
   if (a.own) {  // the own-block partial follows the sequence's chunks
     const int n_chunk = (n_ctx + a.chunk - 1) / a.chunk;
     sum += *reinterpret_cast<const f32x4*>(src + n_chunk * cstride);

@@ -67,7 +67,8 @@ struct BwdArgs {
   void* dq;
   void* dk;
   void* dv;
-  float* dq_part;     // per-chunk dQ partials, the forward's partial layout, [rows][d] fp32
+  float* dq_part;     // dQ partials, the forward's partial layout, [rows][d] fp32
+  int32_t* dq_run;    // [rows]: chunks covered by the dQ partial in that row (written with it)
   // Packed row order: row P = q_off[s]*hq + g*G*Mq_s + (b*G + hl)*B + i holds
   // token q_off[s] + b*B + i of query head g*G + hl.
   uint16_t* qp;       // [sum Mq * hq][d] bf16 copy of Q

@@ -141,7 +141,8 @@ class SplitKVAttention:
         self.bwd_plan = (_PlanSlots(self.problem, B.SKV_ITEM_BWD, self.bwd_granule, self.n_workers, policy, **kw)
                          if with_bwd else None)
         # dQ runs over the forward's items; its own slots give it separate claim cursors
-        self.dq_plan = (_PlanSlots(self.problem, B.SKV_ITEM_FWD, self.fwd_granule, self.n_workers, policy, **kw)
+        self.dq_plan = (_PlanSlots(self.problem, B.SKV_ITEM_FWD, self.fwd_granule, self.n_workers, policy, **kw,
+                                   runs_per_worker=self.fwd_runs_per_worker)
                         if with_bwd else None)
         self.replan()
         self.part_base, self.n_chunk = self.problem.partial_layout()

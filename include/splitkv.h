@@ -266,7 +266,8 @@ int lse_merge(int32_t n_part, int32_t hq, int64_t mq, int32_t d, const float* o_
               float* lse_out, int64_t lse_stride_tok, void* stream);
 
 /* Bytes of device workspace sparse_attn_bwd needs (256-byte aligned pieces):
- * fp32 dQ partials in the layout of skv_partial_layout ([rows][d]); bf16
+ * fp32 dQ partials in the layout of skv_partial_layout ([rows][d]) and an
+ * int32 run length per partial row; bf16
  * copies of Q and dO and fp32 LSE, Delta and int32 prefix ends in the
  * backward's packed row order; n_seq+1 int64 partial offsets.  0 for an
  * invalid problem. */
@@ -280,8 +281,10 @@ size_t skv_bwd_workspace_bytes(const skv_problem* p);
  * [sum Mq][hq]), dout = dO.  Outputs dq (Q layout), dk and dv (K/V layout)
  * are fully written, dk = dv = 0 for keys no query sees.
  * plan_kv is a BWD plan (key ranges; dK, dV are owned by their item);
- * plan_q is a FWD plan over the forward's items (each writes the dQ partial of
- * its chunk, summed per row afterwards).  The two plans need distinct claim
+ * plan_q is a FWD plan over the forward's items or chunk runs
+ * (skv_coarsen_fwd_items): each item writes one dQ partial for all its
+ * chunks, in its first chunk's rows, and the partials a row sees are summed
+ * afterwards (plan_q must cover every nonzero-cost item exactly once).  The two plans need distinct claim
  * arrays.  No atomics: the result is bitwise reproducible.
  * Only SKV_BF16 with d = 128 is supported.
  * Under SKV_MASK_OWN_BLOCK `own` is required: its keys and values enter P and

@@ -188,9 +188,10 @@ def test_device_calls_reject_bad_arguments_before_touching_the_gpu():
     pb = _problem_from(wb)
     pb.c.d_q_off = pb.c.d_kv_off = pb.c.d_anchor = 4096
     need = B.lib.skv_bwd_workspace_bytes(C.byref(pb.c))
-    # dQ partials: 1 chunk (256 keys, chunk 1024) x 32 heads x 32 rows x 128 fp32; packed Q and dO
-    # (1024 rows x 128 bf16 each); packed LSE, Delta, prefix end (1024 x 4 bytes each); 2 offsets
-    assert need == 32 * 32 * 128 * 4 + 2 * 1024 * 128 * 2 + 3 * 1024 * 4 + 256
+    # dQ partials: 1 chunk (256 keys, chunk 1024) x 32 heads x 32 rows x 128 fp32, and their
+    # run lengths (int32 each); packed Q and dO (1024 rows x 128 bf16 each); packed LSE, Delta,
+    # prefix end (1024 x 4 bytes each); 2 offsets
+    assert need == 32 * 32 * 128 * 4 + 1024 * 4 + 2 * 1024 * 128 * 2 + 3 * 1024 * 4 + 256
     qplan = B.skv_plan(B.SKV_ITEM_FWD, 4, 1, 16, 16, 32)
     rc = B.lib.sparse_attn_bwd(C.byref(pb.c), C.byref(bplan), C.byref(qplan), *([fake] * 10), need - 1, None, None)
     assert rc == B.SKV_EWORKSPACE

@@ -199,6 +199,19 @@ def test_bf16_backward_small(case):
     _check_grads(w, got)
 
 
+@pytest.mark.parametrize("case,runs_per_worker", [("c4_small", 1), ("c3_small", 2), ("c5_small", 1)])
+def test_bf16_backward_chunk_runs(case, runs_per_worker):
+    """Forward and query-owner plans over chunk runs (one dQ partial per run,
+    summed along the run lengths) give the oracle's gradients."""
+    cfg, over = SMALL_BF16[case]
+    w = make(cfg, seed=11, with_do=True, **over)
+    path = make_path(w, DEV, with_bwd=True, bwd_granule=192, n_workers=8, fwd_runs_per_worker=runs_per_worker)
+    assert (path.dq_plan.table[0]["n_chunk"] > 1).any()
+    q, k, v = _upload(w)
+    got = _bwd(w, path, q, k, v)
+    _check_grads(w, got)
+
+
 def test_bf16_backward_edge_anchors():
     w = make_custom([1000, 130], [[0, 0, 63, 64, 700], [1, 2, 3, 128, 129]], block=16, hq=4, hkv=2, d=128,
                     dtype="bf16", chunk=128, seed=5, with_do=True)
