@@ -3,12 +3,14 @@
 // result equals the unsharded one).  Bandwidth-bound: every visible partial
 // row (d fp32) is read once, every output row written once.
 //
-// Workgroup = 32 consecutive query rows of one head.  Step A: one thread per
-// row folds the n_part log-sum-exps into the merged LSE.  Then, 64 partials at
-// a time, step B computes the weights exp(m_c - LSE) (0 for partials the row
-// does not see) into LDS with row-coalesced loads, and step C accumulates the
-// weighted partial rows, 16 bytes per lane, skipping zero-weight partials so
-// their (unwritten) rows are never read.
+// Workgroup = 32 consecutive query rows of one head.  Step A: eight lanes
+// per row fold the n_part log-sum-exps (each lane a strided eighth, then the
+// eight partial folds combined) into the merged LSE.  Then, 64 partials at a
+// time, step B lists per row the partials with a nonzero weight
+// exp(m_c - LSE) in ascending partial order (0 for partials the row does not
+// see, whose unwritten rows are never read), and step C accumulates the
+// weighted partial rows of each list, 16 bytes per lane, four independent
+// loads at a time.  The order of every sum is fixed: bitwise deterministic.
 #include "device.h"
 #include "launch.h"
 #include "timing.h"
@@ -18,6 +20,16 @@ namespace {
 
 constexpr int MROWS = 32;   // rows per workgroup
 constexpr int CBLK = 64;    // partials per weight block
+constexpr int LPRA = 8;     // lanes per row in steps A and B
+
+// (max, sum of exp(x - max)) of two disjoint sets combined.
+__device__ __forceinline__ void lse_combine(float& mx, float& sum, float m2, float s2) {
+  if (m2 == -INFINITY) return;
+  if (mx == -INFINITY) { mx = m2; sum = s2; return; }
+  const float m = fmaxf(mx, m2);
+  sum = sum * expf(mx - m) + s2 * expf(m2 - m);
+  mx = m;
+}
 
 template <int D>
 __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
@@ -25,34 +37,45 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   constexpr int SLOTS = 256 / LPR;        // row slots per workgroup
   constexpr int RPS = MROWS / SLOTS;      // rows handled per slot
   __shared__ float sLse[MROWS];
-  __shared__ float sW[CBLK][MROWS];
+  __shared__ float sW[MROWS][CBLK];       // nonzero weights of the block, per row, ascending partial
+  __shared__ int sC[MROWS][CBLK];         // their partial index
+  __shared__ int sN[MROWS];
 
   const int tid = threadIdx.x;
+  const int lane = tid & 63;
   const int h = blockIdx.y;
   const int64_t r0 = (int64_t)blockIdx.x * MROWS;
   const int64_t hm = (int64_t)h * a.mq;
   const int64_t pstride = (int64_t)a.hq * a.mq;  // rows between consecutive partials
+  const int ra = tid / LPRA, pa = tid % LPRA;    // steps A, B: row, lane within the row
+  const int64_t rowa = r0 + ra;
+  const bool live_a = rowa < a.mq;
 
   // ---- step A: merged LSE of each row ----
-  if (tid < MROWS) {
-    const int64_t r = r0 + tid;
-    float lse = -INFINITY;
-    if (r < a.mq) {
-      float mx = -INFINITY, sum = 0.f;
-      for (int c = 0; c < a.n_part; ++c) {
-        const float x = a.lse_part[c * pstride + hm + r];
-        if (x == -INFINITY) continue;
-        if (x > mx) {
-          sum = sum * expf(mx - x) + 1.f;
-          mx = x;
-        } else {
-          sum += expf(x - mx);
+  {
+    float mx = -INFINITY, sum = 0.f;
+    if (live_a) {
+      for (int c0 = pa; c0 < a.n_part; c0 += 4 * LPRA) {
+        float x[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int c = c0 + u * LPRA;
+          x[u] = c < a.n_part ? a.lse_part[c * pstride + hm + rowa] : -INFINITY;
         }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) lse_combine(mx, sum, x[u], 1.f);
       }
-      lse = mx == -INFINITY ? -INFINITY : mx + logf(sum);
-      a.lse_out[r * a.lse_st + h] = lse;
     }
-    sLse[tid] = lse;
+#pragma unroll
+    for (int o = 1; o < LPRA; o <<= 1) {
+      const float m2 = __shfl_xor(mx, o), s2 = __shfl_xor(sum, o);
+      lse_combine(mx, sum, m2, s2);
+    }
+    const float lse = mx == -INFINITY ? -INFINITY : mx + logf(sum);
+    if (pa == 0) {
+      if (live_a) a.lse_out[rowa * a.lse_st + h] = lse;
+      sLse[ra] = lse;
+    }
   }
 
   const int slot = tid / LPR, ln = tid % LPR;
@@ -61,34 +84,46 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   for (int i = 0; i < RPS; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   for (int cb = 0; cb < a.n_part; cb += CBLK) {
-    __syncthreads();
-    // ---- step B: weights of partials [cb, cb + 64) for the 32 rows ----
-    for (int idx = tid; idx < CBLK * MROWS; idx += 256) {
-      const int rr = idx % MROWS, cc = idx / MROWS;
-      const int c = cb + cc;
-      const int64_t r = r0 + rr;
-      float w = 0.f;
-      if (c < a.n_part && r < a.mq) {
-        const float lc = a.lse_part[c * pstride + hm + r];
-        const float L = sLse[rr];
-        if (lc != -INFINITY && L != -INFINITY) w = expf(a.m_part[c * pstride + hm + r] - L);
+    __syncthreads();  // sLse written; the previous block's lists are consumed
+    // ---- step B: this row's nonzero weights among partials [cb, cb + 64) ----
+    {
+      const float L = sLse[ra];
+      int count = 0;
+#pragma unroll
+      for (int u = 0; u < CBLK / LPRA; ++u) {
+        const int c = cb + u * LPRA + pa;
+        float w = 0.f;
+        if (live_a && c < a.n_part && L != -INFINITY) {
+          const float lc = a.lse_part[c * pstride + hm + rowa];
+          if (lc != -INFINITY) w = expf(a.m_part[c * pstride + hm + rowa] - L);
+        }
+        const uint64_t bal = __ballot(w != 0.f);
+        const uint32_t bits = (uint32_t)(bal >> (lane & ~(LPRA - 1))) & ((1u << LPRA) - 1);
+        if (w != 0.f) {
+          const int pos = count + __popc(bits & ((1u << pa) - 1));
+          sW[ra][pos] = w;
+          sC[ra][pos] = c;
+        }
+        count += __popc(bits);
       }
-      sW[cc][rr] = w;
+      if (pa == 0) sN[ra] = count;
     }
     __syncthreads();
-    // ---- step C: accumulate weighted partial rows ----
-    const int cn = min(CBLK, a.n_part - cb);
-    for (int cc = 0; cc < cn; ++cc) {
-      const float* base = a.o_part + ((int64_t)(cb + cc) * pstride + hm + r0) * D + ln * 4;
+    // ---- step C: accumulate the listed partial rows ----
 #pragma unroll
-      for (int i = 0; i < RPS; ++i) {
-        const int rr = slot * RPS + i;
-        const float w = sW[cc][rr];
-        if (w != 0.f) {
-          const f32x4 v = *reinterpret_cast<const f32x4*>(base + (int64_t)rr * D);
-          acc[i] += w * v;
-        }
+    for (int i = 0; i < RPS; ++i) {
+      const int rr = slot * RPS + i;
+      const int n = sN[rr];
+      const float* base = a.o_part + (hm + r0 + rr) * D + ln * 4;
+      int k = 0;
+      for (; k + 4 <= n; k += 4) {
+        f32x4 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const f32x4*>(base + (int64_t)sC[rr][k + u] * pstride * D);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) acc[i] += sW[rr][k + u] * v[u];
       }
+      for (; k < n; ++k) acc[i] += sW[rr][k] * *reinterpret_cast<const f32x4*>(base + (int64_t)sC[rr][k] * pstride * D);
     }
   }
 
