@@ -365,6 +365,7 @@ def main():
         "plan": {"host_ms_per_step": round(1e3 * float(np.mean(plan_s)), 3) if plan_s else None,
                  "fwd_items": path.fwd_plan.n_items, "fwd_items_planned": path.fwd_plan.n_planned,
                  "fwd_partial_rows_written": int(torch.isfinite(path.lse_part).sum().item()),
+                 "fwd_runs_per_worker_used": path.fwd_plan.runs_used,
                  "fwd_imbalance": round(path.fwd_plan.imbalance, 5),
                  "bwd_items": path.bwd_plan.n_items if with_bwd else None,
                  "bwd_imbalance": round(path.bwd_plan.imbalance, 5) if with_bwd else None},

@@ -20,18 +20,25 @@ def default_workers(device) -> int:
     return torch.cuda.get_device_properties(device).multi_processor_count
 
 
+RUN_IMBALANCE = 0.02        # LPT cost imbalance accepted for chunk runs
+MAX_RUNS_PER_WORKER = 64
+
+
 class _PlanSlots:
     """Two pinned-host / device buffer pairs for one kind of plan, so that the
     next step's plan uploads (asynchronously, on the compute stream) while the
     previous step's kernels may still read the other pair."""
 
     def __init__(self, problem: B.Problem, kind: int, granule: int, n_workers: int, policy: str,
-                 steal: bool = True, ticks: bool = False, runs_per_worker: Optional[float] = None):
+                 steal: bool = True, ticks: bool = False, runs_per_worker: Optional[float] = None,
+                 run_imbalance: Optional[float] = RUN_IMBALANCE):
         import torch
         self.problem, self.kind, self.granule, self.n_workers, self.policy = problem, kind, granule, n_workers, policy
         # forward only: chunks of the same rows merged into runs of about
         # total cost / (n_workers * runs_per_worker) (None: one chunk per item)
         self.runs_per_worker = runs_per_worker
+        self.run_imbalance = run_imbalance  # None: keep runs_per_worker as given
+        self.runs_used = None
         self.flags = 0 if steal else B.SKV_PLAN_NO_STEAL
         n = len(problem.item_table(kind, granule)[1])
         dev = problem.device
@@ -62,11 +69,25 @@ class _PlanSlots:
         if self.runs_per_worker and self.kind == B.SKV_ITEM_FWD:
             if self.policy != "lpt":
                 raise ValueError("chunk runs are planned with LPT only")
-            target = max(1, int(np.ceil(cost.sum() / (self.n_workers * self.runs_per_worker))))
-            items, cost = B.skv_coarsen_fwd_items(items, cost, target)
+            # Longer runs mean fewer partials but coarser items: halve the run
+            # cost until LPT balances the runs to within RUN_IMBALANCE (or
+            # MAX_RUNS_PER_WORKER is reached).
+            rpw = self.runs_per_worker
+            while True:
+                target = max(1, int(np.ceil(cost.sum() / (self.n_workers * rpw))))
+                r_items, r_cost = B.skv_coarsen_fwd_items(items, cost, target)
+                _, order, off, load = B.lpt_plan(r_cost, self.n_workers)
+                mean = load.mean()
+                if (self.run_imbalance is None or rpw >= MAX_RUNS_PER_WORKER or mean == 0
+                        or load.max() / mean - 1.0 <= self.run_imbalance):
+                    break
+                rpw *= 2
+            items, cost = r_items, r_cost
+            self.runs_used = rpw
         self.table = (items, cost)  # the items planned (chunk runs when asked for)
         if self.policy == "lpt":
-            _, order, off, load = B.lpt_plan(cost, self.n_workers)
+            if not (self.runs_per_worker and self.kind == B.SKV_ITEM_FWD):
+                _, order, off, load = B.lpt_plan(cost, self.n_workers)
         elif self.policy == "static":
             assign, order, off = B.skv_static_plan(tok, total, self.n_workers)
             load = np.bincount(assign, weights=cost, minlength=self.n_workers).astype(np.int64)
@@ -112,7 +133,8 @@ class SplitKVAttention:
                  sm_scale: float, dtype, device, n_workers: Optional[int] = None,
                  fwd_granule: Optional[int] = None, bwd_granule: int = 256, policy: str = "lpt",
                  with_bwd: bool = True, steal: bool = True, ticks: bool = False,
-                 fwd_runs_per_worker: Optional[float] = 4.0, mask: str = "prefix"):
+                 fwd_runs_per_worker: Optional[float] = 4.0, mask: str = "prefix",
+                 fwd_run_imbalance: Optional[float] = RUN_IMBALANCE):
         import torch
         self.device = torch.device(device)
         self.dtype = dtype
@@ -133,16 +155,17 @@ class SplitKVAttention:
         self.bwd_granule = bwd_granule
         kw = dict(steal=steal, ticks=ticks)
         # Forward items cover runs of consecutive chunks of the same rows, about
-        # fwd_runs_per_worker per workgroup, each with one partial (LPT plans
+        # fwd_runs_per_worker per workgroup (more when LPT cannot balance the
+        # runs to within fwd_run_imbalance), each with one partial (LPT plans
         # only; None or a static plan: one chunk per item, one partial per chunk).
         self.fwd_runs_per_worker = fwd_runs_per_worker if policy == "lpt" else None
         self.fwd_plan = _PlanSlots(self.problem, B.SKV_ITEM_FWD, self.fwd_granule, self.n_workers, policy, **kw,
-                                   runs_per_worker=self.fwd_runs_per_worker)
+                                   runs_per_worker=self.fwd_runs_per_worker, run_imbalance=fwd_run_imbalance)
         self.bwd_plan = (_PlanSlots(self.problem, B.SKV_ITEM_BWD, self.bwd_granule, self.n_workers, policy, **kw)
                          if with_bwd else None)
         # dQ runs over the forward's items; its own slots give it separate claim cursors
         self.dq_plan = (_PlanSlots(self.problem, B.SKV_ITEM_FWD, self.fwd_granule, self.n_workers, policy, **kw,
-                                   runs_per_worker=self.fwd_runs_per_worker)
+                                   runs_per_worker=self.fwd_runs_per_worker, run_imbalance=fwd_run_imbalance)
                         if with_bwd else None)
         self.replan()
         self.part_base, self.n_chunk = self.problem.partial_layout()

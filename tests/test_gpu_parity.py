@@ -109,7 +109,8 @@ def test_bf16_forward_chunk_runs(case, runs_per_worker):
     partials, and the run's other chunk rows stay -inf."""
     cfg, over = SMALL_BF16[case]
     w = make(cfg, seed=7, with_do=False, **over)
-    path = make_path(w, DEV, with_bwd=False, n_workers=8, fwd_runs_per_worker=runs_per_worker)
+    path = make_path(w, DEV, with_bwd=False, n_workers=8, fwd_runs_per_worker=runs_per_worker,
+                     fwd_run_imbalance=None)
     q, k, v = _upload(w)
     path.forward(q, k, v)
     torch.cuda.synchronize()
@@ -205,7 +206,8 @@ def test_bf16_backward_chunk_runs(case, runs_per_worker):
     summed along the run lengths) give the oracle's gradients."""
     cfg, over = SMALL_BF16[case]
     w = make(cfg, seed=11, with_do=True, **over)
-    path = make_path(w, DEV, with_bwd=True, bwd_granule=192, n_workers=8, fwd_runs_per_worker=runs_per_worker)
+    path = make_path(w, DEV, with_bwd=True, bwd_granule=192, n_workers=8, fwd_runs_per_worker=runs_per_worker,
+                     fwd_run_imbalance=None)
     assert (path.dq_plan.table[0]["n_chunk"] > 1).any()
     q, k, v = _upload(w)
     got = _bwd(w, path, q, k, v)
@@ -391,7 +393,8 @@ def test_c1_fp32_own_block_forward(seed):
 def test_bf16_own_block_forward_and_backward(case):
     cfg, over = OWN_CASES[case]
     w = add_own_block(make(cfg, seed=13, with_do=True, **over))
-    path = make_path(w, DEV, with_bwd=True, bwd_granule=192, mask="own_block", fwd_runs_per_worker=2)
+    path = make_path(w, DEV, with_bwd=True, bwd_granule=192, mask="own_block", fwd_runs_per_worker=2,
+                     fwd_run_imbalance=None)
     q, k, v = _upload(w)
     ko, vo = _own_upload(w)
     do = to_device(w, "do", DEV)
