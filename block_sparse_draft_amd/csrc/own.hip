@@ -17,11 +17,34 @@ namespace skv {
 namespace {
 
 constexpr int OWN_THREADS = 256;
-constexpr int OWN_MAX_B = 64;        // keys of a block staged in LDS
-constexpr int OWN_MAX_PS = 8192;     // P / dS entries of a block staged in LDS (G*B*B)
+// The host limits block <= 64 and G*B*B <= 8192, so the dynamic LDS of these
+// kernels stays within 2*64*128*4 + 2*8192*4 bytes = 128 KB.
 
 __device__ __forceinline__ float ld_elem(const float* p, int64_t i) { return p[i]; }
 __device__ __forceinline__ float ld_elem(const uint16_t* p, int64_t i) { return bf16_bits_to_f32(p[i]); }
+
+// N consecutive elements (16-byte aligned) widened to fp32, in 16-byte loads.
+template <int N>
+__device__ __forceinline__ void ld_row(const float* p, float* out) {
+#pragma unroll
+  for (int k = 0; k < N / 4; ++k) {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(p + 4 * k);
+    out[4 * k] = v[0]; out[4 * k + 1] = v[1]; out[4 * k + 2] = v[2]; out[4 * k + 3] = v[3];
+  }
+}
+template <int N>
+__device__ __forceinline__ void ld_row(const uint16_t* p, float* out) {
+#pragma unroll
+  for (int k = 0; k < N / 8; ++k) {
+    const uint4 v = *reinterpret_cast<const uint4*>(p + 8 * k);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      out[8 * k + 2 * u] = __uint_as_float(w[u] << 16);
+      out[8 * k + 2 * u + 1] = __uint_as_float(w[u] & 0xffff0000u);
+    }
+  }
+}
 
 // Sequence of token t: q_off[s] <= t < q_off[s + 1].
 __device__ __forceinline__ int seq_of(const int64_t* q_off, int n_seq, int64_t t) {
@@ -44,10 +67,14 @@ __device__ __forceinline__ float quad_sum(float x) {
 // forward: the own-block partial of every row
 // ---------------------------------------------------------------------------
 
+// Dynamic LDS of the own-block kernels: K and V of the block's B own keys as
+// fp32 [B][D] each (the backward adds P and dS, fp32 [G*B][B] each).
+extern __shared__ float own_lds[];
+
 template <typename T, int D>
 __global__ __launch_bounds__(OWN_THREADS) void own_fwd_kernel(OwnFwdArgs a) {
-  __shared__ float sK[OWN_MAX_B][D];
-  __shared__ float sV[OWN_MAX_B][D];
+  float (*sK)[D] = reinterpret_cast<float (*)[D]>(own_lds);
+  float (*sV)[D] = reinterpret_cast<float (*)[D]>(own_lds + a.block * D);
   __shared__ unsigned long long s_base;
   constexpr int D4 = D / 4;
   const int tid = threadIdx.x;
@@ -86,8 +113,7 @@ __global__ __launch_bounds__(OWN_THREADS) void own_fwd_kernel(OwnFwdArgs a) {
     const int h = g * G + hl;
     const int64_t t = t0 + i;
     float qv[D4];
-#pragma unroll
-    for (int x = 0; x < D4; ++x) qv[x] = ld_elem(Q, t * a.q_st + (int64_t)h * a.q_sh + q4 * D4 + x);
+    ld_row<D4>(Q + t * a.q_st + (int64_t)h * a.q_sh + q4 * D4, qv);
     float m = -INFINITY, l = 0.f, o[D4];
 #pragma unroll
     for (int x = 0; x < D4; ++x) o[x] = 0.f;
@@ -124,13 +150,13 @@ __global__ __launch_bounds__(OWN_THREADS) void own_fwd_kernel(OwnFwdArgs a) {
 // the sequence's partial index C_s, summed by the finalize kernel.
 __global__ __launch_bounds__(OWN_THREADS) void own_bwd_kernel(BwdArgs a) {
   constexpr int D = 128, D4 = D / 4;
-  __shared__ float sK[OWN_MAX_B][D];
-  __shared__ float sV[OWN_MAX_B][D];
-  __shared__ float sP[OWN_MAX_PS];
-  __shared__ float sDS[OWN_MAX_PS];
   const int tid = threadIdx.x;
   const int g = blockIdx.y;
   const int B = a.block, G = a.group, R = G * B;
+  float (*sK)[D] = reinterpret_cast<float (*)[D]>(own_lds);
+  float (*sV)[D] = reinterpret_cast<float (*)[D]>(own_lds + B * D);
+  float* sP = own_lds + 2 * B * D;
+  float* sDS = sP + R * B;
   const int64_t t0 = (int64_t)blockIdx.x * B;
   const int s = seq_of(a.q_off, a.n_seq, t0);
   const int64_t q0 = a.q_off[s], mq = a.q_off[s + 1] - q0;
@@ -157,12 +183,10 @@ __global__ __launch_bounds__(OWN_THREADS) void own_bwd_kernel(BwdArgs a) {
     const int hl = r / B, i = r % B;
     const int h = g * G + hl;
     float qv[D4], dov[D4], dq[D4];
+    ld_row<D4>(a.qp + P * D + q4 * D4, qv);
+    ld_row<D4>(a.dop + P * D + q4 * D4, dov);
 #pragma unroll
-    for (int x = 0; x < D4; ++x) {
-      qv[x] = bf16_bits_to_f32(a.qp[P * D + q4 * D4 + x]);
-      dov[x] = bf16_bits_to_f32(a.dop[P * D + q4 * D4 + x]);
-      dq[x] = 0.f;
-    }
+    for (int x = 0; x < D4; ++x) dq[x] = 0.f;
     const float lse2 = a.lsep[P], del = a.deltap[P];
     for (int j = 0; j < B; ++j) {
       float sd = 0.f, pd = 0.f;
@@ -197,18 +221,31 @@ __global__ __launch_bounds__(OWN_THREADS) void own_bwd_kernel(BwdArgs a) {
     float ak[8], av[8];
 #pragma unroll
     for (int x = 0; x < 8; ++x) ak[x] = av[x] = 0.f;
-    for (int r = 0; r < R; ++r) {
-      const int64_t P = P0 + r;
-      const uint4 qw = *reinterpret_cast<const uint4*>(a.qp + P * D + c8 * 8);
-      const uint4 ow = *reinterpret_cast<const uint4*>(a.dop + P * D + c8 * 8);
-      const float ds = sDS[r * B + j], p = sP[r * B + j];
-      const uint32_t qa[4] = {qw.x, qw.y, qw.z, qw.w}, oa[4] = {ow.x, ow.y, ow.z, ow.w};
+    // rows four at a time (R = G*B is a multiple of 4 whenever B is; a
+    // ragged tail is clamped to the last row with zero weights)
+    for (int r0 = 0; r0 < R; r0 += 4) {
+      uint4 qw[4], ow[4];
+      float ds[4], p[4];
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        ak[2 * w] = fmaf(ds, __uint_as_float(qa[w] << 16), ak[2 * w]);
-        ak[2 * w + 1] = fmaf(ds, __uint_as_float(qa[w] & 0xffff0000u), ak[2 * w + 1]);
-        av[2 * w] = fmaf(p, __uint_as_float(oa[w] << 16), av[2 * w]);
-        av[2 * w + 1] = fmaf(p, __uint_as_float(oa[w] & 0xffff0000u), av[2 * w + 1]);
+      for (int u = 0; u < 4; ++u) {
+        const int r = min(r0 + u, R - 1);
+        const int64_t P = P0 + r;
+        qw[u] = *reinterpret_cast<const uint4*>(a.qp + P * D + c8 * 8);
+        ow[u] = *reinterpret_cast<const uint4*>(a.dop + P * D + c8 * 8);
+        const bool in = r0 + u < R;
+        ds[u] = in ? sDS[r * B + j] : 0.f;
+        p[u] = in ? sP[r * B + j] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const uint32_t qa[4] = {qw[u].x, qw[u].y, qw[u].z, qw[u].w}, oa[4] = {ow[u].x, ow[u].y, ow[u].z, ow[u].w};
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          ak[2 * w] = fmaf(ds[u], __uint_as_float(qa[w] << 16), ak[2 * w]);
+          ak[2 * w + 1] = fmaf(ds[u], __uint_as_float(qa[w] & 0xffff0000u), ak[2 * w + 1]);
+          av[2 * w] = fmaf(p[u], __uint_as_float(oa[w] << 16), av[2 * w]);
+          av[2 * w + 1] = fmaf(p[u], __uint_as_float(oa[w] & 0xffff0000u), av[2 * w + 1]);
+        }
       }
     }
     uint32_t kw[4], vw[4];
@@ -230,19 +267,21 @@ hipError_t launch_own_fwd(const OwnFwdArgs& a, int dtype, int d, int64_t n_block
   if (n_blocks == 0) return hipSuccess;
   TimedLaunch t(kOwnFwd, stream);
   const dim3 grid((unsigned)n_blocks, (unsigned)a.hkv);
+  const size_t lds = (size_t)2 * a.block * d * sizeof(float);
   if (dtype == SKV_BF16)
-    hipLaunchKernelGGL((own_fwd_kernel<uint16_t, 128>), grid, dim3(OWN_THREADS), 0, stream, a);
+    hipLaunchKernelGGL((own_fwd_kernel<uint16_t, 128>), grid, dim3(OWN_THREADS), lds, stream, a);
   else if (d == 128)
-    hipLaunchKernelGGL((own_fwd_kernel<float, 128>), grid, dim3(OWN_THREADS), 0, stream, a);
+    hipLaunchKernelGGL((own_fwd_kernel<float, 128>), grid, dim3(OWN_THREADS), lds, stream, a);
   else
-    hipLaunchKernelGGL((own_fwd_kernel<float, 64>), grid, dim3(OWN_THREADS), 0, stream, a);
+    hipLaunchKernelGGL((own_fwd_kernel<float, 64>), grid, dim3(OWN_THREADS), lds, stream, a);
   return hipGetLastError();
 }
 
 hipError_t launch_own_bwd(const BwdArgs& a, int64_t n_blocks, hipStream_t stream) {
   if (n_blocks == 0) return hipSuccess;
   TimedLaunch t(kOwnBwd, stream);
-  hipLaunchKernelGGL(own_bwd_kernel, dim3((unsigned)n_blocks, (unsigned)a.hkv), dim3(OWN_THREADS), 0, stream, a);
+  const size_t lds = (size_t)(2 * a.block * 128 + 2 * a.group * a.block * a.block) * sizeof(float);
+  hipLaunchKernelGGL(own_bwd_kernel, dim3((unsigned)n_blocks, (unsigned)a.hkv), dim3(OWN_THREADS), lds, stream, a);
   return hipGetLastError();
 }
 

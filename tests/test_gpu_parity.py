@@ -450,3 +450,35 @@ def test_bf16_own_block_matches_prefix_mask_when_own_keys_are_context_keys():
             dv_sum[k0 + an:k0 + an + B] += b[6][rows]
     assert_close("dK", dk_sum, a[3], 2 * BF16_ABS, BF16_FROB)
     assert_close("dV", dv_sum, a[4], 2 * BF16_ABS, BF16_FROB)
+
+
+def test_full_size_own_block_sampled():
+    """Own-block mask at the full c3 size in the bench's configuration (default
+    chunk runs, 256 workgroups), checked against the oracle on one sequence and
+    one KV head."""
+    w = add_own_block(make("c3", seed=0))
+    path = make_path(w, DEV, mask="own_block", fwd_runs_per_worker=4)
+    q, k, v = _upload(w)
+    ko, vo = _own_upload(w)
+    do = to_device(w, "do", DEV)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dko, dvo = torch.empty_like(ko), torch.empty_like(vo)
+    path.forward(q, k, v, k_own=ko, v_own=vo)
+    path.backward(q, k, v, do, dq, dk, dv, own=(ko, vo, dko, dvo))
+    torch.cuda.synchronize()
+    s, g = 0, 1
+    G = w.cfg.hq // w.cfg.hkv
+    hs = list(range(g * G, (g + 1) * G))
+    qs = slice(int(w.q_off[s]), int(w.q_off[s + 1]))
+    ks = slice(int(w.kv_off[s]), int(w.kv_off[s + 1]))
+    f = w.as_f64
+    rq, rk, rv, rko, rvo, O, L = oracle.attention_own_bwd(
+        f("q", rows=qs), f("k", rows=ks), f("v", rows=ks), f("k_own", rows=qs), f("v_own", rows=qs),
+        w.seq_anchors(s), w.cfg.block, w.sm_scale, f("do", rows=qs), kv_heads=[g])
+    assert_close("O", to_np64(path.o)[qs][:, hs], O[:, hs], BF16_ABS, BF16_FROB)
+    assert_lse("LSE", to_np64(path.lse)[qs][:, hs], L[:, hs], BF16_LSE_REL)
+    assert_close("dQ", to_np64(dq)[qs][:, hs], rq[:, hs], BF16_ABS, BF16_FROB)
+    assert_close("dK", to_np64(dk)[ks][:, g], rk[:, g], BF16_ABS, BF16_FROB)
+    assert_close("dV", to_np64(dv)[ks][:, g], rv[:, g], BF16_ABS, BF16_FROB)
+    assert_close("dK_own", to_np64(dko)[qs][:, g], rko[:, g], BF16_ABS, BF16_FROB)
+    assert_close("dV_own", to_np64(dvo)[qs][:, g], rvo[:, g], BF16_ABS, BF16_FROB)
