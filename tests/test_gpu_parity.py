@@ -482,3 +482,40 @@ def test_full_size_own_block_sampled():
     assert_close("dV", to_np64(dv)[ks][:, g], rv[:, g], BF16_ABS, BF16_FROB)
     assert_close("dK_own", to_np64(dko)[qs][:, g], rko[:, g], BF16_ABS, BF16_FROB)
     assert_close("dV_own", to_np64(dvo)[qs][:, g], rvo[:, g], BF16_ABS, BF16_FROB)
+
+
+@pytest.mark.parametrize("mask", ["prefix", "own_block"])
+def test_bf16_edge_sequences_both_masks(mask):
+    """An empty context (its rows see nothing under the prefix mask, only their
+    own keys under the own-block mask), anchors at 0, duplicated and at N - 1,
+    a context shorter than one tile; forward with chunk runs, then backward."""
+    w = make_custom([0, 1000, 50], [[0, 0, 0, 0], [0, 0, 500, 999], [0, 10, 20, 49]], block=16, hq=8, hkv=2,
+                    d=128, dtype="bf16", chunk=128, seed=31, with_do=True)
+    if mask == "own_block":
+        add_own_block(w)
+    path = make_path(w, DEV, with_bwd=True, mask=mask, n_workers=16, fwd_runs_per_worker=2,
+                     fwd_run_imbalance=None)
+    q, k, v = _upload(w)
+    do = to_device(w, "do", DEV)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    if mask == "own_block":
+        ko, vo = _own_upload(w)
+        dko, dvo = torch.empty_like(ko), torch.empty_like(vo)
+        path.forward(q, k, v, k_own=ko, v_own=vo)
+        path.backward(q, k, v, do, dq, dk, dv, own=(ko, vo, dko, dvo))
+        torch.cuda.synchronize()
+        O, L = oracle.attention_own_workload(w)
+        rq, rk, rv, rko, rvo = oracle.bwd_own_workload(w)
+        assert_close("dK_own", to_np64(dko), rko, BF16_ABS, BF16_FROB)
+        assert_close("dV_own", to_np64(dvo), rvo, BF16_ABS, BF16_FROB)
+    else:
+        path.forward(q, k, v)
+        path.backward(q, k, v, do, dq, dk, dv)
+        torch.cuda.synchronize()
+        O, L = oracle.attention_workload(w)
+        rq, rk, rv = oracle.bwd_workload(w)[:3]
+        assert np.all(to_np64(path.lse)[:64] == -np.inf) and np.all(to_np64(path.o)[:64] == 0)
+    _check_merged(path, w, O, L)
+    assert_close("dQ", to_np64(dq), rq, BF16_ABS, BF16_FROB)
+    assert_close("dK", to_np64(dk), rk, BF16_ABS, BF16_FROB)
+    assert_close("dV", to_np64(dv), rv, BF16_ABS, BF16_FROB)
