@@ -63,8 +63,7 @@ extern "C" int sparse_attn_partial_fwd(const skv_problem* p, const skv_plan* pla
     part_rows += n_partials(p, v.n) * p->hq * v.mq;
   }
   hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e = launch_claim_reset(plan->d_claim, plan->n_workers, st);
-  if (e == hipSuccess) e = launch_fill_neg_inf(m_part, lse_part, part_rows, st);
+  hipError_t e = launch_fill_neg_inf(m_part, lse_part, part_rows, plan->d_claim, plan->n_workers, st);
   if (e != hipSuccess) return hip_status(e, "sparse_attn_partial_fwd launch");
   e = p->dtype == SKV_BF16 ? launch_fwd_bf16(a, plan->n_workers, st)
                                       : launch_fwd_f32(a, p->d, plan->n_workers, st);
@@ -231,8 +230,8 @@ extern "C" int sparse_attn_bwd(const skv_problem* p, const skv_plan* plan_kv, co
   a.fd_block = FastDiv::make(a.block); a.fd_group = FastDiv::make(a.group); a.fd_gb = FastDiv::make(a.block * a.group);
   a.sm_scale = p->sm_scale; a.scale_log2 = p->sm_scale * kLog2e_host;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e = launch_claim_reset(plan_kv->d_claim, plan_kv->n_workers, st);
-  if (e == hipSuccess) e = launch_claim_reset(plan_q->d_claim, plan_q->n_workers, st);
-  if (e == hipSuccess) e = launch_bwd_bf16(a, plan_kv->n_workers, plan_q->n_workers, st);
+  a.kv_claim_n = plan_kv->n_workers;
+  a.q_claim_n = plan_q->n_workers;
+  hipError_t e = launch_bwd_bf16(a, plan_kv->n_workers, plan_q->n_workers, st);
   return hip_status(e, "sparse_attn_bwd launch");
 }

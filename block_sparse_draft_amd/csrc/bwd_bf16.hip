@@ -41,11 +41,32 @@ constexpr int LDS_ROW = D + 8;   // bf16 per staged row (272 bytes: conflict-fre
 // 1. preprocess
 // ---------------------------------------------------------------------------
 
+// First partial row of every sequence: part_base[s] = sum_{s' < s} P_s' * hq * Mq_s',
+// P_s = C_s partials, plus the own-block partial under the own-block mask.
+__device__ void part_base_all(const BwdArgs& a) {
+  int64_t base = 0;
+  for (int s = 0; s < a.n_seq; ++s) {
+    a.part_base[s] = base;
+    const int64_t n = a.kv_off[s + 1] - a.kv_off[s];
+    base += ((n + a.chunk - 1) / a.chunk + a.own) * a.hq * (a.q_off[s + 1] - a.q_off[s]);
+  }
+  a.part_base[a.n_seq] = base;
+}
+
 // Packed copies for the two main kernels (16 lanes per (token, head), 8 bf16
 // each): Q and dO rows, LSE in log2 units, Delta = sum_x dO * O (from the
 // merged O in bf16) and the prefix end of the row's draft block, all at the
 // row's packed index.
+//
+// The launch also resets both plans' claim cursors and, in one thread, finds
+// the first partial row of every sequence (the dQ partial layout).
 __global__ __launch_bounds__(256) void bwd_pack_kernel(BwdArgs a) {
+  {
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t < a.kv_claim_n) a.kv_claim[t] = 0;
+    if (t < a.q_claim_n) a.q_claim[t] = 0;
+    if (t == 0) part_base_all(a);
+  }
   const int64_t idx = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
   const int ln = threadIdx.x & 15;
   const int64_t n = a.total_q * a.hq;
@@ -85,19 +106,6 @@ __global__ __launch_bounds__(256) void bwd_pack_kernel(BwdArgs a) {
     a.lsep[P] = a.lse[idx] * kLog2e;
     a.endp[P] = min(a.anchor[q0 / a.block + b] + a.end_shift, n_ctx);
   }
-}
-
-// First partial row of every sequence: part_base[s] = sum_{s' < s} P_s' * hq * Mq_s',
-// P_s = C_s partials, plus the own-block partial under the own-block mask.
-__global__ void part_base_kernel(BwdArgs a) {
-  if (threadIdx.x != 0 || blockIdx.x != 0) return;
-  int64_t base = 0;
-  for (int s = 0; s < a.n_seq; ++s) {
-    a.part_base[s] = base;
-    const int64_t n = a.kv_off[s + 1] - a.kv_off[s];
-    base += ((n + a.chunk - 1) / a.chunk + a.own) * a.hq * (a.q_off[s + 1] - a.q_off[s]);
-  }
-  a.part_base[a.n_seq] = base;
 }
 
 // ---------------------------------------------------------------------------
@@ -606,13 +614,12 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, int kv_workers, int q_workers, hipS
   const int64_t rows = a.total_q * a.hq;
   hipError_t e;
   {
-    TimedLaunch t(kBwdPartBase, stream);
-    hipLaunchKernelGGL(part_base_kernel, dim3(1), dim3(64), 0, stream, a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-  }
-  if (rows > 0) {
+    // Packed copies, claim cursor resets and partial offsets in one launch
+    // (at least one workgroup even without query rows).
+    const int64_t claims = std::max(a.kv_claim_n, a.q_claim_n);
+    const int64_t blocks = std::max<int64_t>(std::max<int64_t>((rows + 15) / 16, (claims + 255) / 256), 1);
     TimedLaunch t(kBwdPack, stream);
-    hipLaunchKernelGGL(bwd_pack_kernel, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(bwd_pack_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   {

@@ -324,15 +324,14 @@ void fwd_bf16_kernel(FwdArgs a) {
   record_ticks(a.ticks, me, t_start);
 }
 
-// Resets the per-worker claim cursors of a plan before a launch.
-__global__ void claim_reset_kernel(int32_t* claim, int n) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) claim[i] = 0;
-}
-
-// m = lse = -inf for every partial row (rows of items left out of a plan).
-__global__ __launch_bounds__(256) void fill_neg_inf_kernel(float* m, float* lse, int64_t n) {
-  const int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+// m = lse = -inf for every partial row (rows of items left out of a plan);
+// the plan's claim cursors are reset in the same launch.
+__global__ __launch_bounds__(256) void fill_neg_inf_kernel(float* m, float* lse, int64_t n, int32_t* claim,
+                                                           int n_claim) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t < n_claim) claim[t] = 0;
+  const int64_t i = t * 4;
+  if (i >= n) return;
   const f32x4 v = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
   if (i + 4 <= n && ((reinterpret_cast<uintptr_t>(m) | reinterpret_cast<uintptr_t>(lse)) & 15) == 0) {
     *reinterpret_cast<f32x4*>(m + i) = v;
@@ -344,16 +343,12 @@ __global__ __launch_bounds__(256) void fill_neg_inf_kernel(float* m, float* lse,
 
 }  // namespace
 
-hipError_t launch_claim_reset(int32_t* claim, int n_workers, hipStream_t stream) {
-  TimedLaunch t(kClaimReset, stream);
-  hipLaunchKernelGGL(claim_reset_kernel, dim3((n_workers + 255) / 256), dim3(256), 0, stream, claim, n_workers);
-  return hipGetLastError();
-}
 
-hipError_t launch_fill_neg_inf(float* m, float* lse, int64_t n, hipStream_t stream) {
-  if (n <= 0) return hipSuccess;
+hipError_t launch_fill_neg_inf(float* m, float* lse, int64_t n, int32_t* claim, int n_claim, hipStream_t stream) {
+  const int64_t blocks = std::max<int64_t>((n + 1023) / 1024, (n_claim + 255) / 256);
+  if (blocks == 0) return hipSuccess;
   TimedLaunch t(kFillPartials, stream);
-  hipLaunchKernelGGL(fill_neg_inf_kernel, dim3((unsigned)((n + 1023) / 1024)), dim3(256), 0, stream, m, lse, n);
+  hipLaunchKernelGGL(fill_neg_inf_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, m, lse, n, claim, n_claim);
   return hipGetLastError();
 }
 

@@ -90,6 +90,7 @@ struct BwdArgs {
   int32_t* q_claim;
   int64_t* q_ticks;
   int32_t kv_steal, q_steal;
+  int32_t kv_claim_n, q_claim_n;  // claim cursors reset by the first launch of the backward
   int64_t total_q;  // sum Mq
   int32_t n_seq, block, group, hq, hkv, chunk;
   int32_t end_shift;  // e_b = min(a_b + end_shift, N): block (prefix mask) or 0 (own-block mask)
@@ -103,8 +104,7 @@ struct BwdArgs {
   float sm_scale, scale_log2;
 };
 
-hipError_t launch_claim_reset(int32_t* claim, int n_workers, hipStream_t stream);
-hipError_t launch_fill_neg_inf(float* m, float* lse, int64_t n, hipStream_t stream);
+hipError_t launch_fill_neg_inf(float* m, float* lse, int64_t n, int32_t* claim, int n_claim, hipStream_t stream);
 hipError_t launch_fwd_bf16(const FwdArgs& a, int n_workers, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdArgs& a, int d, int n_workers, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, int d, hipStream_t stream);

@@ -12,8 +12,8 @@
 namespace skv {
 namespace {
 
-const char* const kNames[kNumKernels] = {"claim_reset", "fill_partials", "partial_fwd_bf16", "partial_fwd_f32", "lse_merge",
-                                         "bwd_part_base", "bwd_pack", "bwd_kv", "bwd_dq", "bwd_finalize",
+const char* const kNames[kNumKernels] = {"fill_partials", "partial_fwd_bf16", "partial_fwd_f32", "lse_merge",
+                                         "bwd_pack", "bwd_kv", "bwd_dq", "bwd_finalize",
                                          "own_fwd", "own_bwd"};
 
 struct Pending {

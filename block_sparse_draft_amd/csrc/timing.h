@@ -5,7 +5,7 @@
 namespace skv {
 
 enum KernelId {
-  kClaimReset, kFillPartials, kFwdBf16, kFwdF32, kMerge, kBwdPartBase, kBwdPack, kBwdKv, kBwdDq, kBwdFinalize,
+  kFillPartials, kFwdBf16, kFwdF32, kMerge, kBwdPack, kBwdKv, kBwdDq, kBwdFinalize,
   kOwnFwd, kOwnBwd, kNumKernels
 };
 

@@ -24,10 +24,47 @@ RUN_IMBALANCE = 0.02        # LPT cost imbalance accepted for chunk runs
 MAX_RUNS_PER_WORKER = 64
 
 
+def _align256(n: int) -> int:
+    return (n + 255) & ~255
+
+
+class _Staging:
+    """Two pinned-host / device buffer pairs shared by the step's plans: each
+    step's plans are packed into one pair and uploaded with a single
+    asynchronous copy on the compute stream, while the previous step's kernels
+    may still read the other pair."""
+
+    def __init__(self, nbytes: int, device):
+        import torch
+        self.slots = [{"h": torch.empty(max(nbytes, 256), dtype=torch.uint8, pin_memory=True),
+                       "d": torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device),
+                       "event": torch.cuda.Event(), "used": False} for _ in range(2)]
+        self.next = 0
+
+    def upload(self, parts):
+        """Copy the numpy arrays ``parts`` (256-byte aligned, in order) to the
+        device; returns their device addresses."""
+        slot = self.slots[self.next]
+        self.next ^= 1
+        if slot["used"]:
+            slot["event"].synchronize()   # its previous upload has left the pinned buffer
+        h = slot["h"].numpy()
+        pos, ptrs = 0, []
+        for a in parts:
+            b = np.ascontiguousarray(a).view(np.uint8).reshape(-1)
+            h[pos:pos + len(b)] = b
+            ptrs.append(slot["d"].data_ptr() + pos)
+            pos = _align256(pos + len(b))
+        slot["d"][:pos].copy_(slot["h"][:pos], non_blocking=True)
+        slot["event"].record()
+        slot["used"] = True
+        return ptrs
+
+
 class _PlanSlots:
-    """Two pinned-host / device buffer pairs for one kind of plan, so that the
-    next step's plan uploads (asynchronously, on the compute stream) while the
-    previous step's kernels may still read the other pair."""
+    """One kind of plan: its items, claim cursors and optional busy-time
+    counters; the host arrays it builds each step go to the device through the
+    step's shared staging buffer (_Staging)."""
 
     def __init__(self, problem: B.Problem, kind: int, granule: int, n_workers: int, policy: str,
                  steal: bool = True, ticks: bool = False, runs_per_worker: Optional[float] = None,
@@ -43,26 +80,21 @@ class _PlanSlots:
         n = len(problem.item_table(kind, granule)[1])
         dev = problem.device
         self.n_items = n
-        self.slots = []
-        for _ in range(2):
-            self.slots.append({
-                "h_items": torch.empty(max(n, 1) * B.ITEM_DTYPE.itemsize, dtype=torch.uint8, pin_memory=True),
-                "h_off": torch.empty(n_workers + 1, dtype=torch.int64, pin_memory=True),
-                "d_items": torch.empty(max(n, 1) * B.ITEM_DTYPE.itemsize, dtype=torch.uint8, device=dev),
-                "d_off": torch.empty(n_workers + 1, dtype=torch.int64, device=dev),
-                "event": torch.cuda.Event(), "used": False})
+        # staging bytes this plan needs at most: items, then worker offsets
+        self.stage_bytes = _align256(max(n, 1) * B.ITEM_DTYPE.itemsize) + _align256((n_workers + 1) * 8)
         self.claim = torch.zeros(n_workers, dtype=torch.int32, device=dev)  # reset by the library per call
         # per-workgroup busy time (100 MHz ticks) of the last call, when asked for
         self.ticks = torch.zeros(n_workers, dtype=torch.int64, device=dev) if ticks else None
-        self.next = 0
         self.plan_s = 0.0
         self.c = None
         self.load = self.cost = None
         self.table = None
+        self.worker_off = None
 
-    def replan(self):
-        """Realized costs -> LPT (or static) plan -> async upload.  Returns the skv_plan.
-        ``plan_s`` receives the host planning time (cost model, plan, gather)."""
+    def build(self):
+        """Realized costs -> LPT (or static) plan.  Returns the host arrays to
+        upload (items in plan order, worker offsets); ``plan_s`` receives the
+        host planning time (cost model, plan, gather)."""
         import time
         t0 = time.perf_counter()
         items, cost, tok, total = self.problem.item_table(self.kind, self.granule)
@@ -96,23 +128,17 @@ class _PlanSlots:
         if self.kind == B.SKV_ITEM_FWD:
             # empty forward items only mark rows -inf, which the forward call does for all rows
             order, off = B.skv_drop_zero_cost(cost, order, off)
-        gathered = B.skv_gather_items(items, order).view(np.uint8)
+        gathered = B.skv_gather_items(items, order)
         self.plan_s = time.perf_counter() - t0
-        slot = self.slots[self.next]
-        self.next ^= 1
-        if slot["used"]:
-            slot["event"].synchronize()   # its previous upload has left the pinned buffer
-        slot["h_items"].numpy()[:len(gathered)] = gathered
-        slot["h_off"].numpy()[:] = off
-        slot["d_items"].copy_(slot["h_items"], non_blocking=True)
-        slot["d_off"].copy_(slot["h_off"], non_blocking=True)
-        slot["event"].record()
-        slot["used"] = True
         self.cost, self.load = cost, load
         self.n_planned = len(order)
-        self.c = B.skv_plan(self.kind, self.n_workers, len(order), slot["d_items"].data_ptr(),
-                            slot["d_off"].data_ptr(), self.claim.data_ptr(), self.flags, 0,
-                            None if self.ticks is None else self.ticks.data_ptr())
+        self.worker_off = off
+        return [gathered, np.asarray(off, dtype=np.int64)]
+
+    def bind(self, d_items: int, d_off: int):
+        """The skv_plan of the arrays uploaded to d_items / d_off."""
+        self.c = B.skv_plan(self.kind, self.n_workers, self.n_planned, d_items, d_off, self.claim.data_ptr(),
+                            self.flags, 0, None if self.ticks is None else self.ticks.data_ptr())
         return self.c
 
     @property
@@ -167,6 +193,8 @@ class SplitKVAttention:
         self.dq_plan = (_PlanSlots(self.problem, B.SKV_ITEM_FWD, self.fwd_granule, self.n_workers, policy, **kw,
                                    runs_per_worker=self.fwd_runs_per_worker, run_imbalance=fwd_run_imbalance)
                         if with_bwd else None)
+        self.staging = _Staging(sum(p.stage_bytes for p in (self.fwd_plan, self.bwd_plan, self.dq_plan)
+                                    if p is not None), self.device)
         self.replan()
         self.part_base, self.n_chunk = self.problem.partial_layout()
         rows = int(self.part_base[-1])
@@ -183,13 +211,16 @@ class SplitKVAttention:
 
     # -- steps -------------------------------------------------------------
     def replan(self):
-        """Mask descriptor -> realized cost per item -> LPT plan, uploaded for the next kernels."""
-        self.fwd_plan.replan()
-        self.plan_s = self.fwd_plan.plan_s
-        if self.bwd_plan is not None:
-            self.bwd_plan.replan()
-            self.dq_plan.replan()
-            self.plan_s += self.bwd_plan.plan_s + self.dq_plan.plan_s
+        """Mask descriptor -> realized cost per item -> LPT plans, uploaded
+        together (one copy) for the next kernels."""
+        plans = [self.fwd_plan] + ([self.bwd_plan, self.dq_plan] if self.bwd_plan is not None else [])
+        parts = []
+        for p in plans:
+            parts += p.build()
+        ptrs = self.staging.upload(parts)
+        for i, p in enumerate(plans):
+            p.bind(ptrs[2 * i], ptrs[2 * i + 1])
+        self.plan_s = sum(p.plan_s for p in plans)
 
     def partial_fwd(self, q, k, v, stream=None, k_own=None, v_own=None):
         B.sparse_attn_partial_fwd(self.problem, self.fwd_plan, q, k, v, self.o_part, self.m_part, self.lse_part,

@@ -315,8 +315,10 @@ int sparse_attn_bwd(const skv_problem* p, const skv_plan* plan_kv, const skv_pla
  * the number of launches and their summed event-to-event time into
  * out[0 .. min(max_entries, *n_entries)) and resets the tallies; *n_entries
  * receives the number of kernels with at least one launch.  Kernel names:
- * "claim_reset", "fill_partials", "partial_fwd_bf16", "partial_fwd_f32", "lse_merge",
- * "bwd_part_base", "bwd_pack", "bwd_kv", "bwd_dq", "bwd_finalize", "own_fwd", "own_bwd". */
+ * "fill_partials" (also resets the forward plan's claim cursors), "partial_fwd_bf16",
+ * "partial_fwd_f32", "lse_merge", "bwd_pack" (also resets the backward plans'
+ * claim cursors and finds the partial offsets), "bwd_kv", "bwd_dq",
+ * "bwd_finalize", "own_fwd", "own_bwd". */
 typedef struct skv_kernel_time {
   const char* name;   /* static string */
   int64_t launches;

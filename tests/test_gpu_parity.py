@@ -348,7 +348,7 @@ def test_backward_bitwise_deterministic_across_plans_and_stealing():
         if kw.get("ticks"):
             for plan in (path.fwd_plan, path.bwd_plan, path.dq_plan):
                 t = plan.ticks.cpu().numpy()
-                busy = np.diff(plan.slots[(plan.next + 1) % 2]["h_off"].numpy()) > 0
+                busy = np.diff(plan.worker_off) > 0
                 assert (t >= 0).all() and (t[busy] > 0).all()
 
 
