@@ -61,6 +61,36 @@ def test_c1_fp32_partials_and_merge(seed):
     _check_merged(path, w, O, L, abs_tol=F32_ABS, frob_tol=None, lse_tol=F32_ABS)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_c1_fp32_chunk_runs(d):
+    """The fp32 forward over chunk runs (one partial per run): merged output,
+    each run's partial against the oracle's merge of its chunks."""
+    w = make("c1", seed=5, d=d, n_ctx=2048, n_anchor=8, chunk=128)
+    path = make_path(w, DEV, n_workers=4, fwd_runs_per_worker=1, fwd_run_imbalance=None)
+    q, k, v = _upload(w)
+    path.forward(q, k, v)
+    torch.cuda.synchronize()
+    O, L = oracle.attention_workload(w)
+    _check_merged(path, w, O, L, abs_tol=F32_ABS, frob_tol=None, lse_tol=F32_ABS)
+    items, cost = path.fwd_plan.table
+    assert (items["n_chunk"] > 1).any()
+    op, mp, lp = oracle.partials_workload(w, 0)
+    go, gm, gl = [to_np64(t) for t in path.partial_view(0)]
+    G, B = w.cfg.hq // w.cfg.hkv, w.cfg.block
+    for it, c in zip(items, cost):
+        if c == 0:
+            continue
+        g, c0, n = int(it["kv_head"]), int(it["chunk"]), int(it["n_chunk"])
+        rows, hs = slice(int(it["lo"]) * B, int(it["hi"]) * B), slice(g * G, (g + 1) * G)
+        ro, rl = oracle.lse_merge(op[c0:c0 + n, hs, rows], mp[c0:c0 + n, hs, rows], lp[c0:c0 + n, hs, rows])
+        assert_lse("run lse", gl[c0, hs, rows].T, rl, F32_ABS)
+        vis = np.isfinite(rl)
+        with np.errstate(invalid="ignore"):
+            gn = go[c0, hs, rows] * np.exp(np.where(vis.T, gm[c0, hs, rows] - gl[c0, hs, rows], 0.0))[..., None]
+        assert_close("run o", gn.transpose(1, 0, 2)[vis], ro[vis], F32_ABS)
+        assert np.all(gl[c0 + 1:c0 + n, hs, rows] == -np.inf)
+
+
 def test_fp32_head_dim_128_ragged():
     w = make("c1", seed=3, n_ctx=777, d=128, hq=4, hkv=2, chunk=192)
     path = make_path(w, DEV)
