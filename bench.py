@@ -357,7 +357,7 @@ def main():
                    "fwd_runs_per_worker": path.fwd_runs_per_worker, "mask": args.mask},
         "pct_of_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "fwd": {"ms": round(fwd_ms, 4), "tflops": round(fwd_tf, 2), "frac": round(fwd_tf / PEAK_BF16_TFLOPS, 4)},
-        "merge": {"ms": round(mrg_ms, 4), "launches": c.n_seq, "bytes": mbytes, "gbs": round(merge_gbs, 1),
+        "merge": {"ms": round(mrg_ms, 4), "launches": 1, "bytes": mbytes, "gbs": round(merge_gbs, 1),
                   "frac": round(merge_gbs / PEAK_HBM_GBS, 4)},
         "bwd": {"ms": round(bwd_ms, 4), "tflops": round(bwd_tf, 2), "frac": round(bwd_tf / PEAK_BF16_TFLOPS, 4)}
         if with_bwd else None,

@@ -95,6 +95,7 @@ def _load():
         "sparse_attn_bwd": (C.c_int, [P(skv_problem), P(skv_plan), P(skv_plan)] + [VP] * 10 +
                             [C.c_size_t, P(skv_own_block), VP]),
         "sparse_attn_own_fwd": (C.c_int, [P(skv_problem), VP, VP, VP, I64, I64, VP, VP, VP, VP]),
+        "lse_merge_all": (C.c_int, [P(skv_problem), VP, VP, VP, VP, VP, VP, VP]),
         "skv_timing_enable": (C.c_int, [I32]),
         "skv_timing_collect": (C.c_int, [P(skv_kernel_time), I32, P(I32)]),
     }
@@ -107,7 +108,7 @@ def _load():
 lib = _load()
 EXPORTED = ("skv_last_error", "skv_check_problem", "skv_partial_layout", "skv_item_table", "lpt_plan",
             "skv_static_plan", "skv_gather_items", "skv_drop_zero_cost", "skv_coarsen_fwd_items",
-            "sparse_attn_partial_fwd", "lse_merge",
+            "sparse_attn_partial_fwd", "lse_merge", "lse_merge_all",
             "skv_bwd_workspace_bytes", "sparse_attn_bwd", "sparse_attn_own_fwd", "skv_timing_enable",
             "skv_timing_collect")
 
@@ -326,6 +327,12 @@ def lse_merge(n_part: int, hq: int, mq: int, d: int, o_part, m_part, lse_part, o
                          _ptr(lse_part) + part_offset * 4,
                          _ptr(o_out) + out_offset * o_stride_tok * ob, o_stride_tok, o_stride_head, out_dtype,
                          _ptr(lse_out) + lse_offset * 4, lse_stride_tok, _stream(stream)))
+
+
+def lse_merge_all(problem: Problem, d_part_base, o_part, m_part, lse_part, o_out, lse_out, stream=None):
+    """Merge every sequence's partials in one launch (d_part_base: device part_base)."""
+    _check(lib.lse_merge_all(C.byref(problem.c), _ptr(d_part_base), _ptr(o_part), _ptr(m_part), _ptr(lse_part),
+                             _ptr(o_out), _ptr(lse_out), _stream(stream)))
 
 
 def _own_strides(t):

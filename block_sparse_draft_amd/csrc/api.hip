@@ -136,6 +136,28 @@ extern "C" int lse_merge(int32_t n_part, int32_t hq, int64_t mq, int32_t d, cons
   return hip_status(launch_merge(a, d, static_cast<hipStream_t>(stream)), "lse_merge launch");
 }
 
+extern "C" int lse_merge_all(const skv_problem* p, const int64_t* d_part_base, const float* o_part,
+                             const float* m_part, const float* lse_part, void* o_out, float* lse_out,
+                             void* stream) {
+  int rc = skv_check_problem(p);
+  if (rc) return rc;
+  if ((rc = check_device_problem(p))) return rc;
+  const int64_t rows = p->h_q_off[p->n_seq];
+  if (rows == 0) { clear_error(); return SKV_OK; }
+  if (!d_part_base || !o_part || !m_part || !lse_part || !o_out || !lse_out)
+    return fail(SKV_EINVAL, "tensor pointer is NULL");
+  if (!aligned16(o_part) || (reinterpret_cast<uintptr_t>(o_out) & 7u))
+    return fail(SKV_ESHAPE, "o_part must be 16-byte and o_out 8-byte aligned");
+  if (rows > (int64_t)INT32_MAX * 32) return fail(SKV_ESHAPE, "too many rows");
+  MergeArgs a{};
+  a.o_part = o_part; a.m_part = m_part; a.lse_part = lse_part;
+  a.o_out = o_out; a.lse_out = lse_out;
+  a.mq = rows; a.o_st = p->q_stride_tok; a.o_sh = p->q_stride_head; a.lse_st = p->hq;
+  a.hq = p->hq; a.out_bf16 = p->dtype == SKV_BF16;
+  a.q_off = p->d_q_off; a.part_base = d_part_base; a.n_seq = p->n_seq;
+  return hip_status(launch_merge(a, p->d, static_cast<hipStream_t>(stream)), "lse_merge_all launch");
+}
+
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Workspace of sparse_attn_bwd: dQ partials (the forward's partial layout);

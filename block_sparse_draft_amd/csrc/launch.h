@@ -53,8 +53,14 @@ struct MergeArgs {
   const float* lse_part;
   void* o_out;
   float* lse_out;
-  int64_t mq, o_st, o_sh, lse_st;
+  int64_t mq, o_st, o_sh, lse_st;  // mq: rows (all sequences' rows when n_seq > 0)
   int32_t n_part, hq, out_bf16;
+  // n_seq > 0: rows of several sequences, row t of sequence s (q_off) with
+  // its partials at part_base[s] + c*hq*Mq_s + h*Mq_s + (t - q_off[s]);
+  // n_seq = 0: one sequence, n_part partials at c*hq*mq + h*mq + t.
+  const int64_t* q_off;
+  const int64_t* part_base;
+  int32_t n_seq;
 };
 
 struct BwdArgs {

@@ -40,27 +40,60 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   __shared__ float sW[MROWS][CBLK];       // nonzero weights of the block, per row, ascending partial
   __shared__ int sC[MROWS][CBLK];         // their partial index
   __shared__ int sN[MROWS];
+  __shared__ int64_t sBase[MROWS];        // first partial row of each row, and the partial stride
+  __shared__ int64_t sStride[MROWS];
+  __shared__ int sNp[MROWS];              // partials of each row's sequence
+  __shared__ int sMaxNp;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int h = blockIdx.y;
   const int64_t r0 = (int64_t)blockIdx.x * MROWS;
-  const int64_t hm = (int64_t)h * a.mq;
-  const int64_t pstride = (int64_t)a.hq * a.mq;  // rows between consecutive partials
+
+  // ---- each row's partial layout (its sequence, when rows of several sequences are merged) ----
+  if (tid < 64) {
+    int np = -1;
+    if (tid < MROWS && r0 + tid < a.mq) {
+      const int64_t t = r0 + tid;
+      if (a.n_seq == 0) {
+        sBase[tid] = (int64_t)h * a.mq + t;
+        sStride[tid] = (int64_t)a.hq * a.mq;
+        np = a.n_part;
+      } else {
+        int lo = 0, hi = a.n_seq;  // sequence of row t: q_off[lo] <= t < q_off[lo + 1]
+        while (hi - lo > 1) {
+          const int mid = (lo + hi) >> 1;
+          if (a.q_off[mid] <= t) lo = mid; else hi = mid;
+        }
+        const int64_t q0 = a.q_off[lo], mqs = a.q_off[lo + 1] - q0;
+        const int64_t stride = (int64_t)a.hq * mqs;
+        sBase[tid] = a.part_base[lo] + (int64_t)h * mqs + (t - q0);
+        sStride[tid] = stride;
+        np = (int)((a.part_base[lo + 1] - a.part_base[lo]) / stride);
+      }
+    }
+    if (tid < MROWS) sNp[tid] = np < 0 ? 0 : np;
+    const int mx = wave_max_i(np);
+    if (tid == 0) sMaxNp = mx < 0 ? 0 : mx;
+  }
+  __syncthreads();
+  const int max_np = sMaxNp;
   const int ra = tid / LPRA, pa = tid % LPRA;    // steps A, B: row, lane within the row
   const int64_t rowa = r0 + ra;
   const bool live_a = rowa < a.mq;
+  const int64_t base_a = sBase[ra], stride_a = sStride[ra];
+  const int np_a = sNp[ra];
 
   // ---- step A: merged LSE of each row ----
   {
     float mx = -INFINITY, sum = 0.f;
     if (live_a) {
-      for (int c0 = pa; c0 < a.n_part; c0 += 4 * LPRA) {
+      for (int c0 = pa; c0 < np_a; c0 += 4 * LPRA) {
         float x[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const int c = c0 + u * LPRA;
-          x[u] = c < a.n_part ? a.lse_part[c * pstride + hm + rowa] : -INFINITY;
+          x[u] = c < np_a ? a.lse_part[base_a + c * stride_a] : -INFINITY;
         }
 #pragma unroll
         for (int u = 0; u < 4; ++u) lse_combine(mx, sum, x[u], 1.f);
@@ -83,7 +116,7 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
 #pragma unroll
   for (int i = 0; i < RPS; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int cb = 0; cb < a.n_part; cb += CBLK) {
+  for (int cb = 0; cb < max_np; cb += CBLK) {
     __syncthreads();  // sLse written; the previous block's lists are consumed
     // ---- step B: this row's nonzero weights among partials [cb, cb + 64) ----
     {
@@ -93,9 +126,9 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
       for (int u = 0; u < CBLK / LPRA; ++u) {
         const int c = cb + u * LPRA + pa;
         float w = 0.f;
-        if (live_a && c < a.n_part && L != -INFINITY) {
-          const float lc = a.lse_part[c * pstride + hm + rowa];
-          if (lc != -INFINITY) w = expf(a.m_part[c * pstride + hm + rowa] - L);
+        if (live_a && c < np_a && L != -INFINITY) {
+          const float lc = a.lse_part[base_a + c * stride_a];
+          if (lc != -INFINITY) w = expf(a.m_part[base_a + c * stride_a] - L);
         }
         const uint64_t bal = __ballot(w != 0.f);
         const uint32_t bits = (uint32_t)(bal >> (lane & ~(LPRA - 1))) & ((1u << LPRA) - 1);
@@ -114,16 +147,17 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
     for (int i = 0; i < RPS; ++i) {
       const int rr = slot * RPS + i;
       const int n = sN[rr];
-      const float* base = a.o_part + (hm + r0 + rr) * D + ln * 4;
+      const float* base = a.o_part + sBase[rr] * D + ln * 4;
+      const int64_t pstride = sStride[rr] * D;
       int k = 0;
       for (; k + 4 <= n; k += 4) {
         f32x4 v[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const f32x4*>(base + (int64_t)sC[rr][k + u] * pstride * D);
+        for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const f32x4*>(base + (int64_t)sC[rr][k + u] * pstride);
 #pragma unroll
         for (int u = 0; u < 4; ++u) acc[i] += sW[rr][k + u] * v[u];
       }
-      for (; k < n; ++k) acc[i] += sW[rr][k] * *reinterpret_cast<const f32x4*>(base + (int64_t)sC[rr][k] * pstride * D);
+      for (; k < n; ++k) acc[i] += sW[rr][k] * *reinterpret_cast<const f32x4*>(base + (int64_t)sC[rr][k] * pstride);
     }
   }
 

@@ -197,6 +197,7 @@ class SplitKVAttention:
                                     if p is not None), self.device)
         self.replan()
         self.part_base, self.n_chunk = self.problem.partial_layout()
+        self.d_part_base = torch.from_numpy(self.part_base).to(self.device)
         rows = int(self.part_base[-1])
         tq = self.problem.total_q
         self.o_part = torch.empty((max(rows, 1), d), dtype=torch.float32, device=self.device)
@@ -231,6 +232,12 @@ class SplitKVAttention:
             B.sparse_attn_own_fwd(self.problem, q, k_own, v_own, self.o_part, self.m_part, self.lse_part, stream)
 
     def merge(self, stream=None):
+        """The exact merge of every sequence's partials, in one launch."""
+        B.lse_merge_all(self.problem, self.d_part_base, self.o_part, self.m_part, self.lse_part, self.o, self.lse,
+                        stream)
+
+    def merge_per_sequence(self, stream=None):
+        """The same merge, one lse_merge call per sequence."""
         p = self.problem
         out_dtype = self.skv_dtype
         for s in range(p.n_seq):

@@ -265,6 +265,15 @@ int lse_merge(int32_t n_part, int32_t hq, int64_t mq, int32_t d, const float* o_
               const float* lse_part, void* o_out, int64_t o_stride_tok, int64_t o_stride_head, int32_t out_dtype,
               float* lse_out, int64_t lse_stride_tok, void* stream);
 
+/* lse_merge of every sequence of a problem in one launch: the partials in
+ * the layout of skv_partial_layout (d_part_base: its part_base array
+ * [n_seq+1], copied to the device by the caller), O written in the problem
+ * dtype with the Q layout, LSE as float [sum Mq][hq].  Per row the same
+ * arithmetic, in the same order, as lse_merge on that row's sequence, so the
+ * results are bitwise equal. */
+int lse_merge_all(const skv_problem* p, const int64_t* d_part_base, const float* o_part, const float* m_part,
+                  const float* lse_part, void* o_out, float* lse_out, void* stream);
+
 /* Bytes of device workspace sparse_attn_bwd needs (256-byte aligned pieces):
  * fp32 dQ partials in the layout of skv_partial_layout ([rows][d]) and an
  * int32 run length per partial row; bf16

@@ -549,3 +549,30 @@ def test_bf16_edge_sequences_both_masks(mask):
     assert_close("dQ", to_np64(dq), rq, BF16_ABS, BF16_FROB)
     assert_close("dK", to_np64(dk), rk, BF16_ABS, BF16_FROB)
     assert_close("dV", to_np64(dv), rv, BF16_ABS, BF16_FROB)
+
+
+@pytest.mark.parametrize("mask", ["prefix", "own_block"])
+def test_merge_all_equals_per_sequence_merge(mask):
+    """The one-launch merge of every sequence gives bitwise the per-sequence
+    lse_merge results (sequences of different lengths, rows straddling
+    workgroup boundaries, a sequence without context)."""
+    w = make_custom([0, 900, 3000], [[0, 5, 9], [3, 300, 880], [10, 1500, 2999]], block=16, hq=8, hkv=2, d=128,
+                    dtype="bf16", chunk=256, seed=41, with_do=False)
+    kw = {}
+    if mask == "own_block":
+        add_own_block(w)
+    path = make_path(w, DEV, mask=mask)
+    q, k, v = _upload(w)
+    if mask == "own_block":
+        kw = dict(zip(("k_own", "v_own"), _own_upload(w)))
+    path.partial_fwd(q, k, v, **kw)
+    path.merge()
+    torch.cuda.synchronize()
+    o1, l1 = path.o.clone(), path.lse.clone()
+    path.o.zero_()
+    path.lse.zero_()
+    path.merge_per_sequence()
+    torch.cuda.synchronize()
+    assert torch.equal(path.o, o1) and torch.equal(path.lse, l1)
+    O, L = oracle.attention_own_workload(w) if mask == "own_block" else oracle.attention_workload(w)
+    _check_merged(path, w, O, L)
