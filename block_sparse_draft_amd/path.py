@@ -163,6 +163,8 @@ class SplitKVAttention:
                  fwd_run_imbalance: Optional[float] = RUN_IMBALANCE):
         import torch
         self.device = torch.device(device)
+        if self.device.type == "cuda" and self.device.index is None:
+            self.device = torch.device("cuda", torch.cuda.current_device())
         self.dtype = dtype
         self.skv_dtype = B.SKV_BF16 if dtype == torch.bfloat16 else B.SKV_F32
         if mask not in ("prefix", "own_block"):
@@ -223,7 +225,22 @@ class SplitKVAttention:
             p.bind(ptrs[2 * i], ptrs[2 * i + 1])
         self.plan_s = sum(p.plan_s for p in plans)
 
+    def _check(self, **tensors):
+        """The problem uses contiguous [rows, heads, d] strides for every tensor."""
+        p = self.problem
+        shapes = {"q": (p.total_q, p.hq, p.d), "dout": (p.total_q, p.hq, p.d), "dq": (p.total_q, p.hq, p.d),
+                  "k": (p.total_kv, p.hkv, p.d), "v": (p.total_kv, p.hkv, p.d), "dk": (p.total_kv, p.hkv, p.d),
+                  "dv": (p.total_kv, p.hkv, p.d)}
+        for name, t in tensors.items():
+            if t is None:
+                continue
+            want = shapes.get(name, (p.total_q, p.hkv, p.d))  # own-block tensors
+            if tuple(t.shape) != want or not t.is_contiguous() or t.dtype != self.dtype or t.device != self.device:
+                raise ValueError(f"{name}: need a contiguous {self.dtype} tensor of shape {want} on {self.device}, "
+                                 f"got {t.dtype} {tuple(t.shape)} on {t.device}")
+
     def partial_fwd(self, q, k, v, stream=None, k_own=None, v_own=None):
+        self._check(q=q, k=k, v=v, k_own=k_own, v_own=v_own)
         B.sparse_attn_partial_fwd(self.problem, self.fwd_plan, q, k, v, self.o_part, self.m_part, self.lse_part,
                                   stream)
         if self.mask == "own_block":
@@ -258,6 +275,8 @@ class SplitKVAttention:
         own-block mask ``own`` = (k_own, v_own, dk_own, dv_own)."""
         if (self.mask == "own_block") != (own is not None):
             raise ValueError("own-block tensors go with the own-block mask")
+        self._check(q=q, k=k, v=v, dout=dout, dq=dq, dk=dk, dv=dv,
+                    **(dict(zip(("k_own", "v_own", "dk_own", "dv_own"), own)) if own is not None else {}))
         B.sparse_attn_bwd(self.problem, self.bwd_plan, self.dq_plan, q, k, v, self.o, self.lse, dout, dq, dk, dv,
                           self.workspace, stream, own=own)
         return dq, dk, dv
