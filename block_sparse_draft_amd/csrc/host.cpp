@@ -9,10 +9,9 @@
 // ("Split-KV's Core Mechanism"; arXiv:2611.05926, Abstract).
 #include <algorithm>
 #include <cmath>
+#include <cstdint>
 #include <cstdio>
-#include <queue>
 #include <string>
-#include <tuple>
 #include <vector>
 
 #include "internal.h"
@@ -118,45 +117,58 @@ extern "C" int skv_item_table(const skv_problem* p, int32_t kind, int32_t granul
     return fail(SKV_EINVAL, "bwd granule = %d is not a multiple of %d", granule, SKV_TILE);
   const int64_t G = p->hq / p->hkv;
   int64_t n = 0, tok = 0, base = 0;
-  std::vector<int64_t> ends;
+  std::vector<int64_t> ends, seq_cost;
   for (int s = 0; s < p->n_seq; ++s) {
     const SeqView v = seq_view(p, s);
     const int64_t C = ceil_div(v.n, p->chunk);
     ends.resize(v.n_blk);
     for (int64_t b = 0; b < v.n_blk; ++b)
       ends[b] = std::min<int64_t>((int64_t)p->h_anchor[v.blk0 + b] + end_shift(p), v.n);
-    for (int g = 0; g < p->hkv; ++g) {
+    // Items per chunk, and the cost of each (chunk, range): the same for every
+    // KV head, so it is computed once per sequence.
+    const int64_t nr_fwd = ceil_div(v.n_blk, granule);
+    const int64_t nr_max = kind == SKV_ITEM_FWD ? nr_fwd : ceil_div(std::min<int64_t>(p->chunk, v.n), granule);
+    if (cost) {
+      seq_cost.assign(C * nr_max, 0);
       for (int64_t c = 0; c < C; ++c) {
         const int64_t lo = c * p->chunk, hi = std::min<int64_t>(lo + p->chunk, v.n);
         if (kind == SKV_ITEM_FWD) {
           const int64_t t0 = lo / SKV_TILE, t1 = ceil_div(hi, SKV_TILE);
-          const int64_t nr = ceil_div(v.n_blk, granule);
-          for (int64_t r = 0; r < nr; ++r) {
+          for (int64_t r = 0; r < nr_fwd; ++r) {
             const int64_t b0 = r * granule, b1 = std::min<int64_t>(b0 + granule, v.n_blk);
-            if (cost) {
-              int64_t sum = 0;
-              for (int64_t b = b0; b < b1; ++b) sum += tiles_seen(ends[b], t0, t1);
-              cost[n] = G * sum;
-            }
-            if (tok_start) tok_start[n] = tok;
-            if (items)
-              items[n] = skv_item{s, g, (int32_t)c, (int32_t)r, base + c * p->hq * v.mq, (int32_t)b0, (int32_t)b1, 1, 0};
-            ++n;
+            int64_t sum = 0;
+            for (int64_t b = b0; b < b1; ++b) sum += tiles_seen(ends[b], t0, t1);
+            seq_cost[c * nr_max + r] = G * sum;
           }
         } else {
           const int64_t nr = ceil_div(hi - lo, granule);
           for (int64_t r = 0; r < nr; ++r) {
             const int64_t klo = lo + r * granule, khi = std::min<int64_t>(klo + granule, hi);
-            if (cost) {
-              const int64_t t0 = klo / SKV_TILE, t1 = ceil_div(khi, SKV_TILE);
-              int64_t sum = 0;
-              for (int64_t b = 0; b < v.n_blk; ++b) sum += tiles_seen(ends[b], t0, t1);
-              cost[n] = G * sum;
-            }
+            const int64_t t0 = klo / SKV_TILE, t1 = ceil_div(khi, SKV_TILE);
+            int64_t sum = 0;
+            for (int64_t b = 0; b < v.n_blk; ++b) sum += tiles_seen(ends[b], t0, t1);
+            seq_cost[c * nr_max + r] = G * sum;
+          }
+        }
+      }
+    }
+    for (int g = 0; g < p->hkv; ++g) {
+      for (int64_t c = 0; c < C; ++c) {
+        const int64_t lo = c * p->chunk, hi = std::min<int64_t>(lo + p->chunk, v.n);
+        const int64_t nr = kind == SKV_ITEM_FWD ? nr_fwd : ceil_div(hi - lo, granule);
+        for (int64_t r = 0; r < nr; ++r) {
+          if (cost) cost[n] = seq_cost[c * nr_max + r];
+          if (kind == SKV_ITEM_FWD) {
+            const int64_t b0 = r * granule, b1 = std::min<int64_t>(b0 + granule, v.n_blk);
+            if (tok_start) tok_start[n] = tok;
+            if (items)
+              items[n] = skv_item{s, g, (int32_t)c, (int32_t)r, base + c * p->hq * v.mq, (int32_t)b0, (int32_t)b1, 1, 0};
+          } else {
+            const int64_t klo = lo + r * granule, khi = std::min<int64_t>(klo + granule, hi);
             if (tok_start) tok_start[n] = tok + (klo - lo);
             if (items) items[n] = skv_item{s, g, (int32_t)c, (int32_t)r, 0, (int32_t)klo, (int32_t)khi, 1, 0};
-            ++n;
           }
+          ++n;
         }
         tok += hi - lo;
       }
@@ -181,6 +193,26 @@ static int write_csr(const std::vector<std::vector<int64_t>>& lists, int64_t* or
   return SKV_OK;
 }
 
+// Stable sort of idx by key(i) ascending (key values in [0, max_key]): LSD
+// radix, 8 bits per pass, so equal keys keep their order in idx.
+template <class Key>
+static void radix_sort_by(std::vector<int64_t>& idx, uint64_t max_key, Key key) {
+  std::vector<int64_t> tmp(idx.size());
+  for (int shift = 0; shift < 64 && (max_key >> shift) != 0; shift += 8) {
+    int64_t cnt[257] = {0};
+    for (int64_t i : idx) ++cnt[((key(i) >> shift) & 255) + 1];
+    for (int d = 0; d < 256; ++d) cnt[d + 1] += cnt[d];
+    for (int64_t i : idx) tmp[cnt[(key(i) >> shift) & 255]++] = i;
+    idx.swap(tmp);
+  }
+}
+
+static int bit_width(uint64_t x) {
+  int b = 0;
+  while (b < 64 && (x >> b) != 0) ++b;
+  return b;
+}
+
 extern "C" int lpt_plan(const int64_t* cost, int64_t n, int32_t n_workers, int32_t* assign, int64_t* order,
                         int64_t* worker_off, int64_t* load) {
   if (n < 0) return fail(SKV_EINVAL, "n = %lld < 0", (long long)n);
@@ -189,26 +221,81 @@ extern "C" int lpt_plan(const int64_t* cost, int64_t n, int32_t n_workers, int32
   for (int64_t i = 0; i < n; ++i)
     if (cost[i] < 0) return fail(SKV_EINVAL, "cost[%lld] < 0", (long long)i);
   // Longest first; equal costs keep ascending item id.
+  int64_t max_cost = 0, total = 0;
+  for (int64_t i = 0; i < n; ++i) {
+    max_cost = std::max(max_cost, cost[i]);
+    total = cost[i] > INT64_MAX - total ? INT64_MAX : total + cost[i];
+  }
   std::vector<int64_t> seq(n);
   for (int64_t i = 0; i < n; ++i) seq[i] = i;
-  std::stable_sort(seq.begin(), seq.end(), [&](int64_t a, int64_t b) { return cost[a] > cost[b]; });
-  // Min-heap of (load, worker): the top is the least-loaded worker, lowest id on ties.
-  using Slot = std::pair<int64_t, int32_t>;
-  std::priority_queue<Slot, std::vector<Slot>, std::greater<Slot>> heap;
-  for (int32_t w = 0; w < n_workers; ++w) heap.push({0, w});
-  std::vector<std::vector<int64_t>> lists(n_workers);
-  std::vector<int64_t> ld(n_workers, 0);
-  for (int64_t i : seq) {
-    Slot top = heap.top();
-    heap.pop();
-    const int32_t w = top.second;
-    if (assign) assign[i] = w;
-    lists[w].push_back(i);
-    ld[w] = top.first + cost[i];
-    heap.push({ld[w], w});
+  radix_sort_by(seq, (uint64_t)max_cost, [&](int64_t i) { return (uint64_t)(max_cost - cost[i]); });
+  // Min-heap of (load, worker): the top is the least-loaded worker, lowest id
+  // on ties.  Each item replaces the top and sifts it down.  When every load
+  // fits, a worker's slot is one integer, load * 2^wb + worker.
+  std::vector<int32_t> owner(n);
+  std::vector<int64_t> count(n_workers + 1, 0);
+  std::vector<int64_t> final_load(n_workers, 0);
+  const int wb = bit_width((uint64_t)(n_workers - 1));
+  const size_t H = (size_t)n_workers;
+  if (wb < 62 && total < (INT64_C(1) << (62 - wb))) {
+    std::vector<uint64_t> heap(H);
+    for (size_t w = 0; w < H; ++w) heap[w] = (uint64_t)w;  // already a heap
+    const uint64_t wmask = (UINT64_C(1) << wb) - 1;
+    for (int64_t i : seq) {
+      uint64_t top = heap[0];
+      owner[i] = (int32_t)(top & wmask);
+      top += (uint64_t)cost[i] << wb;
+      size_t k = 0;
+      for (;;) {
+        size_t c = 2 * k + 1;
+        if (c >= H) break;
+        uint64_t cv = heap[c];
+        if (c + 1 < H && heap[c + 1] < cv) cv = heap[++c];
+        if (cv >= top) break;
+        heap[k] = cv;
+        k = c;
+      }
+      heap[k] = top;
+    }
+    for (uint64_t sl : heap) final_load[sl & wmask] = (int64_t)(sl >> wb);
+  } else {
+    struct Slot {
+      int64_t load;
+      int32_t w;
+      bool operator<(const Slot& o) const { return load < o.load || (load == o.load && w < o.w); }
+    };
+    std::vector<Slot> heap(H);
+    for (size_t w = 0; w < H; ++w) heap[w] = Slot{0, (int32_t)w};
+    for (int64_t i : seq) {
+      Slot top = heap[0];
+      owner[i] = top.w;
+      top.load += cost[i];
+      size_t k = 0;
+      for (;;) {
+        size_t c = 2 * k + 1;
+        if (c >= H) break;
+        if (c + 1 < H && heap[c + 1] < heap[c]) ++c;
+        if (!(heap[c] < top)) break;
+        heap[k] = heap[c];
+        k = c;
+      }
+      heap[k] = top;
+    }
+    for (const Slot& sl : heap) final_load[sl.w] = sl.load;
   }
-  if (load) std::copy(ld.begin(), ld.end(), load);
-  return write_csr(lists, order, worker_off);
+  // CSR by worker; each list keeps the order the items were assigned in.
+  for (int64_t i : seq) ++count[owner[i] + 1];
+  for (int32_t w = 0; w < n_workers; ++w) count[w + 1] += count[w];
+  if (worker_off) std::copy(count.begin(), count.end(), worker_off);
+  if (load) std::copy(final_load.begin(), final_load.end(), load);
+  std::vector<int64_t> pos(count.begin(), count.end() - 1);
+  for (int64_t i : seq) {
+    const int32_t w = owner[i];
+    if (assign) assign[i] = w;
+    if (order) order[pos[w]] = i;
+    ++pos[w];
+  }
+  return SKV_OK;
 }
 
 extern "C" int skv_static_plan(const int64_t* tok_start, int64_t n, int64_t total_tok, int32_t n_workers,
@@ -273,14 +360,29 @@ extern "C" int skv_coarsen_fwd_items(const skv_item* items, const int64_t* cost,
     if (items[i].n_chunk != 1 || cost[i] < 0)
       return fail(SKV_EINVAL, "item %lld: n_chunk %d, cost %lld (single-chunk items with cost >= 0 expected)",
                   (long long)i, items[i].n_chunk, (long long)cost[i]);
-  // group order: (seq, kv_head, lo, hi, chunk), ties by input index
+  // group order: (seq, kv_head, lo, hi, chunk), ties by input index: stable
+  // radix passes from the last field to the first
+  for (int64_t i = 0; i < n; ++i) {
+    const skv_item& t = items[i];
+    if (t.seq < 0 || t.kv_head < 0 || t.lo < 0 || t.hi < 0 || t.chunk < 0)
+      return fail(SKV_EINVAL, "item %lld has a negative field", (long long)i);
+  }
   std::vector<int64_t> idx(n);
   for (int64_t i = 0; i < n; ++i) idx[i] = i;
-  auto key = [&](int64_t i) {
-    const skv_item& t = items[i];
-    return std::make_tuple(t.seq, t.kv_head, t.lo, t.hi, t.chunk, i);
+  std::vector<uint32_t> field(n);
+  auto by = [&](int32_t skv_item::*f) {
+    uint64_t mx = 0;
+    for (int64_t i = 0; i < n; ++i) {
+      field[i] = (uint32_t)(items[i].*f);
+      mx = std::max<uint64_t>(mx, field[i]);
+    }
+    radix_sort_by(idx, mx, [&](int64_t i) { return (uint64_t)field[i]; });
   };
-  std::sort(idx.begin(), idx.end(), [&](int64_t x, int64_t y) { return key(x) < key(y); });
+  by(&skv_item::chunk);
+  by(&skv_item::hi);
+  by(&skv_item::lo);
+  by(&skv_item::kv_head);
+  by(&skv_item::seq);
   struct Run { int64_t first; int32_t len; int64_t cost; };
   std::vector<Run> runs;
   bool open = false;
@@ -301,12 +403,18 @@ extern "C" int skv_coarsen_fwd_items(const skv_item* items, const int64_t* cost,
     }
     open = cost[i] > 0;  // a zero-cost item stands alone
   }
-  std::sort(runs.begin(), runs.end(), [](const Run& x, const Run& y) { return x.first < y.first; });
-  for (size_t r = 0; r < runs.size(); ++r) {
-    items_out[r] = items[runs[r].first];
-    items_out[r].n_chunk = runs[r].len;
-    cost_out[r] = runs[r].cost;
+  // output in order of each run's first item (first items are distinct)
+  std::vector<int64_t> run_of(n, -1);
+  for (size_t r = 0; r < runs.size(); ++r) run_of[runs[r].first] = (int64_t)r;
+  int64_t k = 0;
+  for (int64_t i = 0; i < n; ++i) {
+    if (run_of[i] < 0) continue;
+    const Run& R = runs[run_of[i]];
+    items_out[k] = items[i];
+    items_out[k].n_chunk = R.len;
+    cost_out[k] = R.cost;
+    ++k;
   }
-  *n_out = (int64_t)runs.size();
+  *n_out = k;
   return SKV_OK;
 }

@@ -135,6 +135,14 @@ class _PlanSlots:
         self.worker_off = off
         return [gathered, np.asarray(off, dtype=np.int64)]
 
+    def follow(self, other: "_PlanSlots"):
+        """Take the host results of an identical plan (same problem, kind,
+        granule, policy and runs), whose uploaded arrays this plan then binds
+        as well; only the claim cursors and busy-time counters stay separate."""
+        self.table, self.cost, self.load = other.table, other.cost, other.load
+        self.runs_used, self.n_planned, self.worker_off = other.runs_used, other.n_planned, other.worker_off
+        self.plan_s = 0.0
+
     def bind(self, d_items: int, d_off: int):
         """The skv_plan of the arrays uploaded to d_items / d_off."""
         self.c = B.skv_plan(self.kind, self.n_workers, self.n_planned, d_items, d_off, self.claim.data_ptr(),
@@ -191,12 +199,13 @@ class SplitKVAttention:
                                    runs_per_worker=self.fwd_runs_per_worker, run_imbalance=fwd_run_imbalance)
         self.bwd_plan = (_PlanSlots(self.problem, B.SKV_ITEM_BWD, self.bwd_granule, self.n_workers, policy, **kw)
                          if with_bwd else None)
-        # dQ runs over the forward's items; its own slots give it separate claim cursors
+        # dQ runs over the forward's plan (the same uploaded arrays); its own
+        # slots give it separate claim cursors
         self.dq_plan = (_PlanSlots(self.problem, B.SKV_ITEM_FWD, self.fwd_granule, self.n_workers, policy, **kw,
                                    runs_per_worker=self.fwd_runs_per_worker, run_imbalance=fwd_run_imbalance)
                         if with_bwd else None)
-        self.staging = _Staging(sum(p.stage_bytes for p in (self.fwd_plan, self.bwd_plan, self.dq_plan)
-                                    if p is not None), self.device)
+        self.staging = _Staging(sum(p.stage_bytes for p in (self.fwd_plan, self.bwd_plan) if p is not None),
+                                self.device)
         self.replan()
         self.part_base, self.n_chunk = self.problem.partial_layout()
         self.d_part_base = torch.from_numpy(self.part_base).to(self.device)
@@ -216,13 +225,16 @@ class SplitKVAttention:
     def replan(self):
         """Mask descriptor -> realized cost per item -> LPT plans, uploaded
         together (one copy) for the next kernels."""
-        plans = [self.fwd_plan] + ([self.bwd_plan, self.dq_plan] if self.bwd_plan is not None else [])
+        plans = [self.fwd_plan] + ([self.bwd_plan] if self.bwd_plan is not None else [])
         parts = []
         for p in plans:
             parts += p.build()
         ptrs = self.staging.upload(parts)
         for i, p in enumerate(plans):
             p.bind(ptrs[2 * i], ptrs[2 * i + 1])
+        if self.dq_plan is not None:
+            self.dq_plan.follow(self.fwd_plan)
+            self.dq_plan.bind(ptrs[0], ptrs[1])
         self.plan_s = sum(p.plan_s for p in plans)
 
     def _check(self, **tensors):

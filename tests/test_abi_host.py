@@ -82,6 +82,22 @@ def test_lpt_bit_exact_with_oracle_under_ties(seed):
     assert np.array_equal(a1, a2) and np.array_equal(o1, o2) and np.array_equal(f1, f2) and np.array_equal(l1, l2)
 
 
+@pytest.mark.parametrize("n_workers,shift", [(1, 54), (37, 55), (300, 54), (256, 30)])
+def test_lpt_bit_exact_with_oracle_at_large_costs(n_workers, shift):
+    """Totals past 2^(62 - bits(W - 1)) no longer fit the packed (load, worker)
+    heap key and take the general heap ((37, 55) and (300, 54)); costs that
+    span several bytes take several radix passes.  Totals stay below 2^62."""
+    rng = np.random.default_rng(shift * 1000 + n_workers)
+    n = 64
+    big = rng.integers(0, 4, size=n) * (np.int64(1) << shift)
+    small = rng.integers(0, 1 << 20, size=n)
+    cost = np.where(rng.random(n) < 0.5, big, small).astype(np.int64)
+    assert int(cost.sum()) < 1 << 62
+    a1, o1, f1, l1 = B.lpt_plan(cost, n_workers)
+    a2, o2, f2, l2 = oracle.lpt(cost, n_workers)
+    assert np.array_equal(a1, a2) and np.array_equal(o1, o2) and np.array_equal(f1, f2) and np.array_equal(l1, l2)
+
+
 def test_lpt_worked_example_and_degenerate_inputs():
     a, o, f, l = B.lpt_plan([3, 3, 2, 2, 2], 2)
     assert list(a) == [0, 1, 0, 1, 0] and list(l) == [7, 5]
