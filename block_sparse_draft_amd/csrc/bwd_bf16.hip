@@ -24,9 +24,13 @@
 //      draft blocks), structured like the forward: 64 rows per wave with Q
 //      in registers and dO in LDS, K/V tiles of the chunk through two LDS
 //      buffers;
-//      S^T = K Q^T, dP^T = V dO^T, dS^T, then dQ^T += K^T dS^T.  Each item
-//      writes its chunk's dQ partial, like the forward's O partial.
+//      S^T = K Q^T, dP^T = V dO^T, dS^T, then dQ^T += K^T dS^T, with the two
+//      32-key halves of a tile software-pipelined (one half's dS work beside
+//      the other half's MFMAs).  Each item writes its chunk's dQ partial, like
+//      the forward's O partial.
 //   4. finalize: dQ = scale * sum of the row's visible chunk partials, bf16.
+#include <type_traits>
+
 #include "device.h"
 #include "launch.h"
 #include "timing.h"
@@ -493,56 +497,88 @@ void bwd_dq_kernel(BwdArgs a) {
         const uint16_t* sK = sKV[t & 1][0];
         const uint16_t* sV = sKV[t & 1][1];
 
-        const bool need_mask = kb + KT2 > wave_full;
-        // The 64 keys are handled as two halves of 32 (mt), which halves the
-        // live S^T / dP^T accumulators without re-reading any operand.
+        // The 64 keys are two halves of 32 (mt = 0, 1).  Within the tile the
+        // halves are software-pipelined: each k step of half 1's S^T / dP^T
+        // products carries part of half 0's dS work, and each step of half 0's
+        // dQ products part of half 1's, so the VALU work of one half runs in
+        // the shadow of the other half's MFMAs.  Every value is computed as in
+        // a plain half-by-half loop; only the instruction order differs.
+        auto tile = [&](auto mask_c) {
+          constexpr bool MASK = decltype(mask_c)::value;  // partial tile: keys past a row's end are masked
+          // dS^T = P^T (dP^T - Delta), P^T = exp2(s*c - LSE2) on visible keys,
+          // for elements e0 and e0 + 1 of both row groups of half mt
+          auto ds_pair = [&](int mt, int e0, f32x16 (&sacc)[2], const f32x16 (&pacc)[2]) {
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-          // ---- S^T = K Q^T and dP^T = V dO^T for keys mt*32 .. +32 ----
-          f32x16 sacc[2], pacc[2];
-          sacc[0] = sacc[1] = pacc[0] = pacc[1] = f32x16{};
+            for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-          for (int ks = 0; ks < 8; ++ks) {
+              for (int e = e0; e < e0 + 2; ++e) {
+                float p = fast_exp2(__builtin_fmaf(sacc[nt][e], c, -lse2[nt]));
+                if (MASK) {
+                  const int key = kb + mt * 32 + (e >> 2) * 8 + hf * 4 + (e & 3);
+                  if (key >= vend[nt]) p = 0.f;
+                }
+                sacc[nt][e] = p * (pacc[nt][e] - del[nt]);
+              }
+          };
+          // k step ks of S^T = K Q^T and dP^T = V dO^T for keys mt*32 .. +32
+          auto sp_step = [&](int mt, int ks, f32x16 (&sacc)[2], f32x16 (&pacc)[2]) {
             const bf16x8 kf = lds_load_bf16x8(sK + (mt * 32 + l32) * LDS_ROW + ks * 16 + hf * 8);
             const bf16x8 vf = lds_load_bf16x8(sV + (mt * 32 + l32) * LDS_ROW + ks * 16 + hf * 8);
             sacc[0] = mfma32x32x16(kf, qf[0][ks], sacc[0]);
             sacc[1] = mfma32x32x16(kf, qf[1][ks], sacc[1]);
             pacc[0] = mfma32x32x16(vf, lds_load_bf16x8(my_dO + ks * 16), pacc[0]);
             pacc[1] = mfma32x32x16(vf, lds_load_bf16x8(my_dO + 32 * LDS_ROW + ks * 16), pacc[1]);
-          }
-          // ---- dS^T = P^T (dP^T - Delta), P^T = exp2(s*c - LSE2) on visible keys ----
-#pragma unroll
-          for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-              float p = fast_exp2(__builtin_fmaf(sacc[nt][e], c, -lse2[nt]));
-              if (need_mask) {
-                const int key = kb + mt * 32 + (e >> 2) * 8 + hf * 4 + (e & 3);
-                if (key >= vend[nt]) p = 0.f;
-              }
-              sacc[nt][e] = p * (pacc[nt][e] - del[nt]);
-            }
-          // ---- dQ^T += K^T dS^T over these 32 keys (K^T read transposed from LDS) ----
-#pragma unroll
-          for (int half = 0; half < 2; ++half) {
+          };
+          // dS^T of keys mt*32 + 16*half .. +16 as bf16 MFMA operands
+          auto to_df = [&](const f32x16 (&sacc)[2], int half, bf16x8 (&df)[2]) {
             const int qh = half * 8;
-            bf16x8 df[2];
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt) {
               const f32x16& sv = sacc[nt];
               df[nt] = to_bf16x8(sv[qh + 0], sv[qh + 1], sv[qh + 2], sv[qh + 3], sv[qh + 4], sv[qh + 5],
                                  sv[qh + 6], sv[qh + 7]);
             }
+          };
+          // head-dim block md of dQ^T += K^T dS^T over keys mt*32 + 16*half .. +16
+          // (K^T read transposed from LDS)
+          auto dq_step = [&](int mt, int half, int md, const bf16x8 (&df)[2]) {
             const int key0 = (2 * mt + half) * 16 + 4 * hf + (li >> 2);
+            const int col = md * 32 + 16 * (gi & 1) + 4 * (li & 3);
+            const bf16x8 kt = lds_tr_pair(sK + key0 * LDS_ROW + col, sK + (key0 + 8) * LDS_ROW + col);
+            acc[md][0] = mfma32x32x16(kt, df[0], acc[md][0]);
+            acc[md][1] = mfma32x32x16(kt, df[1], acc[md][1]);
+          };
+
+          f32x16 s0[2], p0[2], s1[2], p1[2];
+          s0[0] = s0[1] = p0[0] = p0[1] = f32x16{};
+          s1[0] = s1[1] = p1[0] = p1[1] = f32x16{};
+#pragma unroll
+          for (int ks = 0; ks < 8; ++ks) sp_step(0, ks, s0, p0);
+#pragma unroll
+          for (int ks = 0; ks < 8; ++ks) {  // half 1's scores with half 0's dS
+            sp_step(1, ks, s1, p1);
+            ds_pair(0, 2 * ks, s0, p0);
+          }
+#pragma unroll
+          for (int half = 0; half < 2; ++half) {  // half 0's dQ with half 1's dS
+            bf16x8 df[2];
+            to_df(s0, half, df);
 #pragma unroll
             for (int md = 0; md < 4; ++md) {
-              const int col = md * 32 + 16 * (gi & 1) + 4 * (li & 3);
-              const bf16x8 kt = lds_tr_pair(sK + key0 * LDS_ROW + col, sK + (key0 + 8) * LDS_ROW + col);
-              acc[md][0] = mfma32x32x16(kt, df[0], acc[md][0]);
-              acc[md][1] = mfma32x32x16(kt, df[1], acc[md][1]);
+              dq_step(0, half, md, df);
+              ds_pair(1, 2 * (half * 4 + md), s1, p1);
             }
           }
-        }
+#pragma unroll
+          for (int half = 0; half < 2; ++half) {
+            bf16x8 df[2];
+            to_df(s1, half, df);
+#pragma unroll
+            for (int md = 0; md < 4; ++md) dq_step(1, half, md, df);
+          }
+        };
+        if (kb + KT2 > wave_full) tile(std::integral_constant<bool, true>{});
+        else tile(std::integral_constant<bool, false>{});
       }
 
       // ---- the item's dQ partial (unscaled) for rows that see its keys ----
