@@ -26,10 +26,10 @@
 // exp2 domain with lazy rescaling (the reference maximum only moves when the
 // true maximum exceeds it by 2^8; the output is corrected to the true maximum
 // once per item), O^T += V^T P^T with P^T taken straight from the S^T
-// accumulators.  The scores of tile t+1 are issued in the same scheduling
-// block as the exponentials and PV products of tile t (software pipeline),
-// and K/V tiles are fetched through buffer descriptors so that the per-tile
-// address work is scalar.
+// accumulators.  The scores of tile t+1 are computed before the exponentials
+// and PV products of tile t (software pipeline), every LDS operand is read one
+// MFMA step ahead of its use, and K/V tiles are fetched through buffer
+// descriptors so that the per-tile address work is scalar.
 #include "device.h"
 #include "launch.h"
 #include "timing.h"
@@ -203,19 +203,27 @@ void fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc_o[i] = f32x16{};
 
-      // S^T = K Q^T of the tile in buffer `buf` (raw scores), 16 MFMAs.
+      // S^T = K Q^T of the tile in buffer `buf` (raw scores), 16 MFMAs.  The K
+      // operands of k step ks+1 are read before the MFMAs of k step ks, so a
+      // read's latency overlaps the previous step's products.
       auto scores = [&](int buf, f32x16 (&sacc)[2]) {
         uint32_t ka = lds_addr(sKb[buf] + l32 * LDS_ROW_K + hf * 8);
         asm volatile("" : "+v"(ka));  // keeps the per-read offsets as immediates
         sacc[0] = sacc[1] = f32x16{};
+        bf16x8 kc[2];
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) kc[mt] = lds_read_b128(ka + 2u * (mt * 32 * LDS_ROW_K));
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) {
-          if (ks & 1) asm volatile("" ::: "memory");  // bounds how far the compiler hoists the reads
+          bf16x8 kn[2] = {kc[0], kc[1]};
+          if (ks + 1 < 8) {
 #pragma unroll
-          for (int mt = 0; mt < 2; ++mt) {
-            const bf16x8 kf = lds_read_b128(ka + 2u * (mt * 32 * LDS_ROW_K + ks * 16));
-            sacc[mt] = mfma32x32x16(kf, qf[ks], sacc[mt]);
+            for (int mt = 0; mt < 2; ++mt) kn[mt] = lds_read_b128(ka + 2u * (mt * 32 * LDS_ROW_K + (ks + 1) * 16));
           }
+#pragma unroll
+          for (int mt = 0; mt < 2; ++mt) sacc[mt] = mfma32x32x16(kc[mt], qf[ks], sacc[mt]);
+          kc[0] = kn[0];
+          kc[1] = kn[1];
         }
       };
 
@@ -265,13 +273,19 @@ void fwd_bf16_kernel(FwdArgs a) {
         scores((t + 1) % NBUF, snext);
         // ---- P = exp2(s*c - m_ref*c), 16 keys at a time right before their
         //      part of O^T += V^T P^T; the row sum in fp32 (bf16-rounded P
-        //      would cost the log-sum-exp up to 2^-9 relative on short rows) ----
+        //      would cost the log-sum-exp up to 2^-9 relative on short rows).
+        //      The V operands of the next 16 keys are read before this step's
+        //      MFMAs, so they arrive while the next exponentials are computed;
+        //      the empty asm ends each step's scheduling region, which bounds
+        //      how many operands the compiler keeps in flight. ----
         uint32_t va = lds_addr(sVb[t % NBUF] + l32 * LDS_ROW_VT + hf * 8);
         asm volatile("" : "+v"(va));
         const float mc = m_ref == -INFINITY ? 0.f : m_ref * c;
+        bf16x8 vc[4];
+#pragma unroll
+        for (int md = 0; md < 4; ++md) vc[md] = lds_read_b128(va + 2u * (md * 32 * LDS_ROW_VT));
 #pragma unroll
         for (int kstep = 0; kstep < 4; ++kstep) {
-          asm volatile("" ::: "memory");
           const int mt = kstep >> 1, qh = (kstep & 1) * 8;
           const f32x16& sv = scur[mt];
           float pe[8];
@@ -279,19 +293,16 @@ void fwd_bf16_kernel(FwdArgs a) {
           for (int u = 0; u < 8; ++u) pe[u] = fast_exp2(__builtin_fmaf(sv[qh + u], c, -mc));
           const bf16x8 pf = to_bf16x8(pe[0], pe[1], pe[2], pe[3], pe[4], pe[5], pe[6], pe[7]);
           l += ((pe[0] + pe[1]) + (pe[2] + pe[3])) + ((pe[4] + pe[5]) + (pe[6] + pe[7]));
+          bf16x8 vn[4] = {vc[0], vc[1], vc[2], vc[3]};
+          if (kstep + 1 < 4) {
 #pragma unroll
-          for (int md = 0; md < 4; ++md) {
-            const bf16x8 vf = lds_read_b128(va + 2u * (md * 32 * LDS_ROW_VT + kstep * 16));
-            acc_o[md] = mfma32x32x16(vf, pf, acc_o[md]);
+            for (int md = 0; md < 4; ++md) vn[md] = lds_read_b128(va + 2u * (md * 32 * LDS_ROW_VT + (kstep + 1) * 16));
           }
-        }
-        // Interleave the block's 32 MFMAs with its operand reads and VALU work
-        // (exponentials of this tile) instead of issuing them in bursts.
 #pragma unroll
-        for (int g = 0; g < 32; ++g) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
-          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // 4 VALU
+          for (int md = 0; md < 4; ++md) acc_o[md] = mfma32x32x16(vc[md], pf, acc_o[md]);
+          asm volatile("" ::: "memory");
+#pragma unroll
+          for (int md = 0; md < 4; ++md) vc[md] = vn[md];
         }
         scur[0] = snext[0];
         scur[1] = snext[1];
