@@ -1,6 +1,8 @@
 """Build libsplitkv.so (gfx950) in-tree with hipcc.
 
-    python -m block_sparse_draft_amd.build      # or __graft_entry__.build()
+    python block_sparse_draft_amd/build.py      # or __graft_entry__.build()
+
+(Run it as a script: importing the package needs the library it builds.)
 
 Every HIP source is compiled with packed-FP32 instructions disabled (the
 compiler otherwise forms v_pk_* fp32 ops on its own) and linked into one shared
