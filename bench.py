@@ -125,17 +125,19 @@ KERNEL_FLOPS_D = {"partial_fwd_bf16": 4, "partial_fwd_f32": 4, "bwd_kv": 8, "bwd
 KERNEL_EXEC_FLOPS_D = {"partial_fwd_bf16": 4, "partial_fwd_f32": 4, "bwd_kv": 8, "bwd_dq": 6}
 # Sources whose text defines each kernel's device code (the kernel file and
 # the device-side helpers it includes).
+# Files a kernel's machine code depends on: its source, the shared device
+# headers and the build script (compile flags), relative to the package.
 KERNEL_SOURCES = {
-    "bwd_kv": ["bwd_bf16.hip", "device.h", "fastdiv.h"],
-    "bwd_dq": ["bwd_bf16.hip", "device.h", "fastdiv.h"],
-    "partial_fwd_bf16": ["fwd_bf16.hip", "device.h", "fastdiv.h"],
+    "bwd_kv": ["csrc/bwd_bf16.hip", "csrc/device.h", "csrc/fastdiv.h", "build.py"],
+    "bwd_dq": ["csrc/bwd_bf16.hip", "csrc/device.h", "csrc/fastdiv.h", "build.py"],
+    "partial_fwd_bf16": ["csrc/fwd_bf16.hip", "csrc/device.h", "csrc/fastdiv.h", "build.py"],
 }
 
 
 def kernel_source_hash(kernel: str) -> str:
     h = hashlib.sha256()
     for f in KERNEL_SOURCES.get(kernel, []):
-        with open(os.path.join(ROOT, "block_sparse_draft_amd", "csrc", f), "rb") as fh:
+        with open(os.path.join(ROOT, "block_sparse_draft_amd", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
@@ -143,8 +145,8 @@ def kernel_source_hash(kernel: str) -> str:
 def hbm_traffic(kernel: str, config: str):
     """HBM bytes per launch of `kernel` on `config` from the committed counter
     summary (rocprofv3 FETCH_SIZE / WRITE_SIZE, scaled by a copy kernel of
-    known size), or None when there is none or the kernel source has changed
-    since the counters were taken."""
+    known size), or None when there is none or the kernel's sources or build
+    flags have changed since the counters were taken."""
     path = os.path.join(ROOT, "profiles", f"{kernel}_{config}_hbm_traffic.txt")
     if not os.path.exists(path):
         return None
