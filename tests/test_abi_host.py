@@ -292,6 +292,27 @@ def test_coarsen_fwd_items_matches_oracle(cfg, granule, target):
         assert np.array_equal(it2[f], ref[f]), f
 
 
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_coarsen_fwd_items_any_input_order(seed):
+    """Items in a random order (the grouping sort must not rely on the item
+    table's order): runs, costs and output order still equal the oracle's on the
+    same permuted table."""
+    w = _meta_only("c3", {})
+    p = _problem_from(w)
+    items, cost, _, _ = p.item_table(B.SKV_ITEM_FWD, 4)
+    desc, ocost, _, _ = _oracle_table(w, "fwd", 4)
+    perm = np.random.default_rng(seed).permutation(len(cost))
+    items, cost, desc, ocost = items[perm], cost[perm], desc[perm], ocost[perm]
+    target = int(cost.sum() // 700) + 1
+    it2, c2 = B.skv_coarsen_fwd_items(items, cost, target)
+    first, length, rcost = oracle.coarsen_runs(desc, ocost, target)
+    assert np.array_equal(c2, rcost) and np.array_equal(it2["n_chunk"], length)
+    ref = items[first]
+    for f in ("seq", "kv_head", "chunk", "range", "part_base", "lo", "hi"):
+        assert np.array_equal(it2[f], ref[f]), f
+    assert (length > 1).any()
+
+
 def test_coarsen_fwd_items_rejects_bad_input():
     w = make("c2", seed=0, n_ctx=4096, n_anchor=4, with_do=False)
     p = _problem_from(w)
