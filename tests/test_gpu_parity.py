@@ -552,6 +552,48 @@ def test_bf16_edge_sequences_both_masks(mask):
 
 
 @pytest.mark.parametrize("mask", ["prefix", "own_block"])
+def test_bf16_more_than_64_partials_per_row(mask):
+    """71 chunks of 128 keys (72 partials per row with the own-block one), one
+    partial per chunk: the merge lists a row's nonzero weights 64 partials at a
+    time, so late anchors take its second block; the dQ finalize sums as many
+    partials.  Forward, both merges and backward against the oracle."""
+    w = make("c4", seed=70, with_do=True, n_ctx=9000, n_anchor=8, hq=4, hkv=1, chunk=128)
+    # three blocks whose context prefix (under either mask) spans more than 64 chunks
+    assert -(-9000 // 128) == 71 and int(np.sum(w.anchors > 64 * 128)) == 3
+    if mask == "own_block":
+        add_own_block(w)
+    path = make_path(w, DEV, with_bwd=True, mask=mask, fwd_runs_per_worker=None)
+    q, k, v = _upload(w)
+    do = to_device(w, "do", DEV)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    if mask == "own_block":
+        ko, vo = _own_upload(w)
+        dko, dvo = torch.empty_like(ko), torch.empty_like(vo)
+        path.forward(q, k, v, k_own=ko, v_own=vo)
+        o_all, l_all = path.o.clone(), path.lse.clone()
+        path.merge_per_sequence()
+        path.backward(q, k, v, do, dq, dk, dv, own=(ko, vo, dko, dvo))
+        torch.cuda.synchronize()
+        O, L = oracle.attention_own_workload(w)
+        rq, rk, rv, rko, rvo = oracle.bwd_own_workload(w)
+        assert_close("dK_own", to_np64(dko), rko, BF16_ABS, BF16_FROB)
+        assert_close("dV_own", to_np64(dvo), rvo, BF16_ABS, BF16_FROB)
+    else:
+        path.forward(q, k, v)
+        o_all, l_all = path.o.clone(), path.lse.clone()
+        path.merge_per_sequence()
+        path.backward(q, k, v, do, dq, dk, dv)
+        torch.cuda.synchronize()
+        O, L = oracle.attention_workload(w)
+        rq, rk, rv = oracle.bwd_workload(w)[:3]
+    assert torch.equal(o_all, path.o) and torch.equal(l_all, path.lse)
+    _check_merged(path, w, O, L)
+    assert_close("dQ", to_np64(dq), rq, BF16_ABS, BF16_FROB)
+    assert_close("dK", to_np64(dk), rk, BF16_ABS, BF16_FROB)
+    assert_close("dV", to_np64(dv), rv, BF16_ABS, BF16_FROB)
+
+
+@pytest.mark.parametrize("mask", ["prefix", "own_block"])
 def test_merge_all_equals_per_sequence_merge(mask):
     """The one-launch merge of every sequence gives bitwise the per-sequence
     lse_merge results (sequences of different lengths, rows straddling
