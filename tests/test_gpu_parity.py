@@ -593,6 +593,56 @@ def test_bf16_more_than_64_partials_per_row(mask):
     assert_close("dV", to_np64(dv), rv, BF16_ABS, BF16_FROB)
 
 
+ODD_SHAPES = {
+    # (block, hq, hkv): rows per (draft block, KV head) G*B = 16, 15, 1 and 80, so
+    # the 32-row query tiles of the backward end in padding rows and the packed
+    # row index splits at odd strides
+    "gb16": (16, 2, 2),
+    "gb15": (5, 6, 2),
+    "gb1": (1, 4, 4),
+    "gb80": (40, 2, 1),
+}
+
+
+@pytest.mark.parametrize("mask", ["prefix", "own_block"])
+@pytest.mark.parametrize("shape", sorted(ODD_SHAPES))
+def test_bf16_odd_block_and_group_sizes(shape, mask):
+    """Forward, merge and backward at draft-block sizes and GQA groups whose
+    row counts are not multiples of the kernels' tiles, two ragged sequences."""
+    block, hq, hkv = ODD_SHAPES[shape]
+    rng = np.random.default_rng(61)
+    anchors = [sorted(rng.integers(0, 1500, size=9).tolist()), sorted(rng.integers(0, 700, size=9).tolist())]
+    anchors[0][-1] = 1499  # a block reaching the end of the context
+    w = make_custom([1500, 700], anchors, block=block, hq=hq, hkv=hkv, d=128, dtype="bf16", chunk=256, seed=62,
+                    with_do=True)
+    if mask == "own_block":
+        add_own_block(w)
+    path = make_path(w, DEV, with_bwd=True, mask=mask, fwd_runs_per_worker=2, fwd_run_imbalance=None)
+    q, k, v = _upload(w)
+    do = to_device(w, "do", DEV)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    if mask == "own_block":
+        ko, vo = _own_upload(w)
+        dko, dvo = torch.empty_like(ko), torch.empty_like(vo)
+        path.forward(q, k, v, k_own=ko, v_own=vo)
+        path.backward(q, k, v, do, dq, dk, dv, own=(ko, vo, dko, dvo))
+        torch.cuda.synchronize()
+        O, L = oracle.attention_own_workload(w)
+        rq, rk, rv, rko, rvo = oracle.bwd_own_workload(w)
+        assert_close("dK_own", to_np64(dko), rko, BF16_ABS, BF16_FROB)
+        assert_close("dV_own", to_np64(dvo), rvo, BF16_ABS, BF16_FROB)
+    else:
+        path.forward(q, k, v)
+        path.backward(q, k, v, do, dq, dk, dv)
+        torch.cuda.synchronize()
+        O, L = oracle.attention_workload(w)
+        rq, rk, rv = oracle.bwd_workload(w)[:3]
+    _check_merged(path, w, O, L)
+    assert_close("dQ", to_np64(dq), rq, BF16_ABS, BF16_FROB)
+    assert_close("dK", to_np64(dk), rk, BF16_ABS, BF16_FROB)
+    assert_close("dV", to_np64(dv), rv, BF16_ABS, BF16_FROB)
+
+
 @pytest.mark.parametrize("mask", ["prefix", "own_block"])
 def test_merge_all_equals_per_sequence_merge(mask):
     """The one-launch merge of every sequence gives bitwise the per-sequence
