@@ -643,6 +643,50 @@ def test_bf16_odd_block_and_group_sizes(shape, mask):
     assert_close("dV", to_np64(dv), rv, BF16_ABS, BF16_FROB)
 
 
+def test_bf16_strided_views_through_the_c_abi():
+    """Q, O, dO and dQ as views with a padding head slot; K and V as two halves
+    of one packed [N, 2, hkv + 1, d] tensor, dK and dV likewise.  The C ABI
+    takes the row and head strides; every output equals the contiguous run
+    bitwise, NaN padding in the inputs is never read and the outputs' padding
+    is never written."""
+    from block_sparse_draft_amd import binding as B
+    w = make("c3", seed=71, with_do=True, n_ctx_range=(900, 2100), n_anchor=5, hq=8, hkv=2, chunk=512)
+    c = w.cfg
+    path = make_path(w, DEV, with_bwd=True, fwd_runs_per_worker=2, fwd_run_imbalance=None)
+    q, k, v = _upload(w)
+    do = to_device(w, "do", DEV)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    path.forward(q, k, v)
+    ref_o, ref_l = path.o.clone(), path.lse.clone()
+    path.backward(q, k, v, do, dq, dk, dv)
+    torch.cuda.synchronize()
+
+    tq, tk, hq, hkv, d = q.shape[0], k.shape[0], c.hq, c.hkv, c.d
+    nan, mark = float("nan"), 7.0
+    bf = dict(dtype=torch.bfloat16, device=DEV)
+    Qb = torch.full((tq, hq + 1, d), nan, **bf); Qb[:, :hq] = q
+    DOb = torch.full((tq, hq + 1, d), nan, **bf); DOb[:, :hq] = do
+    KVb = torch.full((tk, 2, hkv + 1, d), nan, **bf); KVb[:, 0, :hkv] = k; KVb[:, 1, :hkv] = v
+    Ob = torch.full((tq, hq + 1, d), mark, **bf)
+    dQb = torch.full((tq, hq + 1, d), mark, **bf)
+    dKVb = torch.full((tk, 2, hkv + 1, d), mark, **bf)
+    lse = torch.empty((tq, hq), dtype=torch.float32, device=DEV)
+    prob = B.Problem(w.q_off, w.kv_off, w.anchors, c.block, hq, hkv, d, c.chunk, B.SKV_BF16, w.sm_scale,
+                     q_strides=((hq + 1) * d, d), kv_strides=(2 * (hkv + 1) * d, d), device=DEV)
+    prob.check()
+    B.sparse_attn_partial_fwd(prob, path.fwd_plan, Qb[:, :hq], KVb[:, 0, :hkv], KVb[:, 1, :hkv], path.o_part,
+                              path.m_part, path.lse_part)
+    B.lse_merge_all(prob, path.d_part_base, path.o_part, path.m_part, path.lse_part, Ob[:, :hq], lse)
+    B.sparse_attn_bwd(prob, path.bwd_plan, path.dq_plan, Qb[:, :hq], KVb[:, 0, :hkv], KVb[:, 1, :hkv], Ob[:, :hq],
+                      lse, DOb[:, :hq], dQb[:, :hq], dKVb[:, 0, :hkv], dKVb[:, 1, :hkv], path.workspace)
+    torch.cuda.synchronize()
+    assert torch.equal(Ob[:, :hq], ref_o) and torch.equal(lse, ref_l)
+    assert torch.equal(dQb[:, :hq], dq)
+    assert torch.equal(dKVb[:, 0, :hkv], dk) and torch.equal(dKVb[:, 1, :hkv], dv)
+    assert bool((Ob[:, hq] == mark).all()) and bool((dQb[:, hq] == mark).all())
+    assert bool((dKVb[:, :, hkv] == mark).all())
+
+
 @pytest.mark.parametrize("mask", ["prefix", "own_block"])
 def test_merge_all_equals_per_sequence_merge(mask):
     """The one-launch merge of every sequence gives bitwise the per-sequence
