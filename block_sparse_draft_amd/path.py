@@ -29,25 +29,32 @@ def _align256(n: int) -> int:
 
 
 class _Staging:
-    """Two pinned-host / device buffer pairs shared by the step's plans: each
-    step's plans are packed into one pair and uploaded with a single
-    asynchronous copy on the compute stream, while the previous step's kernels
-    may still read the other pair."""
+    """Two pinned-host / device buffer pairs shared by the step's plans.  A
+    step's plans are packed into one pair on the host (``stage``); the copy to
+    the device is issued by the step's first kernel call, on that call's stream
+    (``flush``), so the kernels that read the plans are ordered after it on
+    whatever stream the caller uses.  Each kernel call records on its stream
+    that the pair is in use (``used_on``), and the next copy into the pair
+    waits for it, while the previous step's kernels may still read the other
+    pair."""
 
     def __init__(self, nbytes: int, device):
         import torch
         self.slots = [{"h": torch.empty(max(nbytes, 256), dtype=torch.uint8, pin_memory=True),
                        "d": torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device),
-                       "event": torch.cuda.Event(), "used": False} for _ in range(2)]
+                       "copied": torch.cuda.Event(), "done": torch.cuda.Event(), "used": False}
+                      for _ in range(2)]
         self.next = 0
+        self.cur = None       # the slot of the current step
+        self.pending = 0      # bytes staged on the host, not yet copied
 
-    def upload(self, parts):
-        """Copy the numpy arrays ``parts`` (256-byte aligned, in order) to the
-        device; returns their device addresses."""
+    def stage(self, parts):
+        """Pack the numpy arrays ``parts`` (256-byte aligned, in order) into the
+        next slot's pinned buffer; returns their device addresses."""
         slot = self.slots[self.next]
         self.next ^= 1
         if slot["used"]:
-            slot["event"].synchronize()   # its previous upload has left the pinned buffer
+            slot["copied"].synchronize()   # its previous copy has left the pinned buffer
         h = slot["h"].numpy()
         pos, ptrs = 0, []
         for a in parts:
@@ -55,10 +62,27 @@ class _Staging:
             h[pos:pos + len(b)] = b
             ptrs.append(slot["d"].data_ptr() + pos)
             pos = _align256(pos + len(b))
-        slot["d"][:pos].copy_(slot["h"][:pos], non_blocking=True)
-        slot["event"].record()
-        slot["used"] = True
+        self.cur, self.pending = slot, pos
         return ptrs
+
+    def flush(self, stream):
+        """Issue the staged copy on ``stream`` (a torch stream) if not done yet."""
+        import torch
+        slot = self.cur
+        if slot is None or not self.pending:
+            return
+        if slot["used"]:
+            stream.wait_event(slot["done"])  # kernels of two steps ago read this device buffer
+        with torch.cuda.stream(stream):
+            slot["d"][:self.pending].copy_(slot["h"][:self.pending], non_blocking=True)
+        slot["copied"].record(stream)
+        slot["used"] = True
+        self.pending = 0
+
+    def used_on(self, stream):
+        """Kernels reading the current slot were launched on ``stream``."""
+        if self.cur is not None:
+            self.cur["done"].record(stream)
 
 
 class _PlanSlots:
@@ -223,13 +247,13 @@ class SplitKVAttention:
 
     # -- steps -------------------------------------------------------------
     def replan(self):
-        """Mask descriptor -> realized cost per item -> LPT plans, uploaded
-        together (one copy) for the next kernels."""
+        """Mask descriptor -> realized cost per item -> LPT plans, staged for
+        one copy to the device that the next kernel call issues on its stream."""
         plans = [self.fwd_plan] + ([self.bwd_plan] if self.bwd_plan is not None else [])
         parts = []
         for p in plans:
             parts += p.build()
-        ptrs = self.staging.upload(parts)
+        ptrs = self.staging.stage(parts)
         for i, p in enumerate(plans):
             p.bind(ptrs[2 * i], ptrs[2 * i + 1])
         if self.dq_plan is not None:
@@ -251,14 +275,26 @@ class SplitKVAttention:
                 raise ValueError(f"{name}: need a contiguous {self.dtype} tensor of shape {want} on {self.device}, "
                                  f"got {t.dtype} {tuple(t.shape)} on {t.device}")
 
+    def _stream(self, stream):
+        """The torch stream of a call (None: the current stream of the device;
+        an int: a raw hipStream_t)."""
+        import torch
+        if stream is None:
+            return torch.cuda.current_stream(self.device)
+        if isinstance(stream, int):
+            return torch.cuda.ExternalStream(stream, device=self.device)
+        return stream
+
     def partial_fwd(self, q, k, v, stream=None, k_own=None, v_own=None):
         self._check(q=q, k=k, v=v, k_own=k_own, v_own=v_own)
-        B.sparse_attn_partial_fwd(self.problem, self.fwd_plan, q, k, v, self.o_part, self.m_part, self.lse_part,
-                                  stream)
+        if self.mask == "own_block" and (k_own is None or v_own is None):
+            raise ValueError("the own-block mask needs k_own and v_own")
+        ts = self._stream(stream)
+        self.staging.flush(ts)
+        B.sparse_attn_partial_fwd(self.problem, self.fwd_plan, q, k, v, self.o_part, self.m_part, self.lse_part, ts)
         if self.mask == "own_block":
-            if k_own is None or v_own is None:
-                raise ValueError("the own-block mask needs k_own and v_own")
-            B.sparse_attn_own_fwd(self.problem, q, k_own, v_own, self.o_part, self.m_part, self.lse_part, stream)
+            B.sparse_attn_own_fwd(self.problem, q, k_own, v_own, self.o_part, self.m_part, self.lse_part, ts)
+        self.staging.used_on(ts)
 
     def merge(self, stream=None):
         """The exact merge of every sequence's partials, in one launch."""
@@ -289,8 +325,11 @@ class SplitKVAttention:
             raise ValueError("own-block tensors go with the own-block mask")
         self._check(q=q, k=k, v=v, dout=dout, dq=dq, dk=dk, dv=dv,
                     **(dict(zip(("k_own", "v_own", "dk_own", "dv_own"), own)) if own is not None else {}))
+        ts = self._stream(stream)
+        self.staging.flush(ts)
         B.sparse_attn_bwd(self.problem, self.bwd_plan, self.dq_plan, q, k, v, self.o, self.lse, dout, dq, dk, dv,
-                          self.workspace, stream, own=own)
+                          self.workspace, ts, own=own)
+        self.staging.used_on(ts)
         return dq, dk, dv
 
     # -- views ---------------------------------------------------------------

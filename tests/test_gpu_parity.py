@@ -687,6 +687,35 @@ def test_bf16_strided_views_through_the_c_abi():
     assert bool((dKVb[:, :, hkv] == mark).all())
 
 
+def test_side_streams_match_the_default_stream():
+    """Steps replanned and run on a caller's side streams (forward on one,
+    backward on another, one step passing raw stream handles): the plan copy
+    goes to the stream of the step's first kernel call, and every result equals
+    the default-stream one bitwise."""
+    w = make("c3", seed=81, with_do=True, n_ctx_range=(900, 2100), n_anchor=5, hq=8, hkv=2, chunk=512)
+    path = make_path(w, DEV, with_bwd=True, fwd_runs_per_worker=2, fwd_run_imbalance=None)
+    q, k, v = _upload(w)
+    do = to_device(w, "do", DEV)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    path.forward(q, k, v)
+    ref_o, ref_l = path.o.clone(), path.lse.clone()
+    path.backward(q, k, v, do, dq, dk, dv)
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    for step in range(3):
+        path.replan()
+        dq2, dk2, dv2 = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        a1, a2 = (s1, s2) if step != 1 else (s1.cuda_stream, s2.cuda_stream)
+        s1.wait_stream(torch.cuda.current_stream())
+        path.forward(q, k, v, stream=a1)
+        s2.wait_stream(s1)
+        path.backward(q, k, v, do, dq2, dk2, dv2, stream=a2)
+        torch.cuda.current_stream().wait_stream(s2)
+        torch.cuda.synchronize()
+        assert torch.equal(path.o, ref_o) and torch.equal(path.lse, ref_l), step
+        assert torch.equal(dq2, dq) and torch.equal(dk2, dk) and torch.equal(dv2, dv), step
+
+
 @pytest.mark.parametrize("mask", ["prefix", "own_block"])
 def test_merge_all_equals_per_sequence_merge(mask):
     """The one-launch merge of every sequence gives bitwise the per-sequence
