@@ -27,8 +27,12 @@
  * Conventions shared by every call:
  *  - All device pointers are caller-owned; the library never allocates,
  *    frees or synchronizes.  Device calls are asynchronous on `stream`
- *    (a hipStream_t; NULL = the default stream).  Host calls (planning,
- *    sizing) are synchronous, pure, and touch no GPU.
+ *    (a hipStream_t; NULL = the default stream): the buffers a call reads
+ *    (inputs and plan arrays) must hold their contents, and every buffer must
+ *    stay allocated, until that work completes, and writes to them issued on
+ *    other streams (a plan upload, say) must be ordered before it by the
+ *    caller.  Host calls (planning, sizing) are synchronous, pure, and touch
+ *    no GPU.
  *  - Return value: SKV_OK or a negative skv_status; the reason is available
  *    from skv_last_error() on the calling thread.  Arguments are validated
  *    before any HIP call, so validation errors leave the stream untouched.
