@@ -3,11 +3,11 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c3]
 
 One step = one pass of the whole hot path over one synthetic batch: realized
-cost model + LPT plan (host, uploaded asynchronously), the partial forward of
-every (sequence, KV head, chunk, draft-block range) item, the log-sum-exp merge
-of each sequence, and the backward (Delta, key-owning dK/dV kernel,
-query-owning dQ kernel, dQ finalize).  Inputs are resident in HBM before the
-timed region.
+cost model + LPT plan (host; copied asynchronously on the stream ahead of the
+forward), the partial forward of every chunk-run item (sequence, KV head, run
+of chunks, draft-block range), the log-sum-exp merge of every sequence in one
+launch, and the backward (Delta, key-owning dK/dV kernel, query-owning dQ
+kernel, dQ finalize).  Inputs are resident in HBM before the timed region.
 
 Prints ONE JSON line.  ``value`` is unmasked fwd+bwd TFLOP/s: 4*d (forward) +
 10*d (backward, including the QK^T recompute that reusing the LSE needs) FLOPs
