@@ -355,13 +355,16 @@ def test_identical_keys_and_constant_values():
 
 def test_backward_bitwise_deterministic_across_plans_and_stealing():
     """The backward has no atomics: dQ, dK, dV are bitwise the same on a rerun,
-    under the static plan and with tail stealing off; every workgroup reports
-    its busy time when asked."""
+    under the static plan, with tail stealing off, and on grids of 13 (not a
+    multiple of the 8 XCDs, so workgroups map to workers one to one) and 600
+    workgroups (more than the compute units); every workgroup reports its busy
+    time when asked."""
     w = make("c3", seed=6, with_do=True, n_ctx_range=(2000, 7000), n_anchor=12, hq=8, hkv=2, chunk=1024)
     q, k, v = _upload(w)
     ref = None
     for kw in (dict(), dict(), dict(policy="static"), dict(steal=False, ticks=True),
-               dict(policy="static", steal=False, ticks=True)):
+               dict(policy="static", steal=False, ticks=True), dict(n_workers=13, ticks=True),
+               dict(n_workers=600, steal=False)):
         path = make_path(w, DEV, with_bwd=True, bwd_granule=128, **kw)
         do = to_device(w, "do", DEV)
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
