@@ -23,7 +23,9 @@ int check_plan(const skv_plan* plan, int32_t kind) {
 }
 
 int check_device_problem(const skv_problem* p) {
-  if (!p->d_q_off || !p->d_kv_off || !p->d_anchor) return fail(SKV_EINVAL, "device offset/anchor arrays are NULL");
+  // the anchor array is empty (and may be NULL) when the batch has no draft blocks
+  if (!p->d_q_off || !p->d_kv_off || (!p->d_anchor && p->h_q_off[p->n_seq] > 0))
+    return fail(SKV_EINVAL, "device offset/anchor arrays are NULL");
   return SKV_OK;
 }
 
@@ -41,7 +43,10 @@ extern "C" int sparse_attn_partial_fwd(const skv_problem* p, const skv_plan* pla
   if (rc) return rc;
   if ((rc = check_device_problem(p))) return rc;
   if ((rc = check_plan(plan, SKV_ITEM_FWD))) return rc;
-  if (!q || !k || !v || !o_part || !m_part || !lse_part) return fail(SKV_EINVAL, "tensor pointer is NULL");
+  // query-sized buffers may be NULL without query rows, K/V without context rows
+  const int64_t tq = p->h_q_off[p->n_seq], tk = p->h_kv_off[p->n_seq];
+  if ((tq && (!q || !o_part || !m_part || !lse_part)) || (tk && (!k || !v)))
+    return fail(SKV_EINVAL, "tensor pointer is NULL");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o_part))
     return fail(SKV_ESHAPE, "q, k, v and o_part must be 16-byte aligned");
   FwdArgs a{};
@@ -97,7 +102,8 @@ extern "C" int sparse_attn_own_fwd(const skv_problem* p, const void* q, const vo
   if ((rc = check_device_problem(p))) return rc;
   if ((rc = check_own_shape(p))) return rc;
   if ((rc = check_own_strides(p, own_stride_tok, own_stride_head))) return rc;
-  if (!q || !k_own || !v_own || !o_part || !m_part || !lse_part) return fail(SKV_EINVAL, "tensor pointer is NULL");
+  if (p->h_q_off[p->n_seq] && (!q || !k_own || !v_own || !o_part || !m_part || !lse_part))
+    return fail(SKV_EINVAL, "tensor pointer is NULL");  // all query-sized: NULL only without query rows
   if (!aligned16(q) || !aligned16(k_own) || !aligned16(v_own) || !aligned16(o_part))
     return fail(SKV_ESHAPE, "q, k_own, v_own and o_part must be 16-byte aligned");
   OwnFwdArgs a{};
@@ -122,7 +128,7 @@ extern "C" int lse_merge(int32_t n_part, int32_t hq, int64_t mq, int32_t d, cons
   if (mq == 0) { clear_error(); return SKV_OK; }
   if (!o_out || !lse_out || (n_part > 0 && (!o_part || !m_part || !lse_part)))
     return fail(SKV_EINVAL, "tensor pointer is NULL");
-  const int64_t vec = out_dtype == SKV_BF16 ? 4 : 4;  // 4 elements per lane store
+  const int64_t vec = 4;  // 4 elements per lane store
   if (o_stride_tok < 1 || o_stride_head < d || lse_stride_tok < hq) return fail(SKV_ESHAPE, "bad output strides");
   if (o_stride_tok % vec || o_stride_head % vec) return fail(SKV_ESHAPE, "output strides must be multiples of 4");
   if (!aligned16(o_part) || (reinterpret_cast<uintptr_t>(o_out) & 7u))
@@ -205,12 +211,15 @@ extern "C" int sparse_attn_bwd(const skv_problem* p, const skv_plan* plan_kv, co
   if (plan_kv->d_claim == plan_q->d_claim) return fail(SKV_EPLAN, "the two plans must not share claim cursors");
   if (plan_kv->d_ticks && plan_kv->d_ticks == plan_q->d_ticks)
     return fail(SKV_EPLAN, "the two plans must not share a ticks array");
-  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return fail(SKV_EINVAL, "tensor pointer is NULL");
+  // query-sized buffers may be NULL without query rows, K/V-sized ones without context rows
+  const int64_t tq = p->h_q_off[p->n_seq], tk = p->h_kv_off[p->n_seq];
+  if ((tq && (!q || !o || !lse || !dout || !dq)) || (tk && (!k || !v || !dk || !dv)))
+    return fail(SKV_EINVAL, "tensor pointer is NULL");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) || !aligned16(dq))
     return fail(SKV_ESHAPE, "q, k, v, o, dout and dq must be 16-byte aligned");
   if (p->mask == SKV_MASK_OWN_BLOCK) {
     if ((rc = check_own_shape(p))) return rc;
-    if (!own || !own->k || !own->v || !own->dk || !own->dv)
+    if (!own || (tq && (!own->k || !own->v || !own->dk || !own->dv)))
       return fail(SKV_EINVAL, "the own-block mask needs own-block keys, values and gradient outputs");
     if ((rc = check_own_strides(p, own->stride_tok, own->stride_head))) return rc;
     if (!aligned16(own->k) || !aligned16(own->v) || !aligned16(own->dk) || !aligned16(own->dv))

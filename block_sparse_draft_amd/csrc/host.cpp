@@ -56,7 +56,8 @@ extern "C" int skv_check_problem(const skv_problem* p) {
     return fail(SKV_ESHAPE, "chunk = %d must be a positive multiple of %d", p->chunk, SKV_TILE);
   if (!(std::isfinite(p->sm_scale) && p->sm_scale > 0.f))
     return fail(SKV_EINVAL, "sm_scale must be finite and > 0");
-  if (!p->h_q_off || !p->h_kv_off || !p->h_anchor) return fail(SKV_EINVAL, "host offset/anchor arrays are NULL");
+  if (!p->h_q_off || !p->h_kv_off) return fail(SKV_EINVAL, "host offset arrays are NULL");
+  if (!p->h_anchor && p->h_q_off[p->n_seq] > 0) return fail(SKV_EINVAL, "host anchor array is NULL");
   // Vector loads move 16 bytes: strides must keep every head row 16-byte aligned.
   const int64_t vec = p->dtype == SKV_BF16 ? 8 : 4;
   if (p->q_stride_head < p->d || p->kv_stride_head < p->d || p->q_stride_tok < 1 || p->kv_stride_tok < 1)

@@ -33,6 +33,9 @@
  *    other streams (a plan upload, say) must be ordered before it by the
  *    caller.  Host calls (planning, sizing) are synchronous, pure, and touch
  *    no GPU.
+ *  - A pointer may be NULL only for a buffer with no rows: query-sized ones
+ *    (Q, O, dO, dQ, LSE, partials, own-block tensors) when the batch has no
+ *    query rows, context-sized ones (K, V, dK, dV) when it has no context.
  *  - Return value: SKV_OK or a negative skv_status; the reason is available
  *    from skv_last_error() on the calling thread.  Arguments are validated
  *    before any HIP call, so validation errors leave the stream untouched.

@@ -232,6 +232,20 @@ def test_device_calls_reject_bad_arguments_before_touching_the_gpu():
     assert B.lib.lse_merge(4, 2, 0, 64, None, None, None, None, 128, 64, B.SKV_F32, None, 2, None) == B.SKV_OK
 
 
+def test_null_anchor_array_only_without_draft_blocks():
+    """A batch without draft blocks may pass NULL anchors; one with blocks may not."""
+    empty = B.Problem(np.array([0, 0, 0], np.int64), np.array([0, 300, 377], np.int64), np.zeros(0, np.int32),
+                      16, 4, 2, 128, 128, B.SKV_BF16, 0.088)
+    empty.c.h_anchor = None
+    empty.check()
+    w = make("c2", seed=0, n_ctx=4096, n_anchor=4, with_do=False)
+    p = _problem_from(w)
+    p.c.h_anchor = None
+    with pytest.raises(B.SkvError) as e:
+        p.check()
+    assert e.value.code == B.SKV_EINVAL
+
+
 def test_timing_api_without_launches():
     """Timing switches on and off and collects an empty tally without any GPU work."""
     B.timing_enable(True)

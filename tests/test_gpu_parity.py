@@ -720,6 +720,34 @@ def test_side_streams_match_the_default_stream():
 
 
 @pytest.mark.parametrize("mask", ["prefix", "own_block"])
+def test_bf16_batch_without_queries(mask):
+    """No draft blocks at all (zero query rows; empty tensors may have NULL
+    data pointers): the forward computes nothing, and the backward still writes
+    exact zeros to every dK / dV row."""
+    w = make_custom([300, 0, 77], [[], [], []], block=16, hq=4, hkv=2, d=128, dtype="bf16", chunk=128, seed=91,
+                    with_do=True)
+    if mask == "own_block":
+        add_own_block(w)
+    path = make_path(w, DEV, with_bwd=True, mask=mask)
+    q, k, v = _upload(w)
+    do = to_device(w, "do", DEV)
+    assert q.shape[0] == 0 and k.shape[0] == 377
+    dq = torch.empty_like(q)
+    dk = torch.full_like(k, float("nan"))
+    dv = torch.full_like(v, float("nan"))
+    if mask == "own_block":
+        ko, vo = _own_upload(w)
+        o, lse = path.forward(q, k, v, k_own=ko, v_own=vo)
+        path.backward(q, k, v, do, dq, dk, dv, own=(ko, vo, torch.empty_like(ko), torch.empty_like(vo)))
+    else:
+        o, lse = path.forward(q, k, v)
+        path.backward(q, k, v, do, dq, dk, dv)
+    torch.cuda.synchronize()
+    assert o.shape[0] == 0 and lse.shape[0] == 0
+    assert bool((dk == 0).all()) and bool((dv == 0).all())
+
+
+@pytest.mark.parametrize("mask", ["prefix", "own_block"])
 def test_merge_all_equals_per_sequence_merge(mask):
     """The one-launch merge of every sequence gives bitwise the per-sequence
     lse_merge results (sequences of different lengths, rows straddling
