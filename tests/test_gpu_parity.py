@@ -485,11 +485,12 @@ def test_bf16_own_block_matches_prefix_mask_when_own_keys_are_context_keys():
     assert_close("dV", dv_sum, a[4], 2 * BF16_ABS, BF16_FROB)
 
 
-def test_full_size_own_block_sampled():
-    """Own-block mask at the full c3 size in the bench's configuration (default
-    chunk runs, 256 workgroups), checked against the oracle on one sequence and
-    one KV head."""
-    w = add_own_block(make("c3", seed=0))
+@pytest.mark.parametrize("cfg,g", [("c3", 1), ("c5", 9)])
+def test_full_size_own_block_sampled(cfg, g):
+    """Own-block mask at full c3 and c5 sizes in the bench's configuration
+    (default chunk runs, 256 workgroups), checked against the oracle on one
+    sequence and one KV head (c4's shape is covered under the prefix mask)."""
+    w = add_own_block(make(cfg, seed=0))
     path = make_path(w, DEV, mask="own_block", fwd_runs_per_worker=4)
     q, k, v = _upload(w)
     ko, vo = _own_upload(w)
@@ -499,7 +500,7 @@ def test_full_size_own_block_sampled():
     path.forward(q, k, v, k_own=ko, v_own=vo)
     path.backward(q, k, v, do, dq, dk, dv, own=(ko, vo, dko, dvo))
     torch.cuda.synchronize()
-    s, g = 0, 1
+    s = 0
     G = w.cfg.hq // w.cfg.hkv
     hs = list(range(g * G, (g + 1) * G))
     qs = slice(int(w.q_off[s]), int(w.q_off[s + 1]))
