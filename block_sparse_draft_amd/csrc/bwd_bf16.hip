@@ -6,12 +6,15 @@
 // correct).  With dS = P * (dO.v - Delta), Delta = sum_x dO * O:
 //     dV_j = sum_rows P dO,   dK_j = scale * sum_rows dS q,   dQ = scale * dS K.
 //
-// Four launches on the caller's stream, none with atomics, so the result is
-// bitwise reproducible:
+// Four launches on the caller's stream (five under the own-block mask, whose
+// own keys' share runs after step 3).  No result is accumulated with atomics
+// (the only atomics are the integer cursors through which workgroups claim
+// work items), so the result is bitwise reproducible:
 //   1. preprocess: the first partial row of every sequence (for the dQ
-//      partial layout), and copies of Q, dO, LSE (log2 units), Delta and the
-//      draft block's prefix end in packed row order, so that the query tiles
-//      of both main kernels are contiguous rows.
+//      partial layout), the reset of both plans' claim cursors, and copies of
+//      Q, dO, LSE (log2 units), Delta and the draft block's prefix end in
+//      packed row order, so that the query tiles of both main kernels are
+//      contiguous rows.
 //   2. key-owner kernel (persistent workgroups of 8 waves, two per SIMD, over
 //      BWD items = (sequence, KV head, key range)): 256 keys at a time, 32 per
 //      wave, with the keys' K staged in LDS, their V operands and fp32 dK, dV
@@ -20,15 +23,16 @@
 //      blocks); the next tile's Q, dO, LSE, Delta load while the current one
 //      is computed.  S = Q K^T, dP = dO V^T (A from LDS), P and dS in
 //      registers, dV += P^T dO and dK += dS^T Q (B read transposed from LDS).
-//   3. query-owner kernel over the forward's items (sequence, KV head, chunk,
-//      draft blocks), structured like the forward: 64 rows per wave with Q
-//      in registers and dO in LDS, K/V tiles of the chunk through two LDS
-//      buffers;
-//      S^T = K Q^T, dP^T = V dO^T, dS^T, then dQ^T += K^T dS^T, with the two
-//      32-key halves of a tile software-pipelined (one half's dS work beside
-//      the other half's MFMAs).  Each item writes its chunk's dQ partial, like
-//      the forward's O partial.
-//   4. finalize: dQ = scale * sum of the row's visible chunk partials, bf16.
+//   3. query-owner kernel over the forward's items (sequence, KV head, run of
+//      consecutive chunks, draft blocks), structured like the forward: 64
+//      rows per wave with Q in registers and dO in LDS, K/V tiles of the run
+//      through two LDS buffers; S^T = K Q^T, dP^T = V dO^T, dS^T, then
+//      dQ^T += K^T dS^T, with the two 32-key halves of a tile
+//      software-pipelined (one half's dS work beside the other half's MFMAs).
+//      Each item writes one dQ partial for its run, in its first chunk's rows
+//      (with the run length beside it), like the forward's O partial.
+//   4. finalize: dQ = scale * sum of the row's run partials (and, under the
+//      own-block mask, its own-block partial), bf16.
 #include <type_traits>
 
 #include "device.h"

@@ -1,14 +1,16 @@
 // Split-KV partial forward, bf16 inputs, head_dim 128, gfx950 MFMA.
 //
-// One KV chunk's contribution to the attention of a range of draft blocks
-// (pages: Split-KV article, "Split-KV's Core Mechanism": each KV shard stays
-// local and yields a query-sized result that is later aggregated exactly).
+// The contribution of one KV chunk, or of a run of consecutive chunks, to the
+// attention of a range of draft blocks (pages: Split-KV article, "Split-KV's
+// Core Mechanism": each KV shard stays local and yields a query-sized result
+// that is later aggregated exactly).
 //
 // Persistent workgroups of 8 waves (two per SIMD, so one wave's softmax and
 // memory waits overlap the other's MFMA work): each runs the work items the
 // planner gave its worker, then claims whatever is left on other workers'
-// lists.  An item is (sequence, KV head g with its G query heads, chunk c,
-// draft blocks [lo, hi)).  Its query rows are packed block-major as
+// lists.  An item is (sequence, KV head g with its G query heads, chunks
+// c .. c + n_chunk - 1, draft blocks [lo, hi)); it writes one partial, in
+// chunk c's rows.  Its query rows are packed block-major as
 // p = ((b - lo) * G + head) * B + token, 256 rows per pass: 8 waves x 32 rows.
 // Each wave keeps its 32 Q rows in registers and the unnormalised O^T
 // (128 x 32, fp32) in accumulators.  Only the 64-key tiles that some row of
