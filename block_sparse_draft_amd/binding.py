@@ -71,7 +71,7 @@ class skv_kernel_time(C.Structure):
 
 def _load():
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run `python -m block_sparse_draft_amd.build`")
+        raise ImportError(f"{LIB_PATH} is not built; run `python block_sparse_draft_amd/build.py`")
     # torch ships its own HIP runtime.  Load it first so that libsplitkv binds
     # to that same runtime (its libamdhip64 dependency resolves to the copy
     # already in the process); two runtimes in one process do not share
