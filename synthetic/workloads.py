@@ -175,25 +175,39 @@ def make(cfg, seed: int = 0, with_do: Optional[bool] = None, **overrides) -> Wor
 
 def make_custom(n_ctx: Sequence[int], anchors: Sequence[Sequence[int]], block: int, hq: int, hkv: int,
                 d: int, dtype: str = "bf16", chunk: int = 64, seed: int = 0, with_do: bool = True,
-                name: str = "custom") -> Workload:
-    """Workload with explicit lengths and anchors (anchors are sorted here)."""
+                name: str = "custom", kv_period: Optional[int] = None) -> Workload:
+    """Workload with explicit lengths and anchors (anchors are sorted here).
+
+    ``kv_period``: K and V rows repeat with this period (row r holds the
+    values of row r mod period of one seeded draw), so that contexts of
+    millions of keys are generated in seconds.  An odd prime period keeps
+    rows that differ by a power of two distinct.
+    """
     n_anchor = len(anchors[0])
     if any(len(a) != n_anchor for a in anchors):
         raise ValueError("every sequence needs the same number of anchors")
     cfg = Config(name, 99, len(n_ctx), None, None, n_anchor, "explicit", 0, block, hq, hkv, d, dtype, chunk, with_do)
     n_ctx = np.asarray(n_ctx, dtype=np.int64)
     anc = np.concatenate([np.sort(np.asarray(a, dtype=np.int64)) for a in anchors]).astype(np.int32)
-    return _assemble(cfg, n_ctx, anc, seed, with_do)
+    return _assemble(cfg, n_ctx, anc, seed, with_do, kv_period)
 
 
-def _assemble(cfg: Config, n_ctx: np.ndarray, anchors: np.ndarray, seed: int, with_do: bool) -> Workload:
+def _kv_rows(rng: np.random.Generator, tk: int, cfg: Config, period: Optional[int]) -> np.ndarray:
+    if period is None or period >= tk:
+        return _normal(rng, (tk, cfg.hkv, cfg.d), cfg.dtype)
+    base = _normal(rng, (period, cfg.hkv, cfg.d), cfg.dtype)
+    return np.tile(base, (-(-tk // period), 1, 1))[:tk]
+
+
+def _assemble(cfg: Config, n_ctx: np.ndarray, anchors: np.ndarray, seed: int, with_do: bool,
+              kv_period: Optional[int] = None) -> Workload:
     mq = cfg.n_anchor * cfg.block
     q_off = np.arange(cfg.n_seq + 1, dtype=np.int64) * mq
     kv_off = np.concatenate([[0], np.cumsum(n_ctx)]).astype(np.int64)
     tq, tk = int(q_off[-1]), int(kv_off[-1])
     q = _normal(_rng(seed, cfg.cid, STREAM_Q), (tq, cfg.hq, cfg.d), cfg.dtype)
-    k = _normal(_rng(seed, cfg.cid, STREAM_K), (tk, cfg.hkv, cfg.d), cfg.dtype)
-    v = _normal(_rng(seed, cfg.cid, STREAM_V), (tk, cfg.hkv, cfg.d), cfg.dtype)
+    k = _kv_rows(_rng(seed, cfg.cid, STREAM_K), tk, cfg, kv_period)
+    v = _kv_rows(_rng(seed, cfg.cid, STREAM_V), tk, cfg, kv_period)
     do = _normal(_rng(seed, cfg.cid, STREAM_DO), (tq, cfg.hq, cfg.d), cfg.dtype) if with_do else None
     return Workload(cfg, n_ctx, anchors, q_off, kv_off, q, k, v, do, 1.0 / math.sqrt(cfg.d), seed)
 

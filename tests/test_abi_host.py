@@ -167,6 +167,10 @@ def test_problem_validation_codes():
     pb.c.kv_stride_tok = (1 << 30) // 1024 + 8          # 1024 rows * stride * 2 bytes > 2^31
     pb.c.kv_stride_head = 128
     assert B.lib.skv_check_problem(C.byref(pb.c)) == B.SKV_ESHAPE and "2^31" in B.last_error()
+    # packed [N, 4, 128] bf16 K/V: 2,097,151 keys (2^31 - 1024 bytes) pass, one key more does not
+    for n, code in ((2097151, B.SKV_OK), (2097152, B.SKV_ESHAPE)):
+        pm = B.Problem([0, 48], [0, n], [0, 1_048_570, n - 11], 16, 4, 4, 128, 8192, B.SKV_BF16, 0.125)
+        assert B.lib.skv_check_problem(C.byref(pm.c)) == code, n
     # unsorted anchors
     p = _problem_from(w)
     p.h_anchor[:] = p.h_anchor[::-1].copy()

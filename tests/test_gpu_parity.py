@@ -597,6 +597,63 @@ def test_bf16_more_than_64_partials_per_row(mask):
     assert_close("dV", to_np64(dv), rv, BF16_ABS, BF16_FROB)
 
 
+MAX_KV_HEADS, MAX_D = 4, 128
+MAX_N = (2**31 - 1) // (MAX_KV_HEADS * MAX_D * 2)   # 2,097,151 keys: the longest sequence the C ABI accepts
+
+
+@pytest.mark.parametrize("mask", ["prefix", "own_block"])
+def test_bf16_longest_sequence_the_abi_accepts(mask):
+    """One sequence whose packed K/V rows span 2^31 - 1024 bytes, the most that
+    32-bit buffer offsets address: the last block's window is cut at N (ragged)
+    and reaches the last key (the prefix mask; the own-block window stops 11
+    keys short of it), a middle block ends near 2^20 keys, in the bench's
+    plan (chunk runs).  Forward, backward and every gradient of KV head 3 (the
+    highest byte offsets) against the oracle over all N keys.  K/V rows repeat
+    with an odd prime period, so no power-of-two addressing error lands on an
+    identical row."""
+    n = MAX_N
+    w = make_custom([n], [[0, 1_048_570, n - 11]], block=16, hq=MAX_KV_HEADS, hkv=MAX_KV_HEADS, d=MAX_D,
+                    dtype="bf16", chunk=8192, seed=3, with_do=True, kv_period=16411)
+    if mask == "own_block":
+        add_own_block(w)
+    path = make_path(w, DEV, with_bwd=True, mask=mask, fwd_runs_per_worker=4)
+    q, k, v = _upload(w)
+    do = to_device(w, "do", DEV)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    g = MAX_KV_HEADS - 1
+    f = w.as_f64
+    q64, do64 = f("q")[:, [g]], f("do")[:, [g]]
+    k64, v64 = f("k", head=g)[:, None], f("v", head=g)[:, None]
+    if mask == "own_block":
+        ko, vo = _own_upload(w)
+        dko, dvo = torch.empty_like(ko), torch.empty_like(vo)
+        path.forward(q, k, v, k_own=ko, v_own=vo)
+        path.backward(q, k, v, do, dq, dk, dv, own=(ko, vo, dko, dvo))
+        torch.cuda.synchronize()
+        rq, rk, rv, rko, rvo, O, L = oracle.attention_own_bwd(
+            q64, k64, v64, f("k_own", head=g)[:, None], f("v_own", head=g)[:, None], w.seq_anchors(0),
+            w.cfg.block, w.sm_scale, do64)
+        assert_close("dK_own", to_np64(dko[:, g]), rko[:, 0], BF16_ABS, BF16_FROB)
+        assert_close("dV_own", to_np64(dvo[:, g]), rvo[:, 0], BF16_ABS, BF16_FROB)
+    else:
+        path.forward(q, k, v)
+        path.backward(q, k, v, do, dq, dk, dv)
+        torch.cuda.synchronize()
+        rq, rk, rv, O, L = oracle.attention_bwd(q64, k64, v64, w.seq_anchors(0), w.cfg.block, w.sm_scale, do64)
+    assert_close("O", to_np64(path.o[:, g]), O[:, 0], BF16_ABS, BF16_FROB)
+    assert_lse("LSE", to_np64(path.lse[:, g]), L[:, 0], BF16_LSE_REL)
+    assert_close("dQ", to_np64(dq[:, g]), rq[:, 0], BF16_ABS, BF16_FROB)
+    del k64, v64
+    assert_close("dK", to_np64(dk[:, g]), rk[:, 0], BF16_ABS, BF16_FROB)
+    assert_close("dV", to_np64(dv[:, g]), rv[:, 0], BF16_ABS, BF16_FROB)
+    # the prefix mask's last window reaches key N - 1; the own-block mask's
+    # ends at its anchor, N - 11, and the 11 keys after it get exactly zero
+    last = n - 1 if mask == "prefix" else n - 12
+    assert np.abs(rk[last, 0]).max() > 0 and np.abs(rv[last, 0]).max() > 0
+    if mask == "own_block":
+        assert not torch.any(dk[last + 1:]) and not torch.any(dv[last + 1:])
+
+
 ODD_SHAPES = {
     # (block, hq, hkv): rows per (draft block, KV head) G*B = 16, 15, 1 and 80, so
     # the 32-row query tiles of the backward end in padding rows and the packed
