@@ -79,6 +79,9 @@ extern "C" int skv_check_problem(const skv_problem* p) {
     for (int64_t b = 0; b < v.n_blk; ++b) {
       const int32_t a = p->h_anchor[v.blk0 + b];
       if (a < 0) return fail(SKV_EINVAL, "anchor %lld of sequence %d is negative", (long long)b, s);
+      // kernels form a + block in 32-bit arithmetic
+      if (a > INT32_MAX - p->block)
+        return fail(SKV_EINVAL, "anchor %lld of sequence %d exceeds 2^31 - 1 - block", (long long)b, s);
       if (b > 0 && a < p->h_anchor[v.blk0 + b - 1])
         return fail(SKV_EINVAL, "anchors of sequence %d are not sorted ascending", s);
     }

@@ -97,7 +97,8 @@ typedef struct skv_problem {
   int32_t reserved;       /* 0 */
   const int64_t *h_q_off, *d_q_off;    /* [n_seq+1], multiples of block, non-decreasing */
   const int64_t *h_kv_off, *d_kv_off;  /* [n_seq+1], non-decreasing */
-  const int32_t *h_anchor, *d_anchor;  /* [q_off[n_seq]/block], >= 0, sorted per sequence */
+  const int32_t *h_anchor, *d_anchor;  /* [q_off[n_seq]/block], 0 <= a <= 2^31-1-block, sorted per sequence;
+                                        anchors past the context act as N (the whole context) */
   int64_t q_stride_tok, q_stride_head;   /* elements; head_dim is contiguous */
   int64_t kv_stride_tok, kv_stride_head; /* elements; head_dim is contiguous */
 } skv_problem;

@@ -171,6 +171,10 @@ def test_problem_validation_codes():
     for n, code in ((2097151, B.SKV_OK), (2097152, B.SKV_ESHAPE)):
         pm = B.Problem([0, 48], [0, n], [0, 1_048_570, n - 11], 16, 4, 4, 128, 8192, B.SKV_BF16, 0.125)
         assert B.lib.skv_check_problem(C.byref(pm.c)) == code, n
+    # anchors past the context are allowed (they see all of it) up to 2^31 - 1 - block
+    for a_last, code in ((5000, B.SKV_OK), (2**31 - 1 - 16, B.SKV_OK), (2**31 - 16, B.SKV_EINVAL)):
+        pa = B.Problem([0, 32], [0, 1024], [3, a_last], 16, 4, 4, 128, 256, B.SKV_BF16, 0.125)
+        assert B.lib.skv_check_problem(C.byref(pa.c)) == code, a_last
     # unsorted anchors
     p = _problem_from(w)
     p.h_anchor[:] = p.h_anchor[::-1].copy()

@@ -830,3 +830,68 @@ def test_merge_all_equals_per_sequence_merge(mask):
     assert torch.equal(path.o, o1) and torch.equal(path.lse, l1)
     O, L = oracle.attention_own_workload(w) if mask == "own_block" else oracle.attention_workload(w)
     _check_merged(path, w, O, L)
+
+
+# ---------------------------------------------------------------------------
+# seeded random problems: shapes, masks and plans drawn together
+# ---------------------------------------------------------------------------
+
+def _random_problem(seed):
+    """One random problem: 1-4 sequences of 0-3000 keys, 1-6 anchors each
+    (some past the context end), any draft-block size up to 64, GQA groups of
+    1-8, chunks of 64-1024 keys, either mask where its limits allow, and a
+    random plan (LPT with or without chunk runs, or static; 1-256 workgroups;
+    stealing on or off; backward key ranges of 64-512)."""
+    r = np.random.default_rng([71, seed])
+    n_seq = int(r.integers(1, 5))
+    hkv = int(r.choice([1, 2, 4]))
+    group = int(r.choice([1, 2, 3, 4, 8]))
+    block = int(r.choice([1, 2, 3, 5, 8, 13, 16, 32, 64]))
+    lens = [int(x) for x in r.integers(0, 3001, size=n_seq)]
+    if r.random() < 0.2:
+        lens[int(r.integers(n_seq))] = 0
+    n_anchor = int(r.integers(1, 7))
+    anchors = [[int(x) for x in r.integers(0, n + 9, size=n_anchor)] for n in lens]
+    own_ok = group * block * block <= 8192
+    mask = "own_block" if own_ok and r.random() < 0.5 else "prefix"
+    policy = "static" if r.random() < 0.2 else "lpt"
+    plan = dict(n_workers=int(r.choice([1, 5, 64, 256])), steal=bool(r.random() < 0.7), policy=policy,
+                bwd_granule=int(r.choice([64, 128, 256, 512])),
+                fwd_runs_per_worker=[None, 1, 2, 4][int(r.integers(4))], fwd_run_imbalance=None)
+    w = make_custom(lens, anchors, block=block, hq=hkv * group, hkv=hkv, d=128, dtype="bf16",
+                    chunk=int(r.choice([64, 128, 256, 512, 1024])), seed=1000 + seed, with_do=True)
+    if mask == "own_block":
+        add_own_block(w)
+    return w, mask, plan
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_bf16_random_problems(seed):
+    w, mask, plan = _random_problem(seed)
+    c = w.cfg
+    print(f"seed {seed}: lens {list(w.n_ctx)}, anchors/seq {c.n_anchor}, block {c.block}, hq {c.hq}, "
+          f"hkv {c.hkv}, chunk {c.chunk}, mask {mask}, plan {plan}", flush=True)
+    path = make_path(w, DEV, with_bwd=True, mask=mask, **plan)
+    q, k, v = _upload(w)
+    do = to_device(w, "do", DEV)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    if mask == "own_block":
+        ko, vo = _own_upload(w)
+        dko, dvo = torch.empty_like(ko), torch.empty_like(vo)
+        path.forward(q, k, v, k_own=ko, v_own=vo)
+        path.backward(q, k, v, do, dq, dk, dv, own=(ko, vo, dko, dvo))
+        torch.cuda.synchronize()
+        O, L = oracle.attention_own_workload(w)
+        rq, rk, rv, rko, rvo = oracle.bwd_own_workload(w)
+        assert_close("dK_own", to_np64(dko), rko, BF16_ABS, BF16_FROB)
+        assert_close("dV_own", to_np64(dvo), rvo, BF16_ABS, BF16_FROB)
+    else:
+        path.forward(q, k, v)
+        path.backward(q, k, v, do, dq, dk, dv)
+        torch.cuda.synchronize()
+        O, L = oracle.attention_workload(w)
+        rq, rk, rv = oracle.bwd_workload(w)[:3]
+    _check_merged(path, w, O, L)
+    assert_close("dQ", to_np64(dq), rq, BF16_ABS, BF16_FROB)
+    assert_close("dK", to_np64(dk), rk, BF16_ABS, BF16_FROB)
+    assert_close("dV", to_np64(dv), rv, BF16_ABS, BF16_FROB)
