@@ -836,13 +836,14 @@ def test_merge_all_equals_per_sequence_merge(mask):
 # seeded random problems: shapes, masks and plans drawn together
 # ---------------------------------------------------------------------------
 
-def _random_problem(seed):
+def _random_problem(seed, dtype="bf16"):
     """One random problem: 1-4 sequences of 0-3000 keys, 1-6 anchors each
     (some past the context end), any draft-block size up to 64, GQA groups of
     1-8, chunks of 64-1024 keys, either mask where its limits allow, and a
     random plan (LPT with or without chunk runs, or static; 1-256 workgroups;
-    stealing on or off; backward key ranges of 64-512)."""
-    r = np.random.default_rng([71, seed])
+    stealing on or off; backward key ranges of 64-512); fp32 problems also
+    draw a head dim of 64 or 128."""
+    r = np.random.default_rng([71 if dtype == "bf16" else 72, seed])
     n_seq = int(r.integers(1, 5))
     hkv = int(r.choice([1, 2, 4]))
     group = int(r.choice([1, 2, 3, 4, 8]))
@@ -858,8 +859,9 @@ def _random_problem(seed):
     plan = dict(n_workers=int(r.choice([1, 5, 64, 256])), steal=bool(r.random() < 0.7), policy=policy,
                 bwd_granule=int(r.choice([64, 128, 256, 512])),
                 fwd_runs_per_worker=[None, 1, 2, 4][int(r.integers(4))], fwd_run_imbalance=None)
-    w = make_custom(lens, anchors, block=block, hq=hkv * group, hkv=hkv, d=128, dtype="bf16",
-                    chunk=int(r.choice([64, 128, 256, 512, 1024])), seed=1000 + seed, with_do=True)
+    d = 128 if dtype == "bf16" else int(r.choice([64, 128]))
+    w = make_custom(lens, anchors, block=block, hq=hkv * group, hkv=hkv, d=d, dtype=dtype,
+                    chunk=int(r.choice([64, 128, 256, 512, 1024])), seed=1000 + seed, with_do=dtype == "bf16")
     if mask == "own_block":
         add_own_block(w)
     return w, mask, plan
@@ -895,3 +897,24 @@ def test_bf16_random_problems(seed):
     assert_close("dQ", to_np64(dq), rq, BF16_ABS, BF16_FROB)
     assert_close("dK", to_np64(dk), rk, BF16_ABS, BF16_FROB)
     assert_close("dV", to_np64(dv), rv, BF16_ABS, BF16_FROB)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_fp32_random_problems_forward(seed):
+    """The fp32 forward and merge on random problems drawn as above."""
+    w, mask, plan = _random_problem(seed, dtype="f32")
+    c = w.cfg
+    print(f"seed {seed}: lens {list(w.n_ctx)}, anchors/seq {c.n_anchor}, block {c.block}, hq {c.hq}, "
+          f"hkv {c.hkv}, d {c.d}, chunk {c.chunk}, mask {mask}, plan {plan}", flush=True)
+    path = make_path(w, DEV, mask=mask, **plan)
+    q, k, v = _upload(w)
+    if mask == "own_block":
+        ko, vo = _own_upload(w)
+        path.forward(q, k, v, k_own=ko, v_own=vo)
+        torch.cuda.synchronize()
+        O, L = oracle.attention_own_workload(w)
+    else:
+        path.forward(q, k, v)
+        torch.cuda.synchronize()
+        O, L = oracle.attention_workload(w)
+    _check_merged(path, w, O, L, abs_tol=F32_ABS, frob_tol=None, lse_tol=F32_ABS)
