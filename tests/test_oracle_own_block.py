@@ -87,3 +87,10 @@ def test_anchor_zero_sees_only_its_own_block_like_sdpa():
     # the own partial alone, merged with nothing, is the same output
     o, m, lse = oracle.own_partial(q, ko, vo, B, w.sm_scale, w.cfg.hkv)
     np.testing.assert_allclose((o * np.exp(m - lse)[..., None]).transpose(1, 0, 2), O[0:B], rtol=0, atol=1e-12)
+    # its max and log-sum-exp (and the merged LSE of an anchor-0 block) are
+    # those of the own-block scores, from torch's max and logsumexp
+    for h in range(w.cfg.hq):
+        s = w.sm_scale * (torch.from_numpy(q[:, h]) @ torch.from_numpy(ko[:, h // G]).T)
+        np.testing.assert_allclose(m[h], s.max(dim=-1).values.numpy(), rtol=0, atol=1e-12)
+        np.testing.assert_allclose(lse[h], torch.logsumexp(s, dim=-1).numpy(), rtol=0, atol=1e-12)
+        np.testing.assert_allclose(L[0:B, h], torch.logsumexp(s, dim=-1).numpy(), rtol=0, atol=1e-12)
