@@ -64,7 +64,10 @@ extern "C" int skv_check_problem(const skv_problem* p) {
     return fail(SKV_ESHAPE, "strides must be positive and head strides >= d");
   if (p->q_stride_tok % vec || p->q_stride_head % vec || p->kv_stride_tok % vec || p->kv_stride_head % vec)
     return fail(SKV_ESHAPE, "strides must be multiples of %lld elements (16 bytes)", (long long)vec);
-  if (p->h_q_off[0] < 0 || p->h_kv_off[0] < 0) return fail(SKV_EINVAL, "offsets must be >= 0");
+  // Query rows start at row 0: the kernels that walk every row of the batch
+  // (packing, merge, finalize, own-block) index rows from 0 up to q_off[n_seq].
+  if (p->h_q_off[0] != 0) return fail(SKV_EINVAL, "q_off[0] = %lld must be 0", (long long)p->h_q_off[0]);
+  if (p->h_kv_off[0] < 0) return fail(SKV_EINVAL, "kv_off[0] must be >= 0");
   for (int s = 0; s < p->n_seq; ++s) {
     const int64_t q0 = p->h_q_off[s], q1 = p->h_q_off[s + 1];
     const int64_t k0 = p->h_kv_off[s], k1 = p->h_kv_off[s + 1];

@@ -95,7 +95,7 @@ typedef struct skv_problem {
   float sm_scale;         /* logit scale, finite and > 0 (usually 1/sqrt(d)) */
   int32_t mask;           /* skv_mask: SKV_MASK_PREFIX (0) or SKV_MASK_OWN_BLOCK */
   int32_t reserved;       /* 0 */
-  const int64_t *h_q_off, *d_q_off;    /* [n_seq+1], multiples of block, non-decreasing */
+  const int64_t *h_q_off, *d_q_off;    /* [n_seq+1], multiples of block, non-decreasing, q_off[0] = 0 */
   const int64_t *h_kv_off, *d_kv_off;  /* [n_seq+1], non-decreasing */
   const int32_t *h_anchor, *d_anchor;  /* [q_off[n_seq]/block], 0 <= a <= 2^31-1-block, sorted per sequence;
                                         anchors past the context act as N (the whole context) */

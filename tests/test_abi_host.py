@@ -175,6 +175,12 @@ def test_problem_validation_codes():
     for a_last, code in ((5000, B.SKV_OK), (2**31 - 1 - 16, B.SKV_OK), (2**31 - 16, B.SKV_EINVAL)):
         pa = B.Problem([0, 32], [0, 1024], [3, a_last], 16, 4, 4, 128, 256, B.SKV_BF16, 0.125)
         assert B.lib.skv_check_problem(C.byref(pa.c)) == code, a_last
+    # query rows start at row 0 (kernels that walk the whole batch index rows from 0)
+    for q_off, code in (([0, 48], B.SKV_OK), ([16, 48], B.SKV_EINVAL)):
+        pq = B.Problem(q_off, [0, 1024], [3, 5, 7][:q_off[1] // 16], 16, 4, 4, 128, 256,
+                       B.SKV_BF16, 0.125)
+        assert B.lib.skv_check_problem(C.byref(pq.c)) == code, q_off
+    assert "q_off[0]" in B.last_error()
     # unsorted anchors
     p = _problem_from(w)
     p.h_anchor[:] = p.h_anchor[::-1].copy()
