@@ -7,7 +7,7 @@ Importing the package fails if the library has not been built.
 """
 from . import binding  # noqa: F401  (raises ImportError when libsplitkv.so is missing)
 from .binding import (  # noqa: F401
-    Plan, Problem, SkvError, lpt_plan, lse_merge, lse_merge_all, skv_coarsen_fwd_items, skv_drop_zero_cost,
-    skv_gather_items, skv_static_plan, sparse_attn_bwd, sparse_attn_own_fwd, sparse_attn_partial_fwd,
+    Problem, SkvError, lpt_plan, lse_merge, lse_merge_all, skv_coarsen_fwd_items, skv_drop_zero_cost,
+    skv_gather_items, skv_plan_fwd_runs, skv_static_plan, sparse_attn_bwd, sparse_attn_own_fwd, sparse_attn_partial_fwd,
 )
 from .path import SplitKVAttention, unmasked_pairs  # noqa: F401

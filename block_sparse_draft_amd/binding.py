@@ -89,6 +89,8 @@ def _load():
         "skv_gather_items": (C.c_int, [VP, I64, VP, I64, VP]),
         "skv_drop_zero_cost": (C.c_int, [VP, I64, I32, VP, VP, VP, VP, P(I64)]),
         "skv_coarsen_fwd_items": (C.c_int, [VP, VP, I64, I64, VP, VP, P(I64)]),
+        "skv_plan_fwd_runs": (C.c_int, [VP, VP, I64, I32, I32, I32, C.c_double, VP, VP, P(I64), VP, VP, VP,
+                                        P(I32)]),
         "sparse_attn_partial_fwd": (C.c_int, [P(skv_problem), P(skv_plan), VP, VP, VP, VP, VP, VP, VP]),
         "lse_merge": (C.c_int, [I32, I32, I64, I32, VP, VP, VP, VP, I64, I64, I32, VP, I64, VP]),
         "skv_bwd_workspace_bytes": (C.c_size_t, [P(skv_problem)]),
@@ -108,6 +110,7 @@ def _load():
 lib = _load()
 EXPORTED = ("skv_last_error", "skv_check_problem", "skv_partial_layout", "skv_item_table", "lpt_plan",
             "skv_static_plan", "skv_gather_items", "skv_drop_zero_cost", "skv_coarsen_fwd_items",
+            "skv_plan_fwd_runs",
             "sparse_attn_partial_fwd", "lse_merge", "lse_merge_all",
             "skv_bwd_workspace_bytes", "sparse_attn_bwd", "sparse_attn_own_fwd", "skv_timing_enable",
             "skv_timing_collect")
@@ -215,6 +218,27 @@ def skv_coarsen_fwd_items(items, cost, target: int):
     return it2[:m.value].copy(), c2[:m.value].copy()
 
 
+def skv_plan_fwd_runs(items, cost, n_workers: int, runs_per_worker: int, max_runs_per_worker: int,
+                      max_imbalance: float):
+    """Chunk runs and their LPT plan, with the run length chosen by the
+    library's search.  Returns (items, cost, order, worker_off, load, rpw_used)."""
+    items = np.ascontiguousarray(items, dtype=ITEM_DTYPE)
+    cost = np.ascontiguousarray(cost, dtype=np.int64)
+    n = len(cost)
+    it2 = np.empty(max(n, 1), ITEM_DTYPE)
+    c2 = np.empty(max(n, 1), np.int64)
+    order = np.empty(max(n, 1), np.int64)
+    off = np.empty(n_workers + 1 if n_workers > 0 else 1, np.int64)
+    load = np.empty(max(n_workers, 1), np.int64)
+    m = C.c_int64(0)
+    rpw = C.c_int32(0)
+    _check(lib.skv_plan_fwd_runs(_ptr(items), _ptr(cost), n, n_workers, int(runs_per_worker),
+                                 int(max_runs_per_worker), float(max_imbalance), _ptr(it2), _ptr(c2), C.byref(m),
+                                 _ptr(order), _ptr(off), _ptr(load), C.byref(rpw)))
+    k = m.value
+    return it2[:k].copy(), c2[:k].copy(), order[:k].copy(), off, load, rpw.value
+
+
 class Problem:
     """A skv_problem plus the host and device arrays it points to.
 
@@ -278,39 +302,11 @@ class Problem:
         return int(lib.skv_bwd_workspace_bytes(C.byref(self.c)))
 
 
-class Plan:
-    """A device plan (items in worker order + worker offsets) and its host record."""
-
-    def __init__(self, problem: Problem, kind: int, granule: int, n_workers: int, policy: str = "lpt"):
-        import torch
-        items, cost, tok, total = problem.item_table(kind, granule)
-        if policy == "lpt":
-            assign, order, off, load = lpt_plan(cost, n_workers)
-        elif policy == "static":
-            assign, order, off = skv_static_plan(tok, total, n_workers)
-            load = np.bincount(assign, weights=cost, minlength=n_workers).astype(np.int64)
-        else:
-            raise ValueError(policy)
-        self.kind, self.granule, self.n_workers, self.policy = kind, granule, n_workers, policy
-        self.items, self.cost, self.assign, self.order, self.worker_off, self.load = items, cost, assign, order, off, load
-        self.h_items = skv_gather_items(items, order)
-        self.d_items = torch.from_numpy(self.h_items.view(np.uint8).copy()).to(problem.device)
-        self.d_worker_off = torch.from_numpy(off).to(problem.device)
-        self.d_claim = torch.zeros(n_workers, dtype=torch.int32, device=problem.device)
-        self.c = skv_plan(kind, n_workers, len(items), self.d_items.data_ptr(), self.d_worker_off.data_ptr(),
-                          self.d_claim.data_ptr(), 0, 0, None)
-
-    @property
-    def imbalance(self) -> float:
-        mean = self.load.mean()
-        return float(self.load.max() / mean - 1.0) if mean > 0 else 0.0
-
-
 # ---------------------------------------------------------------------------
 # Device calls (asynchronous on the given / current stream)
 # ---------------------------------------------------------------------------
 
-def sparse_attn_partial_fwd(problem: Problem, plan: Plan, q, k, v, o_part, m_part, lse_part, stream=None):
+def sparse_attn_partial_fwd(problem: Problem, plan, q, k, v, o_part, m_part, lse_part, stream=None):
     _check(lib.sparse_attn_partial_fwd(C.byref(problem.c), C.byref(plan.c), _ptr(q), _ptr(k), _ptr(v),
                                        _ptr(o_part), _ptr(m_part), _ptr(lse_part), _stream(stream)))
 

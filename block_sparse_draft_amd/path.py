@@ -125,21 +125,16 @@ class _PlanSlots:
         if self.runs_per_worker and self.kind == B.SKV_ITEM_FWD:
             if self.policy != "lpt":
                 raise ValueError("chunk runs are planned with LPT only")
-            # Longer runs mean fewer partials but coarser items: halve the run
-            # cost until LPT balances the runs to within RUN_IMBALANCE (or
-            # MAX_RUNS_PER_WORKER is reached).
-            rpw = self.runs_per_worker
-            while True:
-                target = max(1, int(np.ceil(cost.sum() / (self.n_workers * rpw))))
-                r_items, r_cost = B.skv_coarsen_fwd_items(items, cost, target)
-                _, order, off, load = B.lpt_plan(r_cost, self.n_workers)
-                mean = load.mean()
-                if (self.run_imbalance is None or rpw >= MAX_RUNS_PER_WORKER or mean == 0
-                        or load.max() / mean - 1.0 <= self.run_imbalance):
-                    break
-                rpw *= 2
-            items, cost = r_items, r_cost
-            self.runs_used = rpw
+            # Longer runs mean fewer partials but coarser items: the library
+            # doubles the runs per worker until LPT balances the runs to within
+            # run_imbalance (or MAX_RUNS_PER_WORKER is reached).
+            start = int(self.runs_per_worker)
+            if self.run_imbalance is None:   # keep runs_per_worker as given
+                stop, tol = start, 0.0
+            else:
+                stop, tol = max(start, MAX_RUNS_PER_WORKER), self.run_imbalance
+            items, cost, order, off, load, self.runs_used = B.skv_plan_fwd_runs(
+                items, cost, self.n_workers, start, stop, tol)
         self.table = (items, cost)  # the items planned (chunk runs when asked for)
         if self.policy == "lpt":
             if not (self.runs_per_worker and self.kind == B.SKV_ITEM_FWD):

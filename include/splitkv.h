@@ -225,7 +225,32 @@ int skv_drop_zero_cost(const int64_t* cost, int64_t n, int32_t n_workers, const 
 int skv_coarsen_fwd_items(const skv_item* items, const int64_t* cost, int64_t n, int64_t target,
                           skv_item* items_out, int64_t* cost_out, int64_t* n_out);
 
-/* Forward partials, one per (sequence, KV chunk).  For every query row r of
+/* Forward plan over chunk runs (host, pure): picks how long the runs of
+ * skv_coarsen_fwd_items are and plans them with lpt_plan.  Longer runs mean
+ * fewer partials to write and merge but coarser items, so the search starts
+ * at rpw = runs_per_worker runs per worker and doubles rpw until LPT balances
+ * the runs well enough:
+ *   target = ceil(total / (n_workers * rpw))  (total = sum of cost, >= 1)
+ *   runs   = skv_coarsen_fwd_items(items, cost, target)
+ *   plan   = lpt_plan(run costs, n_workers)
+ * stopping at the first rpw with max(load)/mean(load) - 1 <= max_imbalance
+ * (mean in double precision), with rpw >= max_runs_per_worker, or with a
+ * zero total.  Inputs as for skv_coarsen_fwd_items; runs_per_worker >= 1,
+ * max_runs_per_worker >= runs_per_worker, max_imbalance >= 0.  Outputs:
+ * items_out, cost_out [n] (first *n_out used: the runs), order [n] (first
+ * *n_out used: run indices grouped by worker), worker_off [n_workers+1],
+ * load [n_workers], *rpw_used (the rpw of the returned plan).  Zero-cost runs
+ * stay in the plan (skv_drop_zero_cost removes them). */
+int skv_plan_fwd_runs(const skv_item* items, const int64_t* cost, int64_t n, int32_t n_workers,
+                      int32_t runs_per_worker, int32_t max_runs_per_worker, double max_imbalance,
+                      skv_item* items_out, int64_t* cost_out, int64_t* n_out, int64_t* order, int64_t* worker_off,
+                      int64_t* load, int32_t* rpw_used);
+
+/* Forward partials, one per (sequence, KV chunk): the shard-local step of
+ * Split-KV (article "Split-KV: Breaking the Context Parallelism Bottleneck in
+ * Diffusion Drafter Training", section "Split-KV's Core Mechanism": each KV
+ * shard stays where it is and computes attention of the full query set
+ * against its own keys, giving a query-sized result).  For every query row r of
  * sequence s, query head h and chunk c with visible keys
  * J = {j in [c*L, min((c+1)*L, N_s)) : j < e_b}:
  *   m_part   = max_{j in J} s_j                        (s_j = sm_scale*q.k_j)
@@ -245,16 +270,6 @@ int skv_coarsen_fwd_items(const skv_item* items, const int64_t* cost, int64_t n,
 int sparse_attn_partial_fwd(const skv_problem* p, const skv_plan* plan, const void* q, const void* k,
                             const void* v, float* o_part, float* m_part, float* lse_part, void* stream);
 
-/* Exact log-sum-exp merge of n_part partials of one sequence.
- * Inputs: o_part [n_part][hq][mq][d], m_part and lse_part [n_part][hq][mq]
- * (fp32, the layout sparse_attn_partial_fwd writes for one sequence: pass
- * pointers offset to part_base[s]).  Per row (h, r):
- *   M = max_c lse_c,  LSE = M + ln sum_c exp(lse_c - M),
- *   O = sum_{c : lse_c > -inf} exp(m_c - LSE) * o_c
- * (o_c rows of partials with lse_c = -inf are never read).  A row with every
- * lse_c = -inf gets O = 0 and LSE = -inf.  O is written in out_dtype at
- * o_out + r*o_stride_tok + h*o_stride_head (+ x); LSE at lse_out[r*lse_stride_tok + h].
- * n_part may be 0.  Bitwise deterministic. */
 /* The own-block partial of every draft row (SKV_MASK_OWN_BLOCK only): for
  * row r of block b, query head h and the block's own keys J (its `block`
  * draft tokens, KV head h / (hq/hkv)), the same m_part / o_part / lse_part
@@ -269,6 +284,20 @@ int sparse_attn_own_fwd(const skv_problem* p, const void* q, const void* k_own, 
                         int64_t own_stride_tok, int64_t own_stride_head, float* o_part, float* m_part,
                         float* lse_part, void* stream);
 
+/* Exact log-sum-exp merge of n_part partials of one sequence: the exact
+ * aggregation of the shard results (article "Split-KV: Breaking the Context
+ * Parallelism Bottleneck in Diffusion Drafter Training", section "Split-KV's
+ * Core Mechanism": the query-sized results are combined exactly, so the
+ * output equals attention over the unsharded context).
+ * Inputs: o_part [n_part][hq][mq][d], m_part and lse_part [n_part][hq][mq]
+ * (fp32, the layout sparse_attn_partial_fwd writes for one sequence: pass
+ * pointers offset to part_base[s]).  Per row (h, r):
+ *   M = max_c lse_c,  LSE = M + ln sum_c exp(lse_c - M),
+ *   O = sum_{c : lse_c > -inf} exp(m_c - LSE) * o_c
+ * (o_c rows of partials with lse_c = -inf are never read).  A row with every
+ * lse_c = -inf gets O = 0 and LSE = -inf.  O is written in out_dtype at
+ * o_out + r*o_stride_tok + h*o_stride_head (+ x); LSE at lse_out[r*lse_stride_tok + h].
+ * n_part may be 0.  Bitwise deterministic. */
 int lse_merge(int32_t n_part, int32_t hq, int64_t mq, int32_t d, const float* o_part, const float* m_part,
               const float* lse_part, void* o_out, int64_t o_stride_tok, int64_t o_stride_head, int32_t out_dtype,
               float* lse_out, int64_t lse_stride_tok, void* stream);
@@ -290,7 +319,12 @@ int lse_merge_all(const skv_problem* p, const int64_t* d_part_base, const float*
  * invalid problem. */
 size_t skv_bwd_workspace_bytes(const skv_problem* p);
 
-/* Backward of O with respect to Q, K, V, reusing the merged LSE.
+/* Backward of O with respect to Q, K, V, reusing the merged LSE (article
+ * "Split-KV: Breaking the Context Parallelism Bottleneck in Diffusion Drafter
+ * Training", section "Split-KV's Core Mechanism": the sharded result equals
+ * the unsharded one, which the article ties to correct gradients in training;
+ * so the backward works from the merged statistics as unsharded attention
+ * would).
  * With P = exp(s - LSE) on visible entries (0 elsewhere), Delta = sum_x dO*O,
  * dS = P*(dO.v - Delta):  dV_j = sum P dO,  dQ = sm_scale * dS K,
  * dK_j = sm_scale * sum dS q, summed over the query heads of each KV head.

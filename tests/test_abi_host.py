@@ -341,6 +341,54 @@ def test_coarsen_fwd_items_any_input_order(seed):
     assert (length > 1).any()
 
 
+def _oracle_run_search(desc, cost, n_workers, start, stop, tol):
+    """The run-length search restated on the oracle: double the runs per worker
+    until LPT over the oracle's runs balances them to within tol."""
+    rpw = start
+    total = int(np.asarray(cost, dtype=np.int64).sum())
+    while True:
+        target = max(1, -(-total // (n_workers * rpw)))
+        first, length, rcost = oracle.coarsen_runs(desc, cost, target)
+        _, order, off, load = oracle.lpt(rcost, n_workers)
+        mean = total / n_workers
+        if rpw >= stop or mean == 0 or load.max() / mean - 1.0 <= tol:
+            return first, length, rcost, order, off, load, rpw
+        rpw = min(2 * rpw, stop)
+
+
+@pytest.mark.parametrize("cfg,n_workers,start,stop,tol", [
+    ("c3", 256, 4, 64, 0.02), ("c5", 256, 4, 64, 0.02), ("c4", 256, 4, 64, 0.02),
+    ("c3", 13, 1, 64, 0.0), ("c5", 64, 2, 2, 0.02), ("c3", 256, 4, 64, 1e9)])
+def test_plan_fwd_runs_matches_oracle_search(cfg, n_workers, start, stop, tol):
+    """skv_plan_fwd_runs picks the same run length as the search over the
+    oracle's runs and LPT, and returns the same runs and plan (bit-exact)."""
+    w = _meta_only(cfg, {})
+    p = _problem_from(w)
+    granule = max(1, 256 // ((w.cfg.hq // w.cfg.hkv) * w.cfg.block))
+    items, cost, _, _ = p.item_table(B.SKV_ITEM_FWD, granule)
+    it2, c2, order, off, load, rpw = B.skv_plan_fwd_runs(items, cost, n_workers, start, stop, tol)
+    desc, ocost, _, _ = _oracle_table(w, "fwd", granule)
+    first, length, rcost, oorder, ooff, oload, orpw = _oracle_run_search(desc, ocost, n_workers, start, stop, tol)
+    assert rpw == orpw
+    assert np.array_equal(c2, rcost) and np.array_equal(it2["n_chunk"], length)
+    for f in ("seq", "kv_head", "chunk", "lo", "hi", "part_base"):
+        assert np.array_equal(it2[f], items[first][f]), f
+    assert np.array_equal(order, oorder) and np.array_equal(off, ooff) and np.array_equal(load, oload)
+
+
+def test_plan_fwd_runs_rejects_bad_input():
+    w = make("c2", seed=0, n_ctx=4096, n_anchor=4, with_do=False)
+    p = _problem_from(w)
+    items, cost, _, _ = p.item_table(B.SKV_ITEM_FWD, 1)
+    for args in ((0, 4, 0.02), (4, 2, 0.02), (4, 8, -1.0), (4, 8, float("nan"))):
+        with pytest.raises(B.SkvError):
+            B.skv_plan_fwd_runs(items, cost, 8, *args)
+    with pytest.raises(B.SkvError):
+        B.skv_plan_fwd_runs(items, cost, 0, 4, 8, 0.02)
+    it2, c2, order, off, load, rpw = B.skv_plan_fwd_runs(items[:0], cost[:0], 8, 4, 8, 0.02)
+    assert len(c2) == 0 and rpw == 4 and off[-1] == 0
+
+
 def test_coarsen_fwd_items_rejects_bad_input():
     w = make("c2", seed=0, n_ctx=4096, n_anchor=4, with_do=False)
     p = _problem_from(w)
