@@ -12,11 +12,14 @@ kernel, dQ finalize).  Inputs are resident in HBM before the timed region.
 Prints ONE JSON line.  ``value`` is unmasked fwd+bwd TFLOP/s: 4*d (forward) +
 10*d (backward, including the QK^T recompute that reusing the LSE needs) FLOPs
 per token-exact visible (query head, query row, key) triple, divided by the
-wall time of the K timed steps.  Per-kernel times come from HIP events recorded
-on the stream the kernels run on; the library brackets each of its own
-launches with events as well (skv_timing_*), which gives the per-kernel
-durations behind ``roofline``.  ``cpu_baseline`` times the float64 CPU oracle on
-a bounded sample of the same workload on this host.
+wall time of the K timed steps, which record no events.  A second pass of K
+steps is instrumented: HIP events on the stream time the phases, and the
+library brackets each of its own launches with events on the stream it runs on
+(skv_timing_*), which gives the per-kernel durations behind ``roofline``; each
+workgroup's busy time (s_memrealtime) gives the measured balance in ``plan``.
+``cpu_baseline`` times the float64 CPU oracle on a bounded sample of the same
+workload on this host, with BLAS on every core the process may use, and the
+oracle's LPT on the step's item sets.
 
     --plan-compare     also run the workload under static and LPT plans, with
                        and without tail stealing, and report cost-model and
@@ -62,16 +65,19 @@ def merge_bytes(path, d: int) -> int:
     return rows * 8 + visible * d * 4 + out_rows * (d * out_el + 4)
 
 
-def cpu_baseline(w, budget_s: float = 12.0, mask: str = "prefix"):
+def cpu_baseline(w, budget_s: float = 12.0, mask: str = "prefix", lpt_costs=None, n_workers: int = 256):
     """Time the float64 oracle (forward + backward) on (sequence, KV head) slices
     of the workload until ~budget_s of CPU work; report unmasked TFLOP/s on the
-    same 14*d-per-triple convention."""
+    same 14*d-per-triple convention.  BLAS runs on every core this process may
+    use (``cores``).  ``lpt_costs``: item costs (name -> int64 array) on which
+    the oracle's LPT is timed as well, for comparison with the library's."""
     import oracle
+    cores = len(os.sched_getaffinity(0))
     try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        from threadpoolctl import threadpool_limits
+        limits = threadpool_limits(limits=cores)
     except Exception:  # pragma: no cover
-        cores = len(os.sched_getaffinity(0))
+        limits = None
     c = w.cfg
     G = c.hq // c.hkv
     done, flops, t = [], 0.0, 0.0
@@ -111,9 +117,18 @@ def cpu_baseline(w, budget_s: float = 12.0, mask: str = "prefix"):
                 break
         if t >= budget_s:
             break
-    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"float64 numpy oracle, {'fwd+bwd' if c.bwd else 'fwd'} of {len(done)} (sequence, KV head) "
-                      f"slice(s) {done} of {c.name}, {t:.1f} s"}
+    out = {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+           "sample": f"float64 numpy oracle, {'fwd+bwd' if c.bwd else 'fwd'} of {len(done)} (sequence, KV head) "
+                     f"slice(s) {done} of {c.name}, {t:.1f} s, BLAS limited to {cores} threads"}
+    if lpt_costs:
+        out["lpt_ms"] = {}
+        for name, cost in lpt_costs.items():
+            t0 = time.perf_counter()
+            oracle.lpt(cost, n_workers)
+            out["lpt_ms"][name] = round(1e3 * (time.perf_counter() - t0), 3)
+    if limits is not None:
+        limits.restore_original_limits()
+    return out
 
 
 # Algorithmic FLOPs per token-exact visible (q head, row, key) triple, in units
@@ -164,12 +179,50 @@ def hbm_traffic(kernel: str, config: str):
         return None
 
 
-def run_steps(path, q, k, v, do, grads, K: int, warmup: int, replan: bool, with_bwd: bool, own=None):
-    """Warm up, then time K steps.  Returns wall seconds, per-phase event ms
-    (lists) and the library's per-kernel event times."""
+def kernel_alg_bytes(w, path, merge_b: int) -> dict:
+    """Algorithmic HBM bytes per launch: what a kernel must move at least, with
+    every input read once and every output written once.
+      partial_fwd_bf16: K and V rows some draft block sees (keys below the
+        sequence's largest prefix end), per KV head; every Q row; d + 2 fp32
+        per partial row written.
+      bwd_kv: those K and V rows read, every dK and dV row written; the packed
+        bf16 Q and dO copies and 12 bytes (LSE, Delta, prefix end) per (row,
+        query head) read.
+      bwd_dq: K and V rows seen read; packed Q and dO and 12 bytes per (row,
+        query head) read; d + 1 words per dQ partial row written.
+      lse_merge: see merge_bytes."""
+    c = w.cfg
+    if not w.is_bf16:
+        return {"lse_merge": merge_b}
+    el = 2
+    seen = 0
+    for s in range(c.n_seq):
+        e = np.minimum(w.seq_anchors(s).astype(np.int64) + (c.block if path.mask == "prefix" else 0), int(w.n_ctx[s]))
+        seen += int(e.max()) if len(e) else 0
+    kv_row = c.hkv * c.d * el
+    q_rows = int(w.q_off[-1]) * c.hq
+    out = {"lse_merge": merge_b}
+    import torch
+    part_rows = int(torch.isfinite(path.lse_part).sum().item())
+    out["partial_fwd_bf16"] = 2 * seen * kv_row + q_rows * c.d * el + part_rows * (c.d + 2) * 4
+    if path.bwd_plan is not None:
+        total_kv = int(w.kv_off[-1])
+        q_side = q_rows * (2 * c.d * el + 12)
+        out["bwd_kv"] = 2 * seen * kv_row + 2 * total_kv * kv_row + q_side
+        out["bwd_dq"] = 2 * seen * kv_row + q_side + part_rows * (c.d + 1) * 4
+    return out
+
+
+def run_steps(path, q, k, v, do, grads, K: int, warmup: int, replan: bool, with_bwd: bool, own=None,
+              instrument: bool = True):
+    """Warm up, then time K steps.  Returns wall seconds, the host planning
+    seconds of each timed step, and (``instrument``) per-phase event ms (lists)
+    and the library's per-kernel event times.  Without ``instrument`` the timed
+    steps record no events at all (the headline number); with it, the library's
+    event pool is filled during the warm-up, so the timed steps create none."""
     import torch
     from block_sparse_draft_amd import binding as Bd
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)] if instrument else None
     plan_s = []
 
     def step(e=None):
@@ -188,22 +241,25 @@ def run_steps(path, q, k, v, do, grads, K: int, warmup: int, replan: bool, with_
             path.backward(q, k, v, do, *grads, own=own)
         if e: e[3].record()
 
+    if instrument:
+        Bd.timing_enable(True)
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
+    Bd.timing_collect()   # the warm-up's launches (the events return to the pool)
     plan_s.clear()
-    Bd.timing_collect()
-    Bd.timing_enable(True)
     t0 = time.perf_counter()
     for i in range(K):
-        step(ev[i])
+        step(ev[i] if instrument else None)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    if not instrument:
+        return wall, plan_s, None, None
     Bd.timing_enable(False)
     kt = Bd.timing_collect()
     ph = {"fwd": [e[0].elapsed_time(e[1]) for e in ev], "merge": [e[1].elapsed_time(e[2]) for e in ev],
           "bwd": [e[2].elapsed_time(e[3]) for e in ev]}
-    return wall, ph, kt, plan_s
+    return wall, plan_s, ph, kt
 
 
 def imbalance(x) -> float:
@@ -226,7 +282,7 @@ def plan_compare(w, q, k, v, do, grads, dt, dev, K: int, warmup: int, bwd_granul
         path = SplitKVAttention(w.q_off, w.kv_off, w.anchors, c.block, c.hq, c.hkv, c.d, c.chunk, w.sm_scale,
                                 dt, dev, policy=policy, bwd_granule=bwd_granule, with_bwd=with_bwd,
                                 steal=steal, ticks=True, fwd_runs_per_worker=runs)
-        wall, ph, kt, _ = run_steps(path, q, k, v, do, grads, K, warmup, False, with_bwd)
+        wall, _, ph, kt = run_steps(path, q, k, v, do, grads, K, warmup, False, with_bwd)
         rec = {"policy": policy, "steal": steal, "fwd_runs_per_worker": runs,
                "ms_per_step": round(wall / K * 1e3, 4),
                "fwd_ms": round(float(np.mean(ph["fwd"])), 4),
@@ -307,9 +363,14 @@ def main():
     path = SplitKVAttention(w.q_off, w.kv_off, w.anchors, c.block, c.hq, c.hkv, c.d, c.chunk, w.sm_scale, dt, dev,
                             policy=args.policy, bwd_granule=args.bwd_granule, with_bwd=with_bwd,
                             steal=not args.no_steal, fwd_runs_per_worker=args.runs_per_worker or None,
-                            mask=args.mask)
+                            mask=args.mask, ticks=True)
     K = args.steps
-    wall, ph, kt, plan_s = run_steps(path, q, k, v, do, grads, K, args.warmup, not args.no_replan, with_bwd, own)
+    # headline: no events of any kind inside the timed steps
+    wall, plan_s, _, _ = run_steps(path, q, k, v, do, grads, K, args.warmup, not args.no_replan, with_bwd, own,
+                                   instrument=False)
+    # per-phase and per-kernel event times, in a second pass of the same steps
+    wall_i, _, ph, kt = run_steps(path, q, k, v, do, grads, K, max(1, min(args.warmup, 3)), not args.no_replan,
+                                  with_bwd, own, instrument=True)
 
     fwd_ms = float(np.mean(ph["fwd"]))
     mrg_ms = float(np.mean(ph["merge"]))
@@ -325,6 +386,7 @@ def main():
     fwd_tf = fwd_flops / (fwd_ms * 1e-3) / 1e12
     bwd_tf = bwd_flops / (bwd_ms * 1e-3) / 1e12 if with_bwd else 0.0
     merge_gbs = mbytes / (mrg_ms * 1e-3) / 1e9
+    alg_bytes = kernel_alg_bytes(w, path, mbytes)
 
     kernels = {}
     for name, (n_launch, tot) in kt.items():
@@ -334,19 +396,47 @@ def main():
             alg = KERNEL_FLOPS_D[name] * c.d * ctx_pairs
             rec["alg_tflops"] = round(alg / (avg * 1e-3) / 1e12, 2)
             rec["exec_tflops"] = round(KERNEL_EXEC_FLOPS_D[name] * c.d * ctx_pairs / (avg * 1e-3) / 1e12, 2)
-        if name == "lse_merge":
-            rec["gbs"] = round(mbytes / (tot / K * 1e-3) / 1e9, 1)
+        if name in alg_bytes:
+            rec["alg_bytes"] = alg_bytes[name]
+            rec["alg_gbs"] = round(alg_bytes[name] / (avg * 1e-3) / 1e9, 1)
         kernels[name] = rec
     compute = {n: kt[n][1] for n in KERNEL_FLOPS_D if n in kt}
     dom = max(compute, key=compute.get)
     dom_avg = kt[dom][1] / kt[dom][0]
     dom_flops = KERNEL_FLOPS_D[dom] * c.d * ctx_pairs
     achieved = dom_flops / (dom_avg * 1e-3) / 1e12
+    traffic = hbm_traffic(dom, c.name) if args.mask == "prefix" else None
     roof = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS
             if w.is_bf16 else 157.3, "unit": "TFLOP/s",
             "frac": round(achieved / (PEAK_BF16_TFLOPS if w.is_bf16 else 157.3), 4),
-            "traffic": hbm_traffic(dom, c.name) if args.mask == "prefix" else None,
+            "traffic": traffic, "alg_bytes": alg_bytes.get(dom),
+            "traffic_over_alg_bytes": round(traffic / alg_bytes[dom], 3) if traffic and alg_bytes.get(dom) else None,
             "alg_flops_per_launch": dom_flops, "avg_launch_ms": round(dom_avg, 4)}
+
+    # measured balance of the last instrumented step: per-workgroup busy time
+    # (s_memrealtime, 100 MHz) against the kernel's event-timed duration
+    measured = {}
+    for name, plan in (("partial_fwd_bf16", path.fwd_plan), ("bwd_kv", path.bwd_plan), ("bwd_dq", path.dq_plan)):
+        if plan is None or plan.ticks is None or name not in kt:
+            continue
+        us = plan.ticks.cpu().numpy().astype(np.float64) / 100.0
+        measured[name] = {"imbalance": round(imbalance(us), 5), "mean_busy_us": round(float(us.mean()), 1),
+                          "max_busy_us": round(float(us.max()), 1),
+                          "kernel_us": round(1e3 * kt[name][1] / kt[name][0], 1)}
+    # planner alone: lpt_plan on the step's item sets (the oracle's LPT on the
+    # same costs is timed in cpu_baseline)
+    lpt_sets = {"fwd_runs": path.fwd_plan.table[1]}
+    if with_bwd:
+        lpt_sets["bwd_items"] = path.bwd_plan.table[1]
+    lpt_us = {}
+    from block_sparse_draft_amd import binding as Bd
+    for name, cost in lpt_sets.items():
+        reps = 20
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            Bd.lpt_plan(cost, path.n_workers)
+        lpt_us[name] = {"items": int(len(cost)), "us": round(1e6 * (time.perf_counter() - t0) / reps, 1)}
+
     out = {
         "metric": "unmasked-FLOP TFLOP/s fwd+bwd, % of bf16 MFMA peak; merge GB/s",
         "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
@@ -358,6 +448,9 @@ def main():
                    "bwd_granule_keys": path.bwd_granule if with_bwd else None,
                    "fwd_runs_per_worker": path.fwd_runs_per_worker, "mask": args.mask},
         "pct_of_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        # the same steps counted at 12*d per triple (backward without the QK^T recompute)
+        "value_12d": round(12.0 * c.d * pairs / (wall / K) / 1e12, 3) if with_bwd else None,
+        "instrumented_ms_per_step": round(wall_i / K * 1e3, 4),
         "fwd": {"ms": round(fwd_ms, 4), "tflops": round(fwd_tf, 2), "frac": round(fwd_tf / PEAK_BF16_TFLOPS, 4)},
         "merge": {"ms": round(mrg_ms, 4), "launches": 1, "bytes": mbytes, "gbs": round(merge_gbs, 1),
                   "frac": round(merge_gbs / PEAK_HBM_GBS, 4)},
@@ -365,12 +458,14 @@ def main():
         if with_bwd else None,
         "kernels": kernels,
         "plan": {"host_ms_per_step": round(1e3 * float(np.mean(plan_s)), 3) if plan_s else None,
+                 "lpt_plan": lpt_us,
                  "fwd_items": path.fwd_plan.n_items, "fwd_items_planned": path.fwd_plan.n_planned,
                  "fwd_partial_rows_written": int(torch.isfinite(path.lse_part).sum().item()),
                  "fwd_runs_per_worker_used": path.fwd_plan.runs_used,
                  "fwd_imbalance": round(path.fwd_plan.imbalance, 5),
                  "bwd_items": path.bwd_plan.n_items if with_bwd else None,
-                 "bwd_imbalance": round(path.bwd_plan.imbalance, 5) if with_bwd else None},
+                 "bwd_imbalance": round(path.bwd_plan.imbalance, 5) if with_bwd else None,
+                 "measured": measured},
         "roofline": roof,
     }
     del path
@@ -379,7 +474,7 @@ def main():
         out["plan_compare"] = plan_compare(w, q, k, v, do, grads, dt, dev, max(3, K // 2), 2, args.bwd_granule,
                                            with_bwd)
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, mask=args.mask)
+        out["cpu_baseline"] = cpu_baseline(w, mask=args.mask, lpt_costs=lpt_sets, n_workers=out["config"]["n_workers"])
     print(json.dumps(out), flush=True)
 
 

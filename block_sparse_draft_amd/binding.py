@@ -89,8 +89,8 @@ def _load():
         "skv_gather_items": (C.c_int, [VP, I64, VP, I64, VP]),
         "skv_drop_zero_cost": (C.c_int, [VP, I64, I32, VP, VP, VP, VP, P(I64)]),
         "skv_coarsen_fwd_items": (C.c_int, [VP, VP, I64, I64, VP, VP, P(I64)]),
-        "skv_plan_fwd_runs": (C.c_int, [VP, VP, I64, I32, I32, I32, C.c_double, VP, VP, P(I64), VP, VP, VP,
-                                        P(I32)]),
+        "skv_plan_fwd_runs": (C.c_int, [VP, VP, I64, I32, C.c_double, C.c_double, C.c_double, VP, VP, P(I64), VP,
+                                        VP, VP, P(C.c_double)]),
         "sparse_attn_partial_fwd": (C.c_int, [P(skv_problem), P(skv_plan), VP, VP, VP, VP, VP, VP, VP]),
         "lse_merge": (C.c_int, [I32, I32, I64, I32, VP, VP, VP, VP, I64, I64, I32, VP, I64, VP]),
         "skv_bwd_workspace_bytes": (C.c_size_t, [P(skv_problem)]),
@@ -218,7 +218,7 @@ def skv_coarsen_fwd_items(items, cost, target: int):
     return it2[:m.value].copy(), c2[:m.value].copy()
 
 
-def skv_plan_fwd_runs(items, cost, n_workers: int, runs_per_worker: int, max_runs_per_worker: int,
+def skv_plan_fwd_runs(items, cost, n_workers: int, runs_per_worker: float, max_runs_per_worker: float,
                       max_imbalance: float):
     """Chunk runs and their LPT plan, with the run length chosen by the
     library's search.  Returns (items, cost, order, worker_off, load, rpw_used)."""
@@ -231,9 +231,9 @@ def skv_plan_fwd_runs(items, cost, n_workers: int, runs_per_worker: int, max_run
     off = np.empty(n_workers + 1 if n_workers > 0 else 1, np.int64)
     load = np.empty(max(n_workers, 1), np.int64)
     m = C.c_int64(0)
-    rpw = C.c_int32(0)
-    _check(lib.skv_plan_fwd_runs(_ptr(items), _ptr(cost), n, n_workers, int(runs_per_worker),
-                                 int(max_runs_per_worker), float(max_imbalance), _ptr(it2), _ptr(c2), C.byref(m),
+    rpw = C.c_double(0)
+    _check(lib.skv_plan_fwd_runs(_ptr(items), _ptr(cost), n, n_workers, float(runs_per_worker),
+                                 float(max_runs_per_worker), float(max_imbalance), _ptr(it2), _ptr(c2), C.byref(m),
                                  _ptr(order), _ptr(off), _ptr(load), C.byref(rpw)))
     k = m.value
     return it2[:k].copy(), c2[:k].copy(), order[:k].copy(), off, load, rpw.value
@@ -345,18 +345,22 @@ def sparse_attn_own_fwd(problem: Problem, q, k_own, v_own, o_part, m_part, lse_p
                                    _ptr(m_part), _ptr(lse_part), _stream(stream)))
 
 
+def _own_block_arg(own):
+    if own is None:
+        return None
+    ko, vo, dko, dvo = own
+    st, sh = _own_strides(ko)
+    if any(_own_strides(t) != (st, sh) for t in (vo, dko, dvo)):
+        raise ValueError("own-block tensors need the same strides")
+    return C.byref(skv_own_block(_ptr(ko), _ptr(vo), _ptr(dko), _ptr(dvo), st, sh))
+
+
 def sparse_attn_bwd(problem: Problem, plan_kv, plan_q, q, k, v, o, lse, dout, dq, dk, dv, workspace, stream=None,
                     own=None):
     """plan_kv: BWD plan (key ranges); plan_q: FWD plan (forward items, for dQ).
     own = (k_own, v_own, dk_own, dv_own) under the own-block mask, else None."""
     nbytes = workspace.numel() * workspace.element_size()
-    ob = None
-    if own is not None:
-        ko, vo, dko, dvo = own
-        st, sh = _own_strides(ko)
-        if any(_own_strides(t) != (st, sh) for t in (vo, dko, dvo)):
-            raise ValueError("own-block tensors need the same strides")
-        ob = C.byref(skv_own_block(_ptr(ko), _ptr(vo), _ptr(dko), _ptr(dvo), st, sh))
+    ob = _own_block_arg(own)
     _check(lib.sparse_attn_bwd(C.byref(problem.c), C.byref(plan_kv.c), C.byref(plan_q.c), _ptr(q), _ptr(k), _ptr(v),
                                _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), nbytes,
                                ob, _stream(stream)))

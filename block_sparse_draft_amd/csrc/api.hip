@@ -15,7 +15,8 @@ int check_plan(const skv_plan* plan, int32_t kind) {
   if (!plan) return fail(SKV_EINVAL, "plan is NULL");
   if (plan->kind != kind) return fail(SKV_EPLAN, "plan kind %d does not match this call (%d)", plan->kind, kind);
   if (plan->n_workers < 1) return fail(SKV_EPLAN, "plan has %d workers", plan->n_workers);
-  if (plan->n_items < 0) return fail(SKV_EPLAN, "plan has a negative item count");
+  if (plan->n_items < 0 || plan->n_items > INT32_MAX)
+    return fail(SKV_EPLAN, "plan item count %lld outside [0, 2^31)", (long long)plan->n_items);
   if (!plan->d_worker_off || !plan->d_claim || (plan->n_items > 0 && !plan->d_items))
     return fail(SKV_EPLAN, "plan arrays are NULL");
   if (plan->flags & ~SKV_PLAN_NO_STEAL) return fail(SKV_EPLAN, "unknown plan flags 0x%x", plan->flags);
@@ -68,7 +69,7 @@ extern "C" int sparse_attn_partial_fwd(const skv_problem* p, const skv_plan* pla
     part_rows += n_partials(p, v.n) * p->hq * v.mq;
   }
   hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e = launch_fill_neg_inf(m_part, lse_part, part_rows, plan->d_claim, plan->n_workers, st);
+  hipError_t e = launch_fill_neg_inf(m_part, lse_part, part_rows, plan->d_claim, plan->n_workers + 1, st);
   if (e != hipSuccess) return hip_status(e, "sparse_attn_partial_fwd launch");
   e = p->dtype == SKV_BF16 ? launch_fwd_bf16(a, plan->n_workers, st)
                                       : launch_fwd_f32(a, p->d, plan->n_workers, st);
@@ -198,10 +199,10 @@ extern "C" size_t skv_bwd_workspace_bytes(const skv_problem* p) {
   return bwd_workspace(p).total;
 }
 
-extern "C" int sparse_attn_bwd(const skv_problem* p, const skv_plan* plan_kv, const skv_plan* plan_q, const void* q,
-                               const void* k, const void* v, const void* o, const float* lse, const void* dout,
-                               void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
-                               const skv_own_block* own, void* stream) {
+// Arguments of sparse_attn_bwd other than the workspace; SKV_OK if usable.
+static int check_bwd_args(const skv_problem* p, const skv_plan* plan_kv, const skv_plan* plan_q, const void* q,
+                          const void* k, const void* v, const void* o, const float* lse, const void* dout, void* dq,
+                          void* dk, void* dv, const skv_own_block* own) {
   int rc = skv_check_problem(p);
   if (rc) return rc;
   if (p->dtype != SKV_BF16) return fail(SKV_EDTYPE, "sparse_attn_bwd supports bf16 only");
@@ -227,10 +228,31 @@ extern "C" int sparse_attn_bwd(const skv_problem* p, const skv_plan* plan_kv, co
   } else if (own) {
     return fail(SKV_EINVAL, "own-block tensors given for the prefix mask");
   }
+  return SKV_OK;
+}
+
+// The backward's launches with a validated workspace of bwd_workspace(p).total bytes.
+static int launch_bwd(const skv_problem* p, const skv_plan* plan_kv, const skv_plan* plan_q, const void* q,
+                      const void* k, const void* v, const void* o, const float* lse, const void* dout, void* dq,
+                      void* dk, void* dv, void* workspace, const skv_own_block* own, void* stream);
+
+extern "C" int sparse_attn_bwd(const skv_problem* p, const skv_plan* plan_kv, const skv_plan* plan_q, const void* q,
+                               const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                               void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                               const skv_own_block* own, void* stream) {
+  int rc = check_bwd_args(p, plan_kv, plan_q, q, k, v, o, lse, dout, dq, dk, dv, own);
+  if (rc) return rc;
   const BwdWorkspace ws = bwd_workspace(p);
   if (!workspace || workspace_bytes < ws.total)
     return fail(SKV_EWORKSPACE, "workspace of %zu bytes needed, %zu given", ws.total, workspace_bytes);
   if (reinterpret_cast<uintptr_t>(workspace) & 255u) return fail(SKV_EWORKSPACE, "workspace must be 256-byte aligned");
+  return launch_bwd(p, plan_kv, plan_q, q, k, v, o, lse, dout, dq, dk, dv, workspace, own, stream);
+}
+
+static int launch_bwd(const skv_problem* p, const skv_plan* plan_kv, const skv_plan* plan_q, const void* q,
+                      const void* k, const void* v, const void* o, const float* lse, const void* dout, void* dq,
+                      void* dk, void* dv, void* workspace, const skv_own_block* own, void* stream) {
+  const BwdWorkspace ws = bwd_workspace(p);
   char* w = static_cast<char*>(workspace);
   BwdArgs a{};
   a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.dout = dout; a.dq = dq; a.dk = dk; a.dv = dv;
@@ -261,8 +283,8 @@ extern "C" int sparse_attn_bwd(const skv_problem* p, const skv_plan* plan_kv, co
   a.fd_block = FastDiv::make(a.block); a.fd_group = FastDiv::make(a.group); a.fd_gb = FastDiv::make(a.block * a.group);
   a.sm_scale = p->sm_scale; a.scale_log2 = p->sm_scale * kLog2e_host;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  a.kv_claim_n = plan_kv->n_workers;
-  a.q_claim_n = plan_q->n_workers;
+  a.kv_claim_n = plan_kv->n_workers + 1;  // cursors and the claimed-items count
+  a.q_claim_n = plan_q->n_workers + 1;
   hipError_t e = launch_bwd_bf16(a, plan_kv->n_workers, plan_q->n_workers, st);
   return hip_status(e, "sparse_attn_bwd launch");
 }

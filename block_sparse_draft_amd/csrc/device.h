@@ -140,21 +140,35 @@ __device__ __forceinline__ int plan_worker() {
 // Next plan slot for this workgroup, or -1 when its work is done.  The
 // workgroup first claims the items of list `victim` (its own list at start)
 // through the cursor claim[victim]; with `steal`, an exhausted list moves it on
-// to the next worker's list, otherwise it stops there.  Uniform across the
-// workgroup (contains barriers).
+// to the next worker's list, otherwise it stops there.  claim[W] counts the
+// items claimed so far: once it reaches the plan's item count, no list holds
+// work, so a stealing workgroup stops after one atomic instead of visiting
+// every remaining list.  Uniform across the workgroup (contains barriers).
 __device__ __forceinline__ int64_t claim_next(const int64_t* worker_off, int32_t* claim, int& victim, int& visited,
                                               int* s_claim, bool steal) {
   const int W = gridDim.x;
   const int lists = steal ? W : 1;
   while (visited < lists) {
-    if (threadIdx.x == 0) *s_claim = atomicAdd(&claim[victim], 1);
+    const int64_t base = worker_off[victim];
+    const int64_t len = worker_off[victim + 1] - base;
+    if (threadIdx.x == 0) {
+      int idx = atomicAdd(&claim[victim], 1);
+      if (idx < len) {
+        atomicAdd(&claim[W], 1);  // one more item claimed
+      } else if (steal) {
+        // -1 once every item of every list is claimed
+        const int seen = __hip_atomic_load(&claim[W], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (seen >= (int)worker_off[W]) idx = -1;
+      }
+      *s_claim = idx;
+    }
     __syncthreads();
     // Uniform by construction; readfirstlane lets the compiler keep the item
     // and everything derived from it in scalar registers.
     const int idx = __builtin_amdgcn_readfirstlane(*s_claim);
     __syncthreads();
-    const int64_t base = worker_off[victim];
-    if (idx < worker_off[victim + 1] - base) return base + idx;
+    if (idx < 0) return -1;
+    if (idx < len) return base + idx;
     victim = victim + 1 == W ? 0 : victim + 1;
     ++visited;
   }

@@ -427,12 +427,12 @@ extern "C" int skv_coarsen_fwd_items(const skv_item* items, const int64_t* cost,
 }
 
 extern "C" int skv_plan_fwd_runs(const skv_item* items, const int64_t* cost, int64_t n, int32_t n_workers,
-                                 int32_t runs_per_worker, int32_t max_runs_per_worker, double max_imbalance,
+                                 double runs_per_worker, double max_runs_per_worker, double max_imbalance,
                                  skv_item* items_out, int64_t* cost_out, int64_t* n_out, int64_t* order,
-                                 int64_t* worker_off, int64_t* load, int32_t* rpw_used) {
+                                 int64_t* worker_off, int64_t* load, double* rpw_used) {
   if (n < 0 || n_workers < 1) return fail(SKV_EINVAL, "bad counts n=%lld n_workers=%d", (long long)n, n_workers);
-  if (runs_per_worker < 1 || max_runs_per_worker < runs_per_worker)
-    return fail(SKV_EINVAL, "runs per worker %d, max %d", runs_per_worker, max_runs_per_worker);
+  if (!(runs_per_worker > 0.0) || !(max_runs_per_worker >= runs_per_worker) || !std::isfinite(max_runs_per_worker))
+    return fail(SKV_EINVAL, "runs per worker %g, max %g", runs_per_worker, max_runs_per_worker);
   if (!(max_imbalance >= 0.0)) return fail(SKV_EINVAL, "max_imbalance must be >= 0");
   if (!n_out || !worker_off || !load || !rpw_used || (n > 0 && (!items || !cost || !items_out || !cost_out || !order)))
     return fail(SKV_EINVAL, "NULL argument");
@@ -442,10 +442,10 @@ extern "C" int skv_plan_fwd_runs(const skv_item* items, const int64_t* cost, int
     if (cost[i] > INT64_MAX - total) return fail(SKV_EINVAL, "total cost overflows");
     total += cost[i];
   }
-  int64_t rpw = runs_per_worker;
+  double rpw = runs_per_worker;
   for (;;) {
-    const int64_t per = (int64_t)n_workers * rpw;
-    const int64_t target = std::max<int64_t>(1, total / per + (total % per != 0));
+    const double t = std::ceil((double)total / ((double)n_workers * rpw));
+    const int64_t target = t < 1.0 ? 1 : (t >= 9.2e18 ? INT64_MAX : (int64_t)t);
     int rc = skv_coarsen_fwd_items(items, cost, n, target, items_out, cost_out, n_out);
     if (rc) return rc;
     if ((rc = lpt_plan(cost_out, *n_out, n_workers, nullptr, order, worker_off, load))) return rc;
@@ -453,9 +453,9 @@ extern "C" int skv_plan_fwd_runs(const skv_item* items, const int64_t* cost, int
     for (int32_t w = 0; w < n_workers; ++w) mx = std::max(mx, load[w]);
     const double mean = (double)total / (double)n_workers;
     if (rpw >= max_runs_per_worker || mean == 0.0 || (double)mx / mean - 1.0 <= max_imbalance) break;
-    rpw = std::min<int64_t>(2 * rpw, max_runs_per_worker);
+    rpw = std::min(2.0 * rpw, max_runs_per_worker);
   }
-  *rpw_used = (int32_t)rpw;
+  *rpw_used = rpw;
   clear_error();
   return SKV_OK;
 }

@@ -106,7 +106,8 @@ class _PlanSlots:
         self.n_items = n
         # staging bytes this plan needs at most: items, then worker offsets
         self.stage_bytes = _align256(max(n, 1) * B.ITEM_DTYPE.itemsize) + _align256((n_workers + 1) * 8)
-        self.claim = torch.zeros(n_workers, dtype=torch.int32, device=dev)  # reset by the library per call
+        # per-worker claim cursors and the claimed-items count, reset by the library per call
+        self.claim = torch.zeros(n_workers + 1, dtype=torch.int32, device=dev)
         # per-workgroup busy time (100 MHz ticks) of the last call, when asked for
         self.ticks = torch.zeros(n_workers, dtype=torch.int64, device=dev) if ticks else None
         self.plan_s = 0.0
@@ -128,7 +129,7 @@ class _PlanSlots:
             # Longer runs mean fewer partials but coarser items: the library
             # doubles the runs per worker until LPT balances the runs to within
             # run_imbalance (or MAX_RUNS_PER_WORKER is reached).
-            start = int(self.runs_per_worker)
+            start = float(self.runs_per_worker)
             if self.run_imbalance is None:   # keep runs_per_worker as given
                 stop, tol = start, 0.0
             else:

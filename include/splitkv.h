@@ -126,10 +126,12 @@ typedef struct skv_item {
  * Each worker claims the items of its own list in order through the atomic
  * cursor d_claim[w]; once its list is exhausted it claims the remaining
  * items of the other lists (the next workers first), so a slow compute unit
- * delays the call by at most the item it holds.  Every item is processed
- * exactly once.  d_claim is caller-owned scratch of n_workers int32 that the
- * library resets at the start of every call; two calls in flight at the same
- * time must not share it.
+ * delays the call by at most the item it holds; a count of the items claimed
+ * so far lets a worker stop as soon as every item is taken.  Every item is
+ * processed exactly once.  d_claim is caller-owned scratch of n_workers + 1
+ * int32 (the cursors, then the count) that the library resets at the start of
+ * every call; two calls in flight at the same time must not share it.  The
+ * lists hold d_worker_off[n_workers] items, fewer than 2^31.
  * flags: SKV_PLAN_NO_STEAL makes every worker run exactly its own list (the
  * plan's assignment as computed, for measuring a plan's balance); the fp32
  * forward never steals.  d_ticks (optional, NULL = off): device int64
@@ -142,7 +144,7 @@ typedef struct skv_plan {
   int64_t n_items;
   const skv_item* d_items;      /* device, [n_items] */
   const int64_t* d_worker_off;  /* device, [n_workers+1], d_worker_off[0] = 0 */
-  int32_t* d_claim;             /* device scratch, [n_workers] */
+  int32_t* d_claim;             /* device scratch, [n_workers + 1] */
   int32_t flags;                /* 0 or SKV_PLAN_NO_STEAL */
   int32_t reserved;             /* 0 */
   int64_t* d_ticks;             /* device, [n_workers], optional */
@@ -230,21 +232,22 @@ int skv_coarsen_fwd_items(const skv_item* items, const int64_t* cost, int64_t n,
  * fewer partials to write and merge but coarser items, so the search starts
  * at rpw = runs_per_worker runs per worker and doubles rpw until LPT balances
  * the runs well enough:
- *   target = ceil(total / (n_workers * rpw))  (total = sum of cost, >= 1)
+ *   target = max(1, ceil(total / (n_workers * rpw)))   (double precision;
+ *            total = sum of cost)
  *   runs   = skv_coarsen_fwd_items(items, cost, target)
  *   plan   = lpt_plan(run costs, n_workers)
  * stopping at the first rpw with max(load)/mean(load) - 1 <= max_imbalance
  * (mean in double precision), with rpw >= max_runs_per_worker, or with a
- * zero total.  Inputs as for skv_coarsen_fwd_items; runs_per_worker >= 1,
+ * zero total.  Inputs as for skv_coarsen_fwd_items; runs_per_worker > 0,
  * max_runs_per_worker >= runs_per_worker, max_imbalance >= 0.  Outputs:
  * items_out, cost_out [n] (first *n_out used: the runs), order [n] (first
  * *n_out used: run indices grouped by worker), worker_off [n_workers+1],
  * load [n_workers], *rpw_used (the rpw of the returned plan).  Zero-cost runs
  * stay in the plan (skv_drop_zero_cost removes them). */
 int skv_plan_fwd_runs(const skv_item* items, const int64_t* cost, int64_t n, int32_t n_workers,
-                      int32_t runs_per_worker, int32_t max_runs_per_worker, double max_imbalance,
+                      double runs_per_worker, double max_runs_per_worker, double max_imbalance,
                       skv_item* items_out, int64_t* cost_out, int64_t* n_out, int64_t* order, int64_t* worker_off,
-                      int64_t* load, int32_t* rpw_used);
+                      int64_t* load, double* rpw_used);
 
 /* Forward partials, one per (sequence, KV chunk): the shard-local step of
  * Split-KV (article "Split-KV: Breaking the Context Parallelism Bottleneck in

@@ -344,10 +344,10 @@ def test_coarsen_fwd_items_any_input_order(seed):
 def _oracle_run_search(desc, cost, n_workers, start, stop, tol):
     """The run-length search restated on the oracle: double the runs per worker
     until LPT over the oracle's runs balances them to within tol."""
-    rpw = start
+    rpw = float(start)
     total = int(np.asarray(cost, dtype=np.int64).sum())
     while True:
-        target = max(1, -(-total // (n_workers * rpw)))
+        target = max(1, int(np.ceil(total / (n_workers * rpw))))
         first, length, rcost = oracle.coarsen_runs(desc, cost, target)
         _, order, off, load = oracle.lpt(rcost, n_workers)
         mean = total / n_workers
@@ -358,7 +358,8 @@ def _oracle_run_search(desc, cost, n_workers, start, stop, tol):
 
 @pytest.mark.parametrize("cfg,n_workers,start,stop,tol", [
     ("c3", 256, 4, 64, 0.02), ("c5", 256, 4, 64, 0.02), ("c4", 256, 4, 64, 0.02),
-    ("c3", 13, 1, 64, 0.0), ("c5", 64, 2, 2, 0.02), ("c3", 256, 4, 64, 1e9)])
+    ("c3", 13, 1, 64, 0.0), ("c5", 64, 2, 2, 0.02), ("c3", 256, 4, 64, 1e9), ("c2", 256, 0.5, 0.5, 0.02),
+    ("c5", 100, 3, 40, 0.001)])
 def test_plan_fwd_runs_matches_oracle_search(cfg, n_workers, start, stop, tol):
     """skv_plan_fwd_runs picks the same run length as the search over the
     oracle's runs and LPT, and returns the same runs and plan (bit-exact)."""
@@ -380,7 +381,7 @@ def test_plan_fwd_runs_rejects_bad_input():
     w = make("c2", seed=0, n_ctx=4096, n_anchor=4, with_do=False)
     p = _problem_from(w)
     items, cost, _, _ = p.item_table(B.SKV_ITEM_FWD, 1)
-    for args in ((0, 4, 0.02), (4, 2, 0.02), (4, 8, -1.0), (4, 8, float("nan"))):
+    for args in ((0, 4, 0.02), (4, 2, 0.02), (4, 8, -1.0), (4, 8, float("nan")), (4, float("inf"), 0.02)):
         with pytest.raises(B.SkvError):
             B.skv_plan_fwd_runs(items, cost, 8, *args)
     with pytest.raises(B.SkvError):

@@ -393,6 +393,11 @@ OWN_CASES = {
     "c3_small": ("c3", dict(n_ctx_range=(500, 2500), n_anchor=6, hq=8, hkv=2, chunk=512)),
     "c5_small": ("c5", dict(n_ctx=4100, n_anchor=12, hq=4, hkv=4, chunk=1024)),   # G = 1, 32-token blocks
     "c4_small": ("c4", dict(n_ctx=8192, n_anchor=8, hq=4, hkv=1, chunk=256)),     # G = 4, many chunks
+    # the largest own-block shapes the C ABI accepts: block 64 with G = 1
+    # (G * block^2 = 4096) and with G = 2 (8192: the own-block backward's
+    # largest LDS footprint)
+    "b64_g1": ("c5", dict(n_ctx=3000, n_anchor=6, block=64, hq=4, hkv=4, chunk=512)),
+    "b64_g2": ("c3", dict(n_ctx_range=(1500, 3000), n_anchor=5, block=64, hq=4, hkv=2, chunk=512)),
 }
 
 
