@@ -23,6 +23,7 @@ SKV_MASK_PREFIX, SKV_MASK_OWN_BLOCK = 0, 1
 SKV_ITEM_FWD, SKV_ITEM_BWD = 0, 1
 SKV_TILE = 64
 SKV_PLAN_NO_STEAL = 1
+SKV_NOALLOC_SCRATCH_BYTES = 64 << 20
 _STATUS = {0: "SKV_OK", -1: "SKV_EINVAL", -2: "SKV_EDTYPE", -3: "SKV_ESHAPE", -4: "SKV_EHIP",
            -5: "SKV_EWORKSPACE", -6: "SKV_EPLAN"}
 
@@ -96,6 +97,8 @@ def _load():
         "skv_bwd_workspace_bytes": (C.c_size_t, [P(skv_problem)]),
         "sparse_attn_bwd": (C.c_int, [P(skv_problem), P(skv_plan), P(skv_plan)] + [VP] * 10 +
                             [C.c_size_t, P(skv_own_block), VP]),
+        "sparse_attn_bwd_noalloc": (C.c_int, [P(skv_problem), P(skv_plan), P(skv_plan)] + [VP] * 9 +
+                                    [P(skv_own_block), VP]),
         "sparse_attn_own_fwd": (C.c_int, [P(skv_problem), VP, VP, VP, I64, I64, VP, VP, VP, VP]),
         "lse_merge_all": (C.c_int, [P(skv_problem), VP, VP, VP, VP, VP, VP, VP]),
         "skv_timing_enable": (C.c_int, [I32]),
@@ -112,7 +115,8 @@ EXPORTED = ("skv_last_error", "skv_check_problem", "skv_partial_layout", "skv_it
             "skv_static_plan", "skv_gather_items", "skv_drop_zero_cost", "skv_coarsen_fwd_items",
             "skv_plan_fwd_runs",
             "sparse_attn_partial_fwd", "lse_merge", "lse_merge_all",
-            "skv_bwd_workspace_bytes", "sparse_attn_bwd", "sparse_attn_own_fwd", "skv_timing_enable",
+            "skv_bwd_workspace_bytes", "sparse_attn_bwd", "sparse_attn_bwd_noalloc", "sparse_attn_own_fwd",
+            "skv_timing_enable",
             "skv_timing_collect")
 
 
@@ -353,6 +357,14 @@ def _own_block_arg(own):
     if any(_own_strides(t) != (st, sh) for t in (vo, dko, dvo)):
         raise ValueError("own-block tensors need the same strides")
     return C.byref(skv_own_block(_ptr(ko), _ptr(vo), _ptr(dko), _ptr(dvo), st, sh))
+
+
+def sparse_attn_bwd_noalloc(problem: Problem, plan_kv, plan_q, q, k, v, o, lse, dout, dq, dk, dv, stream=None,
+                            own=None):
+    """sparse_attn_bwd with the library's static scratch in place of a workspace."""
+    _check(lib.sparse_attn_bwd_noalloc(C.byref(problem.c), C.byref(plan_kv.c), C.byref(plan_q.c), _ptr(q), _ptr(k),
+                                       _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+                                       _own_block_arg(own), _stream(stream)))
 
 
 def sparse_attn_bwd(problem: Problem, plan_kv, plan_q, q, k, v, o, lse, dout, dq, dk, dv, workspace, stream=None,

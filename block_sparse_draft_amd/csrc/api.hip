@@ -1,6 +1,7 @@
 // Device entry points of libsplitkv: argument checks (host copies only, before
 // any HIP call), then kernel launches on the caller's stream.
 #include <cmath>
+#include <mutex>
 
 #include "internal.h"
 #include "launch.h"
@@ -287,4 +288,54 @@ static int launch_bwd(const skv_problem* p, const skv_plan* plan_kv, const skv_p
   a.q_claim_n = plan_q->n_workers + 1;
   hipError_t e = launch_bwd_bf16(a, plan_kv->n_workers, plan_q->n_workers, st);
   return hip_status(e, "sparse_attn_bwd launch");
+}
+
+// ---------------------------------------------------------------------------
+// sparse_attn_bwd without a caller workspace: the workspace lives in `scratch`,
+// one copy per GPU, for callers that cannot allocate device memory.
+// ---------------------------------------------------------------------------
+
+// In host code `scratch` names a host-side stand-in, not the device array:
+// only the address from hipGetSymbolAddress, taken once per device with that
+// device current, is ever handed to kernels.
+static __device__ __align__(256) char scratch[SKV_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch` on each device, once looked up
+}  // namespace
+
+// Device address of `scratch` on the current device.
+static int scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(SKV_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(SKV_EHIP, "device %d outside [0, %d)", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(SKV_EHIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return SKV_OK;
+}
+
+extern "C" int sparse_attn_bwd_noalloc(const skv_problem* p, const skv_plan* plan_kv, const skv_plan* plan_q,
+                                       const void* q, const void* k, const void* v, const void* o, const float* lse,
+                                       const void* dout, void* dq, void* dk, void* dv, const skv_own_block* own,
+                                       void* stream) {
+  int rc = check_bwd_args(p, plan_kv, plan_q, q, k, v, o, lse, dout, dq, dk, dv, own);
+  if (rc) return rc;
+  const size_t need = bwd_workspace(p).total;
+  if (need > (size_t)SKV_NOALLOC_SCRATCH_BYTES)
+    return fail(SKV_EWORKSPACE, "the backward of this problem needs %zu bytes of workspace, more than the %d bytes "
+                "of the library's static scratch; use sparse_attn_bwd with a caller workspace", need,
+                (int)SKV_NOALLOC_SCRATCH_BYTES);
+  void* ptr = nullptr;
+  if ((rc = scratch_address(&ptr))) return rc;
+  return launch_bwd(p, plan_kv, plan_q, q, k, v, o, lse, dout, dq, dk, dv, ptr, own, stream);
 }

@@ -314,17 +314,23 @@ class SplitKVAttention:
         self.merge(stream)
         return self.o, self.lse
 
-    def backward(self, q, k, v, dout, dq, dk, dv, stream=None, own=None):
+    def backward(self, q, k, v, dout, dq, dk, dv, stream=None, own=None, noalloc: bool = False):
         """dQ, dK, dV from the merged O and LSE of the last forward.  Under the
-        own-block mask ``own`` = (k_own, v_own, dk_own, dv_own)."""
+        own-block mask ``own`` = (k_own, v_own, dk_own, dv_own).  ``noalloc``:
+        the library's static scratch instead of this object's workspace
+        (sparse_attn_bwd_noalloc)."""
         if (self.mask == "own_block") != (own is not None):
             raise ValueError("own-block tensors go with the own-block mask")
         self._check(q=q, k=k, v=v, dout=dout, dq=dq, dk=dk, dv=dv,
                     **(dict(zip(("k_own", "v_own", "dk_own", "dv_own"), own)) if own is not None else {}))
         ts = self._stream(stream)
         self.staging.flush(ts)
-        B.sparse_attn_bwd(self.problem, self.bwd_plan, self.dq_plan, q, k, v, self.o, self.lse, dout, dq, dk, dv,
-                          self.workspace, ts, own=own)
+        if noalloc:
+            B.sparse_attn_bwd_noalloc(self.problem, self.bwd_plan, self.dq_plan, q, k, v, self.o, self.lse, dout, dq,
+                                      dk, dv, ts, own=own)
+        else:
+            B.sparse_attn_bwd(self.problem, self.bwd_plan, self.dq_plan, q, k, v, self.o, self.lse, dout, dq, dk, dv,
+                              self.workspace, ts, own=own)
         self.staging.used_on(ts)
         return dq, dk, dv
 

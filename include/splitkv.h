@@ -360,6 +360,24 @@ int sparse_attn_bwd(const skv_problem* p, const skv_plan* plan_kv, const skv_pla
                     void* dk, void* dv, void* workspace, size_t workspace_bytes, const skv_own_block* own,
                     void* stream);
 
+/* sparse_attn_bwd for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * Same arguments, checks and results as sparse_attn_bwd, without the
+ * workspace: the library keeps it in a static device array of
+ * SKV_NOALLOC_SCRATCH_BYTES (64 MiB) that every GPU the library runs on holds
+ * from its first such call until the process ends.  The call allocates and
+ * frees nothing; problems whose skv_bwd_workspace_bytes exceeds the array are
+ * rejected with SKV_EWORKSPACE before any device work.  The stream must belong
+ * to the device current on the calling thread.  Every call on one GPU shares
+ * that GPU's array: calls that overlap in time on one GPU (other streams, or
+ * other threads) race and must be serialized by the caller; calls in order on
+ * one stream are safe.  Nothing in the array needs to start at zero: each call
+ * writes every part it later reads. */
+enum { SKV_NOALLOC_SCRATCH_BYTES = 64 << 20 };
+int sparse_attn_bwd_noalloc(const skv_problem* p, const skv_plan* plan_kv, const skv_plan* plan_q, const void* q,
+                            const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                            void* dq, void* dk, void* dv, const skv_own_block* own, void* stream);
+
 /* ---- Instrumentation (host) ----
  * Per-kernel timing with HIP events, off by default.  While enabled, every
  * kernel the library launches is bracketed by two events recorded on the

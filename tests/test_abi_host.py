@@ -233,6 +233,16 @@ def test_device_calls_reject_bad_arguments_before_touching_the_gpu():
     tq = B.skv_plan(B.SKV_ITEM_FWD, 4, 1, 16, 16, 32, 0, 0, 64)
     rc = B.lib.sparse_attn_bwd(C.byref(pb.c), C.byref(tk), C.byref(tq), *([fake] * 10), need, None, None)
     assert rc == B.SKV_EPLAN and "ticks" in B.last_error()   # shared ticks arrays are rejected
+    # the no-allocation backward: the same checks, and problems whose workspace
+    # exceeds the static scratch are rejected before any device work
+    rc = B.lib.sparse_attn_bwd_noalloc(C.byref(pb.c), C.byref(bplan), C.byref(plan), *([fake] * 9), None, None)
+    assert rc == B.SKV_EPLAN
+    wbig = _meta_only("c3", {})
+    pbig = _problem_from(wbig)
+    pbig.c.d_q_off = pbig.c.d_kv_off = pbig.c.d_anchor = 4096
+    assert B.lib.skv_bwd_workspace_bytes(C.byref(pbig.c)) > B.SKV_NOALLOC_SCRATCH_BYTES
+    rc = B.lib.sparse_attn_bwd_noalloc(C.byref(pbig.c), C.byref(bplan), C.byref(qplan), *([fake] * 9), None, None)
+    assert rc == B.SKV_EWORKSPACE and "static scratch" in B.last_error()
     badflags = B.skv_plan(B.SKV_ITEM_FWD, 4, 1, 16, 16, 16, 2, 0, None)
     rc = B.lib.sparse_attn_partial_fwd(C.byref(p.c), C.byref(badflags), fake, fake, fake, fake, fake, fake, None)
     assert rc == B.SKV_EPLAN and "flags" in B.last_error()
