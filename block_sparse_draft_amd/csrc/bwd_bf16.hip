@@ -44,6 +44,10 @@ namespace {
 
 constexpr int D = 128;
 constexpr int LDS_ROW = D + 8;   // bf16 per staged row (272 bytes: conflict-free 16-byte reads)
+// Rows read with ds_read_b64_tr_b16 (four consecutive rows, 64 bytes each, per
+// 32 lanes) are staged at a 320-byte stride, which puts those rows in disjoint
+// bank quarters; at 272 bytes they overlap.
+constexpr int LDS_ROW_TR = D + 32;
 
 // ---------------------------------------------------------------------------
 // 1. preprocess
@@ -142,8 +146,13 @@ struct QTileMeta {
 
 __global__ __launch_bounds__(KV_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_kv_kernel(BwdArgs a) {
+  // Each query tile is staged twice: row-major at a 272-byte stride for the S
+  // and dP products, and at a 320-byte stride for the transposed reads of the
+  // dV and dK products.
   __shared__ __attribute__((aligned(16))) uint16_t sQ[2][QT * LDS_ROW];
   __shared__ __attribute__((aligned(16))) uint16_t sdO[2][QT * LDS_ROW];
+  __shared__ __attribute__((aligned(16))) uint16_t sQt[2][QT * LDS_ROW_TR];
+  __shared__ __attribute__((aligned(16))) uint16_t sdOt[2][QT * LDS_ROW_TR];
   __shared__ __attribute__((aligned(16))) QTileMeta sMeta[2];
   __shared__ __attribute__((aligned(16))) uint16_t sK[KV_KEYS * LDS_ROW];
   __shared__ int s_claim;
@@ -213,8 +222,11 @@ void bwd_kv_kernel(BwdArgs a) {
       };
       auto store_q = [&](const QTileRegs& r, int buf) {
         const int o = (tid >> 4) * LDS_ROW + (tid & 15) * 8;
+        const int ot = (tid >> 4) * LDS_ROW_TR + (tid & 15) * 8;
         *reinterpret_cast<uint4*>(sQ[buf] + o) = r.q;
         *reinterpret_cast<uint4*>(sdO[buf] + o) = r.o;
+        *reinterpret_cast<uint4*>(sQt[buf] + ot) = r.q;
+        *reinterpret_cast<uint4*>(sdOt[buf] + ot) = r.o;
         if (tid < QT) {
           sMeta[buf].lse[tid] = r.lse;
           sMeta[buf].delta[tid] = r.delta;
@@ -270,8 +282,8 @@ void bwd_kv_kernel(BwdArgs a) {
           const QTileMeta& M = sMeta[buf];
           // 32-bit LDS addresses of this lane's transposed reads; the empty asm
           // keeps the per-read offsets as immediates.
-          uint32_t qt0 = lds_addr(bq + (4 * hf + (li >> 2)) * LDS_ROW + 16 * (gi & 1) + 4 * (li & 3));
-          uint32_t ot0 = lds_addr(bo + (4 * hf + (li >> 2)) * LDS_ROW + 16 * (gi & 1) + 4 * (li & 3));
+          uint32_t qt0 = lds_addr(sQt[buf] + (4 * hf + (li >> 2)) * LDS_ROW_TR + 16 * (gi & 1) + 4 * (li & 3));
+          uint32_t ot0 = lds_addr(sdOt[buf] + (4 * hf + (li >> 2)) * LDS_ROW_TR + 16 * (gi & 1) + 4 * (li & 3));
           asm volatile("" : "+v"(qt0), "+v"(ot0));
 
           // ---- S = Q K^T and dP = dO V^T for 32 rows x this wave's 32 keys ----
@@ -323,9 +335,9 @@ void bwd_kv_kernel(BwdArgs a) {
 #pragma unroll
             for (int nd = 0; nd < 4; ++nd) {
               asm volatile("" ::: "memory");
-              const uint32_t so = 2u * (kstep * 16 * LDS_ROW + nd * 32);
-              const bf16x8 ob = lds_tr_pair(ot0 + so, ot0 + so + 2u * 8 * LDS_ROW);
-              const bf16x8 qb = lds_tr_pair(qt0 + so, qt0 + so + 2u * 8 * LDS_ROW);
+              const uint32_t so = 2u * (kstep * 16 * LDS_ROW_TR + nd * 32);
+              const bf16x8 ob = lds_tr_pair(ot0 + so, ot0 + so + 2u * 8 * LDS_ROW_TR);
+              const bf16x8 qb = lds_tr_pair(qt0 + so, qt0 + so + 2u * 8 * LDS_ROW_TR);
               dv_acc[nd] = mfma32x32x16(pa, ob, dv_acc[nd]);
               dk_acc[nd] = mfma32x32x16(da, qb, dk_acc[nd]);
             }
