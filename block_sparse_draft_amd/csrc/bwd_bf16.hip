@@ -158,7 +158,7 @@ void bwd_kv_kernel(BwdArgs a) {
   __shared__ int s_claim;
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = uniform(tid >> 6);  // readfirstlane: the compiler keeps wave-level control flow scalar
   const int l32 = lane & 31, hf = lane >> 5;
   const int gi = lane >> 4, li = lane & 15;
   const uint16_t* K = static_cast<const uint16_t*>(a.k);
@@ -415,7 +415,7 @@ void bwd_dq_kernel(BwdArgs a) {
   __shared__ int s_claim;
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = uniform(tid >> 6);
   const int l32 = lane & 31, hf = lane >> 5;
   const int gi = lane >> 4, li = lane & 15;
   const uint16_t* K = static_cast<const uint16_t*>(a.k);

@@ -46,23 +46,34 @@ constexpr int NTHR = 64 * NWAVE;
 constexpr int ROWS = 32 * NWAVE;    // packed query rows per pass
 constexpr int NBUF = 3;
 constexpr float LAZY_LOG2 = 8.f;    // rescale only when the max grows by more than 2^8
-// Padded LDS rows: 272-byte K rows and 144-byte V^T rows put the 16-byte
-// operand reads of 8 consecutive rows in distinct banks.
+// Padded LDS rows: 272-byte K rows put the 16-byte operand reads of 16
+// consecutive rows in distinct banks.  V^T rows are 160 bytes with their eight
+// 16-byte key chunks XOR-swizzled by bits 3..5 of the row (chunk c of row r
+// sits at c ^ ((r >> 3) & 7)): the 8-byte staging writes of 32 lanes (rows
+// 4h, keys of both 8-byte halves) and the 16-byte operand reads of 16
+// consecutive rows then both fall in distinct banks (64 banks of 4 bytes).
 constexpr int LDS_ROW_K = D + 8;
-constexpr int LDS_ROW_VT = KT + 8;
+constexpr int LDS_ROW_VT = KT + 16;
 constexpr int TILE_K = KT * LDS_ROW_K;
 constexpr int TILE_VT = D * LDS_ROW_VT;
 
 // Staging registers of one K/V tile.  K: 2 x 16 bytes (rows r and r + 32,
 // 8 head-dim values each).  V: 4 keys x 4 head-dim values (8 bytes per key).
+// V key groups (4 keys each): wave w stages groups g0 = 4 (w / 2) + w % 2 and
+// g0 + 2 (even and odd lanes), head-dim values 4 (lane / 2) .. + 3.
 struct TileRegs {
   uint4 k0, k1;
   uint2 v0, v1, v2, v3;
 };
 
+__device__ __forceinline__ int v_group(int tid) {
+  const int w = tid >> 6;
+  return 4 * (w >> 1) + (w & 1) + 2 * (tid & 1);
+}
+
 // Byte offsets of this thread's staging loads inside a tile: K rows tid/16 and
-// tid/16 + 32 (16 bytes at head-dim 8*(tid%16)); V rows 4*(tid/32) + j
-// (8 bytes at head-dim 4*(tid%32)).
+// tid/16 + 32 (16 bytes at head-dim 8*(tid%16)); V keys 4*g + j of its key
+// group g (8 bytes at head-dim 4*((tid%64)/2)).
 struct TileOffsets {
   int k0, k1, v0, v1, v2, v3;
 };
@@ -72,7 +83,7 @@ __device__ __forceinline__ TileOffsets tile_offsets(int kv_st, int tid) {
   const int rb = kv_st * 2;  // bytes per key row
   o.k0 = (tid >> 4) * rb + (tid & 15) * 16;
   o.k1 = o.k0 + 32 * rb;
-  o.v0 = (tid >> 5) * 4 * rb + (tid & 31) * 8;
+  o.v0 = v_group(tid) * 4 * rb + ((tid & 63) >> 1) * 8;
   o.v1 = o.v0 + rb;
   o.v2 = o.v0 + 2 * rb;
   o.v3 = o.v0 + 3 * rb;
@@ -99,16 +110,19 @@ __device__ __forceinline__ TileRegs load_tile(const uint16_t* Kseq, const uint16
   return r;
 }
 
-// Position of key kk (0..15) of a 16-key group inside a V^T row: lane half h
-// of the PV operand reads positions 8h..8h+7, which hold keys 4h..4h+3 and
-// 8+4h..8+4h+3 (the order the S^T accumulators deliver P^T in).
+// Position of key kk (0..15) of a 16-key group inside a V^T row (before the
+// swizzle): lane half h of the PV operand reads positions 8h..8h+7, which hold
+// keys 4h..4h+3 and 8+4h..8+4h+3 (the order the S^T accumulators deliver P^T
+// in).  Key group g (keys 4g..4g+3) thus fills 16-byte chunk 2 (g / 4) + g % 2,
+// 8-byte half (g / 2) % 2.
 __device__ __forceinline__ void store_tile(const TileRegs& r, uint16_t* sK, uint16_t* sVt, int tid) {
   *reinterpret_cast<uint4*>(sK + (tid >> 4) * LDS_ROW_K + (tid & 15) * 8) = r.k0;
   *reinterpret_cast<uint4*>(sK + ((tid >> 4) + 32) * LDS_ROW_K + (tid & 15) * 8) = r.k1;
   // 4 keys x 4 values -> 4 rows of V^T with 4 keys each
-  const int kg = tid >> 5;                                  // keys 4kg .. 4kg+3
-  const int pos = (kg >> 2) * 16 + ((kg >> 1) & 1) * 4 + (kg & 1) * 8;
-  uint16_t* dst = sVt + (tid & 31) * 4 * LDS_ROW_VT + pos;
+  const int kg = v_group(tid);                              // keys 4kg .. 4kg+3
+  const int h4 = (tid & 63) >> 1;                           // V^T rows 4h4 .. 4h4+3
+  const int chunk = (2 * (kg >> 2) + (kg & 1)) ^ ((h4 >> 1) & 7);
+  uint16_t* dst = sVt + h4 * 4 * LDS_ROW_VT + chunk * 8 + ((kg >> 1) & 1) * 4;
   // byte selectors of v_perm_b32(hi, lo, sel): bytes 0-3 from lo, 4-7 from hi
   const uint32_t lo16 = 0x05040100u, hi16 = 0x07060302u;
   uint2 y0, y1, y2, y3;
@@ -128,7 +142,7 @@ void fwd_bf16_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t sVb[NBUF][TILE_VT];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = uniform(tid >> 6);
   const int l32 = lane & 31, hf = lane >> 5;
   const uint16_t* Q = static_cast<const uint16_t*>(a.q);
   const uint16_t* K = static_cast<const uint16_t*>(a.k);
@@ -137,6 +151,8 @@ void fwd_bf16_kernel(FwdArgs a) {
   const float c = a.scale_log2;
   const int kv_st = (int)a.kv_st;  // the host checks that a sequence's K/V span fits 31 bits of bytes
   const TileOffsets toff = tile_offsets(kv_st, tid);
+  const uint32_t va_lane = 2u * (l32 * LDS_ROW_VT) + 16u * (hf ^ ((l32 >> 3) & 1));
+  const int va_z = (l32 >> 4) & 1;
 
   __shared__ int s_claim;
   const uint64_t t_start = __builtin_amdgcn_s_memrealtime();
@@ -280,12 +296,19 @@ void fwd_bf16_kernel(FwdArgs a) {
         //      MFMAs, so they arrive while the next exponentials are computed;
         //      the empty asm ends each step's scheduling region, which bounds
         //      how many operands the compiler keeps in flight. ----
-        uint32_t va = lds_addr(sVb[t % NBUF] + l32 * LDS_ROW_VT + hf * 8);
-        asm volatile("" : "+v"(va));
+        // Row md*32 + l32, key chunk 2 kstep + hf, swizzled: this lane's chunk
+        // pairs sit at 32-byte slot kstep ^ z (z = va_z for even md, va_z ^ 2
+        // for odd md), its half at 16 (hf ^ (l32 / 8 % 2)).
+        const uint32_t vrow = lds_addr(sVb[t % NBUF]) + va_lane;
+        uint32_t va[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) va[k] = vrow + 32u * (k ^ va_z);
+        asm volatile("" : "+v"(va[0]), "+v"(va[1]), "+v"(va[2]), "+v"(va[3]));
+        auto vaddr = [&](int md, int ks) { return va[(md & 1) ? (ks ^ 2) : ks] + 2u * (md * 32 * LDS_ROW_VT); };
         const float mc = m_ref == -INFINITY ? 0.f : m_ref * c;
         bf16x8 vc[4];
 #pragma unroll
-        for (int md = 0; md < 4; ++md) vc[md] = lds_read_b128(va + 2u * (md * 32 * LDS_ROW_VT));
+        for (int md = 0; md < 4; ++md) vc[md] = lds_read_b128(vaddr(md, 0));
 #pragma unroll
         for (int kstep = 0; kstep < 4; ++kstep) {
           const int mt = kstep >> 1, qh = (kstep & 1) * 8;
@@ -298,7 +321,7 @@ void fwd_bf16_kernel(FwdArgs a) {
           bf16x8 vn[4] = {vc[0], vc[1], vc[2], vc[3]};
           if (kstep + 1 < 4) {
 #pragma unroll
-            for (int md = 0; md < 4; ++md) vn[md] = lds_read_b128(va + 2u * (md * 32 * LDS_ROW_VT + (kstep + 1) * 16));
+            for (int md = 0; md < 4; ++md) vn[md] = lds_read_b128(vaddr(md, kstep + 1));
           }
 #pragma unroll
           for (int md = 0; md < 4; ++md) acc_o[md] = mfma32x32x16(vc[md], pf, acc_o[md]);
