@@ -24,13 +24,13 @@
 //      is computed.  S = Q K^T, dP = dO V^T (A from LDS), P and dS in
 //      registers, dV += P^T dO and dK += dS^T Q (B read transposed from LDS).
 //   3. query-owner kernel over the forward's items (sequence, KV head, run of
-//      consecutive chunks, draft blocks), structured like the forward: 64
-//      rows per wave with Q in registers and dO in LDS, K/V tiles of the run
-//      through two LDS buffers; S^T = K Q^T, dP^T = V dO^T, dS^T, then
-//      dQ^T += K^T dS^T, with the two 32-key halves of a tile
-//      software-pipelined (one half's dS work beside the other half's MFMAs).
-//      Each item writes one dQ partial for its run, in its first chunk's rows
-//      (with the run length beside it), like the forward's O partial.
+//      consecutive chunks, draft blocks), structured like the forward: 8
+//      waves (two per SIMD, so one wave's LDS waits and dS arithmetic overlap
+//      the other's MFMA work), 32 rows per wave with Q and dO in registers,
+//      K/V tiles of the run through three LDS buffers; per 32-key half
+//      S^T = K Q^T, dP^T = V dO^T, dS^T, then dQ^T += K^T dS^T.  Each item
+//      writes one dQ partial for its run, in its first chunk's rows (with the
+//      run length beside it), like the forward's O partial.
 //   4. finalize: dQ = scale * sum of the row's run partials (and, under the
 //      own-block mask, its own-block partial), bf16.
 #include <type_traits>
@@ -367,51 +367,57 @@ void bwd_kv_kernel(BwdArgs a) {
 // ---------------------------------------------------------------------------
 
 constexpr int KT2 = 64;                 // keys per tile of the query-owner kernel
-constexpr int TILE_ELEMS = KT2 * LDS_ROW;
+constexpr int DQ_WAVES = 8;             // two per SIMD
+constexpr int DQ_THREADS = 64 * DQ_WAVES;
+constexpr int DQ_ROWS = 32 * DQ_WAVES;  // packed query rows per pass
+constexpr int DQ_NBUF = 3;
+// K and V tiles of the query-owner kernel: 320-byte rows whose 16-byte chunks
+// are XOR-swizzled by bits 2..3 of the row (chunk c of row r sits at
+// c ^ ((r >> 2) & 3)).  Both the row-major operand reads (16 consecutive rows,
+// one chunk) and the transposed K reads (4 consecutive rows x 64 bytes) then
+// fall in distinct banks; at a 272-byte stride the transposed reads collide.
+constexpr int LDS_ROW_KV = D + 32;
+constexpr int TILE_ELEMS = KT2 * LDS_ROW_KV;
 
+// Staging registers of one K/V tile: rows tid/16 and tid/16 + 32, 16 bytes at
+// head-dim 8*(tid%16), of K and of V.
 struct KVTileRegs {
-  uint4 k0, k1, k2, k3, v0, v1, v2, v3;
+  uint4 k0, k1, v0, v1;
 };
 
+// Loads of key tile [kb, kb+64) through buffer descriptors based at key kb
+// whose range ends with the context: keys past it read as zeros (they are
+// masked for every row).
 __device__ __forceinline__ KVTileRegs load_kv_tile(const uint16_t* Kseq, const uint16_t* Vseq, int kb, int n_ctx,
-                                                   int64_t kv_st, int tid) {
+                                                   int kv_st, int o0) {
+  const int64_t start = (int64_t)kb * kv_st;
+  const int range = (n_ctx - kb) * kv_st * 2;
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kseq + start, range);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vseq + start, range);
+  const int o1 = o0 + 32 * kv_st * 2;
   KVTileRegs r;
-  const int64_t d8 = (tid & 15) * 8;
-  const int row = tid >> 4;
-  const int64_t o0 = (int64_t)min(kb + row, n_ctx - 1) * kv_st + d8;
-  const int64_t o1 = (int64_t)min(kb + row + 16, n_ctx - 1) * kv_st + d8;
-  const int64_t o2 = (int64_t)min(kb + row + 32, n_ctx - 1) * kv_st + d8;
-  const int64_t o3 = (int64_t)min(kb + row + 48, n_ctx - 1) * kv_st + d8;
-  r.k0 = *reinterpret_cast<const uint4*>(Kseq + o0);
-  r.k1 = *reinterpret_cast<const uint4*>(Kseq + o1);
-  r.k2 = *reinterpret_cast<const uint4*>(Kseq + o2);
-  r.k3 = *reinterpret_cast<const uint4*>(Kseq + o3);
-  r.v0 = *reinterpret_cast<const uint4*>(Vseq + o0);
-  r.v1 = *reinterpret_cast<const uint4*>(Vseq + o1);
-  r.v2 = *reinterpret_cast<const uint4*>(Vseq + o2);
-  r.v3 = *reinterpret_cast<const uint4*>(Vseq + o3);
+  r.k0 = buffer_load_b128(rk, o0);
+  r.k1 = buffer_load_b128(rk, o1);
+  r.v0 = buffer_load_b128(rv, o0);
+  r.v1 = buffer_load_b128(rv, o1);
   return r;
 }
 
-__device__ __forceinline__ void store_kv_tile(KVTileRegs r, uint16_t* sK, uint16_t* sV, int tid) {
-  const int o = (tid >> 4) * LDS_ROW + (tid & 15) * 8;
-  constexpr int R16 = 16 * LDS_ROW;
+__device__ __forceinline__ void store_kv_tile(const KVTileRegs& r, uint16_t* sK, uint16_t* sV, int tid) {
+  // rows tid/16 and tid/16 + 32 share the swizzle (tid / 64) % 4
+  const int o = (tid >> 4) * LDS_ROW_KV + ((tid & 15) ^ ((tid >> 6) & 3)) * 8;
+  constexpr int R32 = 32 * LDS_ROW_KV;
   *reinterpret_cast<uint4*>(sK + o) = r.k0;
-  *reinterpret_cast<uint4*>(sK + o + R16) = r.k1;
-  *reinterpret_cast<uint4*>(sK + o + 2 * R16) = r.k2;
-  *reinterpret_cast<uint4*>(sK + o + 3 * R16) = r.k3;
+  *reinterpret_cast<uint4*>(sK + o + R32) = r.k1;
   *reinterpret_cast<uint4*>(sV + o) = r.v0;
-  *reinterpret_cast<uint4*>(sV + o + R16) = r.v1;
-  *reinterpret_cast<uint4*>(sV + o + 2 * R16) = r.v2;
-  *reinterpret_cast<uint4*>(sV + o + 3 * R16) = r.v3;
+  *reinterpret_cast<uint4*>(sV + o + R32) = r.v1;
 }
 
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(DQ_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dq_kernel(BwdArgs a) {
-  // Two K/V buffers: tile t+1 is stored after the barrier that ends tile t-1,
-  // so one barrier per tile suffices.  dO rows of the pass live in LDS.
-  __shared__ __attribute__((aligned(16))) uint16_t sKV[2][2][TILE_ELEMS];
-  __shared__ __attribute__((aligned(16))) uint16_t sdO[256 * LDS_ROW];
+  // Three K/V buffers: tile t+1 is stored while tile t is computed, tile t+2
+  // is in flight, so one barrier per tile suffices (as in the forward).
+  __shared__ __attribute__((aligned(16))) uint16_t sKV[DQ_NBUF][2][TILE_ELEMS];
   __shared__ int s_claim;
 
   const int tid = threadIdx.x;
@@ -422,7 +428,22 @@ void bwd_dq_kernel(BwdArgs a) {
   const uint16_t* V = static_cast<const uint16_t*>(a.v);
   const int GB = a.group * a.block;
   const float c = a.scale_log2;
-  const uint16_t* my_dO = sdO + (wave * 64 + l32) * LDS_ROW + hf * 8;  // this lane's row, nt = 0
+  const int kv_st = (int)a.kv_st;  // a sequence's K/V span fits 31 bits of bytes (checked on the host)
+  const int ld_off = (tid >> 4) * kv_st * 2 + (tid & 15) * 16;
+  // Swizzled element offsets of this lane's K/V tile reads.  Row-major operand
+  // (row 32 mt + l32, chunk 2 ks + hf, swizzle f = (l32 / 4) % 4): chunk
+  // 2 (ks ^ (f / 2)) + (hf ^ f % 2), i.e. kv_row_off[ks % 2] + 16 (ks & ~1).
+  // Transposed K operand (rows key0 = 16 j + 4 hf + li / 4 and key0 + 8, head
+  // dim 32 md + 16 (gi % 2) + 4 (li % 4)): swizzles hf and hf + 2.
+  int kv_row_off[2], kt_off[2];
+  {
+    const int f = (l32 >> 2) & 3;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) kv_row_off[k] = l32 * LDS_ROW_KV + 16 * (k ^ (f >> 1)) + 8 * (hf ^ (f & 1));
+    const int c1 = (2 * (gi & 1) + ((li & 3) >> 1)) ^ hf;
+    kt_off[0] = (4 * hf + (li >> 2)) * LDS_ROW_KV + 8 * c1 + 4 * (li & 1);
+    kt_off[1] = (4 * hf + (li >> 2) + 8) * LDS_ROW_KV + 8 * (c1 ^ 2) + 4 * (li & 1);
+  }
 
   const uint64_t t_start = __builtin_amdgcn_s_memrealtime();
   const int me = plan_worker();
@@ -449,166 +470,116 @@ void bwd_dq_kernel(BwdArgs a) {
     const int klo = it.chunk * a.chunk;
     const int khi = (int)min((int64_t)(it.chunk + n_chunk) * a.chunk, (int64_t)n_ctx);
     const int64_t part_base = it.part_base;
-    for (int rt = 0; rt < nrows; rt += 256) {
-      const int p_last = min(nrows, rt + 256) - 1;
+    for (int rt = 0; rt < nrows; rt += DQ_ROWS) {
+      const int p_last = min(nrows, rt + DQ_ROWS) - 1;
       const int wg_hi = max(klo, min(khi, a.endp[pitem + p_last]));
       const int ntiles = (wg_hi - klo + KT2 - 1) / KT2;
       if (ntiles == 0) continue;  // no row of the pass sees the chunk: no partial to write
 
-      __syncthreads();  // all waves are done with the previous pass's buffers (K/V and dO)
-      KVTileRegs R = load_kv_tile(Kseq, Vseq, klo, n_ctx, a.kv_st, tid);
-      // ---- this lane's two rows: Q as MFMA B operand, LSE, Delta; dO rows to LDS ----
-      int vend[2];
-      int64_t prow[2];
-      bool valid[2];
-      float lse2[2], del[2];
-      bf16x8 qf[2][8];
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        const int p = rt + wave * 64 + nt * 32 + l32;
-        valid[nt] = p < nrows;
-        const int pc = valid[nt] ? p : p_last;
-        const int b = it.lo + a.fd_gb.div(pc);
-        const int hl = a.fd_group.mod(a.fd_block.div(pc));
-        const int64_t r = (int64_t)b * a.block + a.fd_block.mod(pc);
-        const int h = it.kv_head * a.group + hl;
-        const int64_t P = pitem + pc;
-        const int e = a.endp[P];
-        vend[nt] = valid[nt] ? max(klo, min(khi, e)) : klo;
-        prow[nt] = part_base + (int64_t)h * mq + r;
-        lse2[nt] = a.lsep[P];
-        del[nt] = a.deltap[P];
+      __syncthreads();  // all waves are done with the previous pass's buffers
+      KVTileRegs R = load_kv_tile(Kseq, Vseq, klo, n_ctx, kv_st, ld_off);
+      // ---- this lane's row: Q and dO as MFMA B operands, LSE, Delta ----
+      const int p = rt + wave * 32 + l32;
+      const bool valid = p < nrows;
+      const int pc = valid ? p : p_last;  // clamp: loads stay in bounds, results unused
+      const int b = it.lo + a.fd_gb.div(pc);
+      const int hl = a.fd_group.mod(a.fd_block.div(pc));
+      const int64_t r = (int64_t)b * a.block + a.fd_block.mod(pc);
+      const int h = it.kv_head * a.group + hl;
+      const int64_t P = pitem + pc;
+      const int e = a.endp[P];
+      const int vend = valid ? max(klo, min(khi, e)) : klo;  // visible keys of the row: [klo, vend)
+      const int64_t prow = part_base + (int64_t)h * mq + r;
+      const float lse2 = a.lsep[P];
+      const float del = a.deltap[P];
+      bf16x8 qf[8], of[8];
+      {
         const uint16_t* qrow = a.qp + P * D + hf * 8;
+        const uint16_t* orow = a.dop + P * D + hf * 8;
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) qf[nt][ks] = load_bf16x8(qrow + ks * 16);
+        for (int ks = 0; ks < 8; ++ks) {
+          qf[ks] = load_bf16x8(qrow + ks * 16);
+          of[ks] = load_bf16x8(orow + ks * 16);
+        }
       }
-      // dO of the pass's 256 rows: thread (row tid>>4 + 16u, 16-byte column tid&15)
-      uint4 dox[16];
-#pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        const int p = min(rt + (tid >> 4) + 16 * u, p_last);
-        dox[u] = *reinterpret_cast<const uint4*>(a.dop + (pitem + p) * D + (tid & 15) * 8);
-      }
-#pragma unroll
-      for (int u = 0; u < 16; ++u)
-        *reinterpret_cast<uint4*>(sdO + ((tid >> 4) + 16 * u) * LDS_ROW + (tid & 15) * 8) = dox[u];
       store_kv_tile(R, sKV[0][0], sKV[0][1], tid);
-      __builtin_amdgcn_s_waitcnt(0);  // drain before the prefetch (see the forward kernel)
-      if (ntiles > 1) R = load_kv_tile(Kseq, Vseq, klo + KT2, n_ctx, a.kv_st, tid);
-      const int wave_hi = wave_max_i(max(vend[0], vend[1]));
-      const int wave_full = wave_min_i(min(valid[0] ? vend[0] : INT32_MAX, valid[1] ? vend[1] : INT32_MAX));
+      // Drain every outstanding load before the prefetch starts, so that
+      // inside the tile loop only the prefetch itself is in flight.
+      __builtin_amdgcn_s_waitcnt(0);
+      if (ntiles > 1) R = load_kv_tile(Kseq, Vseq, klo + KT2, n_ctx, kv_st, ld_off);
+      const int wave_hi = wave_max_i(vend);
+      const int wave_full = wave_min_i(valid ? vend : INT32_MAX);
 
-      f32x16 acc[4][2];
+      f32x16 acc[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i][0] = acc[i][1] = f32x16{};
+      for (int i = 0; i < 4; ++i) acc[i] = f32x16{};
 
       for (int t = 0; t < ntiles; ++t) {
         const int kb = klo + t * KT2;
-        __syncthreads();  // tile t visible; every wave is done with tile t-1's buffer
         if (t + 1 < ntiles) {
-          store_kv_tile(R, sKV[(t + 1) & 1][0], sKV[(t + 1) & 1][1], tid);
-          if (t + 2 < ntiles) R = load_kv_tile(Kseq, Vseq, kb + 2 * KT2, n_ctx, a.kv_st, tid);
+          store_kv_tile(R, sKV[(t + 1) % DQ_NBUF][0], sKV[(t + 1) % DQ_NBUF][1], tid);
+          if (t + 2 < ntiles) R = load_kv_tile(Kseq, Vseq, kb + 2 * KT2, n_ctx, kv_st, ld_off);
         }
-        if (kb >= wave_hi) continue;
-        const uint16_t* sK = sKV[t & 1][0];
-        const uint16_t* sV = sKV[t & 1][1];
+        __syncthreads();
+        if (kb >= wave_hi) continue;  // no row of this wave sees the tile (nor any later one)
+        const uint16_t* sK = sKV[t % DQ_NBUF][0];
+        const uint16_t* sV = sKV[t % DQ_NBUF][1];
 
-        // The 64 keys are two halves of 32 (mt = 0, 1).  Within the tile the
-        // halves are software-pipelined: each k step of half 1's S^T / dP^T
-        // products carries part of half 0's dS work, and each step of half 0's
-        // dQ products part of half 1's, so the VALU work of one half runs in
-        // the shadow of the other half's MFMAs.  Every value is computed as in
-        // a plain half-by-half loop; only the instruction order differs.
+        // Per 32-key half mt: S^T = K Q^T and dP^T = V dO^T (A from LDS),
+        // dS^T = P^T (dP^T - Delta) with P^T = exp2(s*c - LSE2) on visible keys,
+        // then dQ^T += K^T dS^T (K^T read transposed from LDS).
         auto tile = [&](auto mask_c) {
           constexpr bool MASK = decltype(mask_c)::value;  // partial tile: keys past a row's end are masked
-          // dS^T = P^T (dP^T - Delta), P^T = exp2(s*c - LSE2) on visible keys,
-          // for elements e0 and e0 + 1 of both row groups of half mt
-          auto ds_pair = [&](int mt, int e0, f32x16 (&sacc)[2], const f32x16 (&pacc)[2]) {
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt)
+          for (int mt = 0; mt < 2; ++mt) {
+            const uint16_t* kh = sK + mt * 32 * LDS_ROW_KV;
+            const uint16_t* vh = sV + mt * 32 * LDS_ROW_KV;
+            f32x16 sacc = f32x16{}, pacc = f32x16{};
 #pragma unroll
-              for (int e = e0; e < e0 + 2; ++e) {
-                float p = fast_exp2(__builtin_fmaf(sacc[nt][e], c, -lse2[nt]));
-                if (MASK) {
-                  const int key = kb + mt * 32 + (e >> 2) * 8 + hf * 4 + (e & 3);
-                  if (key >= vend[nt]) p = 0.f;
-                }
-                sacc[nt][e] = p * (pacc[nt][e] - del[nt]);
+            for (int ks = 0; ks < 8; ++ks) {
+              const int o = kv_row_off[ks & 1] + (ks & ~1) * 16;
+              const bf16x8 kf = lds_load_bf16x8(kh + o);
+              const bf16x8 vf = lds_load_bf16x8(vh + o);
+              sacc = mfma32x32x16(kf, qf[ks], sacc);
+              pacc = mfma32x32x16(vf, of[ks], pacc);
+            }
+            // element e holds key kb + mt*32 + 8*(e/4) + 4*hf + e%4 of this lane's row
+#pragma unroll
+            for (int e2 = 0; e2 < 16; ++e2) {
+              float pe = fast_exp2(__builtin_fmaf(sacc[e2], c, -lse2));
+              if (MASK) {
+                const int key = kb + mt * 32 + (e2 >> 2) * 8 + hf * 4 + (e2 & 3);
+                if (key >= vend) pe = 0.f;
               }
-          };
-          // k step ks of S^T = K Q^T and dP^T = V dO^T for keys mt*32 .. +32
-          auto sp_step = [&](int mt, int ks, f32x16 (&sacc)[2], f32x16 (&pacc)[2]) {
-            const bf16x8 kf = lds_load_bf16x8(sK + (mt * 32 + l32) * LDS_ROW + ks * 16 + hf * 8);
-            const bf16x8 vf = lds_load_bf16x8(sV + (mt * 32 + l32) * LDS_ROW + ks * 16 + hf * 8);
-            sacc[0] = mfma32x32x16(kf, qf[0][ks], sacc[0]);
-            sacc[1] = mfma32x32x16(kf, qf[1][ks], sacc[1]);
-            pacc[0] = mfma32x32x16(vf, lds_load_bf16x8(my_dO + ks * 16), pacc[0]);
-            pacc[1] = mfma32x32x16(vf, lds_load_bf16x8(my_dO + 32 * LDS_ROW + ks * 16), pacc[1]);
-          };
-          // dS^T of keys mt*32 + 16*half .. +16 as bf16 MFMA operands
-          auto to_df = [&](const f32x16 (&sacc)[2], int half, bf16x8 (&df)[2]) {
-            const int qh = half * 8;
-#pragma unroll
-            for (int nt = 0; nt < 2; ++nt) {
-              const f32x16& sv = sacc[nt];
-              df[nt] = to_bf16x8(sv[qh + 0], sv[qh + 1], sv[qh + 2], sv[qh + 3], sv[qh + 4], sv[qh + 5],
-                                 sv[qh + 6], sv[qh + 7]);
+              sacc[e2] = pe * (pacc[e2] - del);
             }
-          };
-          // head-dim block md of dQ^T += K^T dS^T over keys mt*32 + 16*half .. +16
-          // (K^T read transposed from LDS)
-          auto dq_step = [&](int mt, int half, int md, const bf16x8 (&df)[2]) {
-            const int key0 = (2 * mt + half) * 16 + 4 * hf + (li >> 2);
-            const int col = md * 32 + 16 * (gi & 1) + 4 * (li & 3);
-            const bf16x8 kt = lds_tr_pair(sK + key0 * LDS_ROW + col, sK + (key0 + 8) * LDS_ROW + col);
-            acc[md][0] = mfma32x32x16(kt, df[0], acc[md][0]);
-            acc[md][1] = mfma32x32x16(kt, df[1], acc[md][1]);
-          };
-
-          f32x16 s0[2], p0[2], s1[2], p1[2];
-          s0[0] = s0[1] = p0[0] = p0[1] = f32x16{};
-          s1[0] = s1[1] = p1[0] = p1[1] = f32x16{};
 #pragma unroll
-          for (int ks = 0; ks < 8; ++ks) sp_step(0, ks, s0, p0);
+            for (int half = 0; half < 2; ++half) {
+              const int qh = half * 8;
+              const bf16x8 df = to_bf16x8(sacc[qh + 0], sacc[qh + 1], sacc[qh + 2], sacc[qh + 3], sacc[qh + 4],
+                                          sacc[qh + 5], sacc[qh + 6], sacc[qh + 7]);
 #pragma unroll
-          for (int ks = 0; ks < 8; ++ks) {  // half 1's scores with half 0's dS
-            sp_step(1, ks, s1, p1);
-            ds_pair(0, 2 * ks, s0, p0);
-          }
-#pragma unroll
-          for (int half = 0; half < 2; ++half) {  // half 0's dQ with half 1's dS
-            bf16x8 df[2];
-            to_df(s0, half, df);
-#pragma unroll
-            for (int md = 0; md < 4; ++md) {
-              dq_step(0, half, md, df);
-              ds_pair(1, 2 * (half * 4 + md), s1, p1);
+              for (int md = 0; md < 4; ++md) {
+                const int o = (2 * mt + half) * 16 * LDS_ROW_KV + md * 32;
+                const bf16x8 kt = lds_tr_pair(sK + kt_off[0] + o, sK + kt_off[1] + o);
+                acc[md] = mfma32x32x16(kt, df, acc[md]);
+              }
             }
-          }
-#pragma unroll
-          for (int half = 0; half < 2; ++half) {
-            bf16x8 df[2];
-            to_df(s1, half, df);
-#pragma unroll
-            for (int md = 0; md < 4; ++md) dq_step(1, half, md, df);
           }
         };
         if (kb + KT2 > wave_full) tile(std::integral_constant<bool, true>{});
         else tile(std::integral_constant<bool, false>{});
       }
 
-      // ---- the item's dQ partial (unscaled) for rows that see its keys ----
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        if (!valid[nt] || vend[nt] <= klo) continue;
-        if (hf == 0) a.dq_run[prow[nt]] = n_chunk;
-        float* op = a.dq_part + prow[nt] * D + hf * 4;
+      // ---- the item's dQ partial (unscaled) for a row that sees its keys ----
+      if (valid && vend > klo) {
+        if (hf == 0) a.dq_run[prow] = n_chunk;
+        float* op = a.dq_part + prow * D + hf * 4;
 #pragma unroll
         for (int md = 0; md < 4; ++md)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            f32x4 v4 = {acc[md][nt][4 * i + 0], acc[md][nt][4 * i + 1], acc[md][nt][4 * i + 2],
-                        acc[md][nt][4 * i + 3]};
+            f32x4 v4 = {acc[md][4 * i + 0], acc[md][4 * i + 1], acc[md][4 * i + 2], acc[md][4 * i + 3]};
             *reinterpret_cast<f32x4*>(op + md * 32 + 8 * i) = v4;
           }
       }
@@ -681,7 +652,7 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, int kv_workers, int q_workers, hipS
   }
   {
     TimedLaunch t(kBwdDq, stream);
-    hipLaunchKernelGGL(bwd_dq_kernel, dim3(q_workers), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(bwd_dq_kernel, dim3(q_workers), dim3(DQ_THREADS), 0, stream, a);
     if ((e = hipGetLastError()) != hipSuccess || rows == 0) return e;
   }
   if (a.own && (e = launch_own_bwd(a, a.total_q / a.block, stream)) != hipSuccess) return e;

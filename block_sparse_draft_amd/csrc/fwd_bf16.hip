@@ -47,13 +47,14 @@ constexpr int ROWS = 32 * NWAVE;    // packed query rows per pass
 constexpr int NBUF = 3;
 constexpr float LAZY_LOG2 = 8.f;    // rescale only when the max grows by more than 2^8
 // Padded LDS rows: 272-byte K rows put the 16-byte operand reads of 16
-// consecutive rows in distinct banks.  V^T rows are 160 bytes with their eight
-// 16-byte key chunks XOR-swizzled by bits 3..5 of the row (chunk c of row r
-// sits at c ^ ((r >> 3) & 7)): the 8-byte staging writes of 32 lanes (rows
-// 4h, keys of both 8-byte halves) and the 16-byte operand reads of 16
-// consecutive rows then both fall in distinct banks (64 banks of 4 bytes).
+// consecutive rows in distinct banks.  V^T rows are 192 bytes with their eight
+// 16-byte key chunks XOR-swizzled by bits 2..4 of the row (chunk c of row r
+// sits at c ^ ((r >> 2) & 7)): measured with the LDS bank-conflict counter,
+// both the 8-byte staging writes and the 16-byte operand reads then run at
+// their conflict-free rate (a 144-byte unswizzled layout serialises the
+// writes 8 ways).
 constexpr int LDS_ROW_K = D + 8;
-constexpr int LDS_ROW_VT = KT + 16;
+constexpr int LDS_ROW_VT = KT + 32;
 constexpr int TILE_K = KT * LDS_ROW_K;
 constexpr int TILE_VT = D * LDS_ROW_VT;
 
@@ -121,7 +122,7 @@ __device__ __forceinline__ void store_tile(const TileRegs& r, uint16_t* sK, uint
   // 4 keys x 4 values -> 4 rows of V^T with 4 keys each
   const int kg = v_group(tid);                              // keys 4kg .. 4kg+3
   const int h4 = (tid & 63) >> 1;                           // V^T rows 4h4 .. 4h4+3
-  const int chunk = (2 * (kg >> 2) + (kg & 1)) ^ ((h4 >> 1) & 7);
+  const int chunk = (2 * (kg >> 2) + (kg & 1)) ^ (h4 & 7);  // rows 4h4 + j share the swizzle
   uint16_t* dst = sVt + h4 * 4 * LDS_ROW_VT + chunk * 8 + ((kg >> 1) & 1) * 4;
   // byte selectors of v_perm_b32(hi, lo, sel): bytes 0-3 from lo, 4-7 from hi
   const uint32_t lo16 = 0x05040100u, hi16 = 0x07060302u;
@@ -151,8 +152,8 @@ void fwd_bf16_kernel(FwdArgs a) {
   const float c = a.scale_log2;
   const int kv_st = (int)a.kv_st;  // the host checks that a sequence's K/V span fits 31 bits of bytes
   const TileOffsets toff = tile_offsets(kv_st, tid);
-  const uint32_t va_lane = 2u * (l32 * LDS_ROW_VT) + 16u * (hf ^ ((l32 >> 3) & 1));
-  const int va_z = (l32 >> 4) & 1;
+  const uint32_t va_lane = 2u * (l32 * LDS_ROW_VT) + 16u * (hf ^ ((l32 >> 2) & 1));
+  const int va_z = (l32 >> 3) & 3;
 
   __shared__ int s_claim;
   const uint64_t t_start = __builtin_amdgcn_s_memrealtime();
@@ -296,15 +297,15 @@ void fwd_bf16_kernel(FwdArgs a) {
         //      MFMAs, so they arrive while the next exponentials are computed;
         //      the empty asm ends each step's scheduling region, which bounds
         //      how many operands the compiler keeps in flight. ----
-        // Row md*32 + l32, key chunk 2 kstep + hf, swizzled: this lane's chunk
-        // pairs sit at 32-byte slot kstep ^ z (z = va_z for even md, va_z ^ 2
-        // for odd md), its half at 16 (hf ^ (l32 / 8 % 2)).
+        // Row md*32 + l32, key chunk 2 kstep + hf, swizzle f = (l32 / 4) % 8:
+        // this lane's chunk pair sits at 32-byte slot kstep ^ (f / 2), its
+        // half at 16 (hf ^ f % 2), the same for every md.
         const uint32_t vrow = lds_addr(sVb[t % NBUF]) + va_lane;
         uint32_t va[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) va[k] = vrow + 32u * (k ^ va_z);
         asm volatile("" : "+v"(va[0]), "+v"(va[1]), "+v"(va[2]), "+v"(va[3]));
-        auto vaddr = [&](int md, int ks) { return va[(md & 1) ? (ks ^ 2) : ks] + 2u * (md * 32 * LDS_ROW_VT); };
+        auto vaddr = [&](int md, int ks) { return va[ks] + 2u * (md * 32 * LDS_ROW_VT); };
         const float mc = m_ref == -INFINITY ? 0.f : m_ref * c;
         bf16x8 vc[4];
 #pragma unroll
