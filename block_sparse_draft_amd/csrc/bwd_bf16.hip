@@ -44,10 +44,39 @@ namespace {
 
 constexpr int D = 128;
 constexpr int LDS_ROW = D + 8;   // bf16 per staged row (272 bytes: conflict-free 16-byte reads)
-// Rows read with ds_read_b64_tr_b16 (four consecutive rows, 64 bytes each, per
-// 32 lanes) are staged at a 320-byte stride, which puts those rows in disjoint
-// bank quarters; at 272 bytes they overlap.
-constexpr int LDS_ROW_TR = D + 32;
+// Tiles read both row-major (16-byte operand reads of 16 consecutive rows) and
+// transposed (ds_read_b64_tr_b16: 4 consecutive rows x 64 bytes per 32 lanes)
+// are staged in 320-byte rows whose 16-byte chunks are XOR-swizzled by bits
+// 2..3 of the row (chunk c of row r sits at c ^ ((r >> 2) & 3)): measured with
+// the LDS bank-conflict counter, both kinds of read are then conflict-free (at
+// 272 bytes the transposed reads collide, at 320 unswizzled the row reads).
+constexpr int LDS_ROW_SW = D + 32;
+
+// Swizzled element offsets of one lane's reads in such a tile.  Row-major
+// operand (row l32 of a 32-row block, chunk 2 ks + hf, swizzle f = (l32/4)%4):
+// chunk 2 (ks ^ (f / 2)) + (hf ^ f % 2), so row_off[ks % 2] + 16 (ks & ~1).
+// Transposed operand (rows 16 j + 4 hf + li / 4 and 8 rows further, columns
+// 32 md + 16 (gi % 2) + 4 (li % 4)): swizzles hf and hf + 2, so
+// tr_off[0|1] + 16 j * LDS_ROW_SW + 32 md.
+struct SwizzledOffsets {
+  int row_off[2], tr_off[2];
+};
+__device__ __forceinline__ SwizzledOffsets swizzled_offsets(int lane) {
+  const int l32 = lane & 31, hf = lane >> 5, gi = lane >> 4, li = lane & 15;
+  SwizzledOffsets o;
+  const int f = (l32 >> 2) & 3;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) o.row_off[k] = l32 * LDS_ROW_SW + 16 * (k ^ (f >> 1)) + 8 * (hf ^ (f & 1));
+  const int c1 = (2 * (gi & 1) + ((li & 3) >> 1)) ^ hf;
+  o.tr_off[0] = (4 * hf + (li >> 2)) * LDS_ROW_SW + 8 * c1 + 4 * (li & 1);
+  o.tr_off[1] = (4 * hf + (li >> 2) + 8) * LDS_ROW_SW + 8 * (c1 ^ 2) + 4 * (li & 1);
+  return o;
+}
+// Element offset of thread tid's 16-byte store into such a tile: row
+// tid / 16 (+ 16 u, 32 u: same swizzle), chunk tid % 16.
+__device__ __forceinline__ int swizzled_store_off(int tid) {
+  return (tid >> 4) * LDS_ROW_SW + ((tid & 15) ^ ((tid >> 6) & 3)) * 8;
+}
 
 // ---------------------------------------------------------------------------
 // 1. preprocess
@@ -146,13 +175,10 @@ struct QTileMeta {
 
 __global__ __launch_bounds__(KV_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_kv_kernel(BwdArgs a) {
-  // Each query tile is staged twice: row-major at a 272-byte stride for the S
-  // and dP products, and at a 320-byte stride for the transposed reads of the
-  // dV and dK products.
-  __shared__ __attribute__((aligned(16))) uint16_t sQ[2][QT * LDS_ROW];
-  __shared__ __attribute__((aligned(16))) uint16_t sdO[2][QT * LDS_ROW];
-  __shared__ __attribute__((aligned(16))) uint16_t sQt[2][QT * LDS_ROW_TR];
-  __shared__ __attribute__((aligned(16))) uint16_t sdOt[2][QT * LDS_ROW_TR];
+  // Query tiles in the swizzled 320-byte layout: read row-major by the S and
+  // dP products and transposed by the dV and dK products.
+  __shared__ __attribute__((aligned(16))) uint16_t sQ[2][QT * LDS_ROW_SW];
+  __shared__ __attribute__((aligned(16))) uint16_t sdO[2][QT * LDS_ROW_SW];
   __shared__ __attribute__((aligned(16))) QTileMeta sMeta[2];
   __shared__ __attribute__((aligned(16))) uint16_t sK[KV_KEYS * LDS_ROW];
   __shared__ int s_claim;
@@ -160,7 +186,8 @@ void bwd_kv_kernel(BwdArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = uniform(tid >> 6);  // readfirstlane: the compiler keeps wave-level control flow scalar
   const int l32 = lane & 31, hf = lane >> 5;
-  const int gi = lane >> 4, li = lane & 15;
+  const SwizzledOffsets so = swizzled_offsets(lane);
+  const int st_off = swizzled_store_off(tid);
   const uint16_t* K = static_cast<const uint16_t*>(a.k);
   const uint16_t* V = static_cast<const uint16_t*>(a.v);
   uint16_t* dK = static_cast<uint16_t*>(a.dk);
@@ -221,12 +248,8 @@ void bwd_kv_kernel(BwdArgs a) {
         return r;
       };
       auto store_q = [&](const QTileRegs& r, int buf) {
-        const int o = (tid >> 4) * LDS_ROW + (tid & 15) * 8;
-        const int ot = (tid >> 4) * LDS_ROW_TR + (tid & 15) * 8;
-        *reinterpret_cast<uint4*>(sQ[buf] + o) = r.q;
-        *reinterpret_cast<uint4*>(sdO[buf] + o) = r.o;
-        *reinterpret_cast<uint4*>(sQt[buf] + ot) = r.q;
-        *reinterpret_cast<uint4*>(sdOt[buf] + ot) = r.o;
+        *reinterpret_cast<uint4*>(sQ[buf] + st_off) = r.q;
+        *reinterpret_cast<uint4*>(sdO[buf] + st_off) = r.o;
         if (tid < QT) {
           sMeta[buf].lse[tid] = r.lse;
           sMeta[buf].delta[tid] = r.delta;
@@ -282,17 +305,18 @@ void bwd_kv_kernel(BwdArgs a) {
           const QTileMeta& M = sMeta[buf];
           // 32-bit LDS addresses of this lane's transposed reads; the empty asm
           // keeps the per-read offsets as immediates.
-          uint32_t qt0 = lds_addr(sQt[buf] + (4 * hf + (li >> 2)) * LDS_ROW_TR + 16 * (gi & 1) + 4 * (li & 3));
-          uint32_t ot0 = lds_addr(sdOt[buf] + (4 * hf + (li >> 2)) * LDS_ROW_TR + 16 * (gi & 1) + 4 * (li & 3));
-          asm volatile("" : "+v"(qt0), "+v"(ot0));
+          uint32_t qt0 = lds_addr(bq + so.tr_off[0]), qt1 = lds_addr(bq + so.tr_off[1]);
+          uint32_t ot0 = lds_addr(bo + so.tr_off[0]), ot1 = lds_addr(bo + so.tr_off[1]);
+          asm volatile("" : "+v"(qt0), "+v"(qt1), "+v"(ot0), "+v"(ot1));
 
           // ---- S = Q K^T and dP = dO V^T for 32 rows x this wave's 32 keys ----
           f32x16 sacc = f32x16{}, pacc = f32x16{};
 #pragma unroll
           for (int ks = 0; ks < 8; ++ks) {
             if (ks & 1) asm volatile("" ::: "memory");  // bounds how far the compiler hoists the reads
-            const bf16x8 qa = lds_load_bf16x8(bq + l32 * LDS_ROW + ks * 16 + hf * 8);
-            const bf16x8 oa = lds_load_bf16x8(bo + l32 * LDS_ROW + ks * 16 + hf * 8);
+            const int ro = so.row_off[ks & 1] + (ks & ~1) * 16;
+            const bf16x8 qa = lds_load_bf16x8(bq + ro);
+            const bf16x8 oa = lds_load_bf16x8(bo + ro);
             const bf16x8 kf = lds_load_bf16x8(sK + (wave * 32 + l32) * LDS_ROW + ks * 16 + hf * 8);
             sacc = mfma32x32x16(qa, kf, sacc);
             pacc = mfma32x32x16(oa, vreg[ks], pacc);
@@ -335,9 +359,9 @@ void bwd_kv_kernel(BwdArgs a) {
 #pragma unroll
             for (int nd = 0; nd < 4; ++nd) {
               asm volatile("" ::: "memory");
-              const uint32_t so = 2u * (kstep * 16 * LDS_ROW_TR + nd * 32);
-              const bf16x8 ob = lds_tr_pair(ot0 + so, ot0 + so + 2u * 8 * LDS_ROW_TR);
-              const bf16x8 qb = lds_tr_pair(qt0 + so, qt0 + so + 2u * 8 * LDS_ROW_TR);
+              const uint32_t to = 2u * (kstep * 16 * LDS_ROW_SW + nd * 32);
+              const bf16x8 ob = lds_tr_pair(ot0 + to, ot1 + to);
+              const bf16x8 qb = lds_tr_pair(qt0 + to, qt1 + to);
               dv_acc[nd] = mfma32x32x16(pa, ob, dv_acc[nd]);
               dk_acc[nd] = mfma32x32x16(da, qb, dk_acc[nd]);
             }
@@ -371,12 +395,9 @@ constexpr int DQ_WAVES = 8;             // two per SIMD
 constexpr int DQ_THREADS = 64 * DQ_WAVES;
 constexpr int DQ_ROWS = 32 * DQ_WAVES;  // packed query rows per pass
 constexpr int DQ_NBUF = 3;
-// K and V tiles of the query-owner kernel: 320-byte rows whose 16-byte chunks
-// are XOR-swizzled by bits 2..3 of the row (chunk c of row r sits at
-// c ^ ((r >> 2) & 3)).  Both the row-major operand reads (16 consecutive rows,
-// one chunk) and the transposed K reads (4 consecutive rows x 64 bytes) then
-// fall in distinct banks; at a 272-byte stride the transposed reads collide.
-constexpr int LDS_ROW_KV = D + 32;
+// K and V tiles of the query-owner kernel in the swizzled 320-byte layout
+// (row-major K and V operands, transposed K operand).
+constexpr int LDS_ROW_KV = LDS_ROW_SW;
 constexpr int TILE_ELEMS = KT2 * LDS_ROW_KV;
 
 // Staging registers of one K/V tile: rows tid/16 and tid/16 + 32, 16 bytes at
@@ -404,8 +425,7 @@ __device__ __forceinline__ KVTileRegs load_kv_tile(const uint16_t* Kseq, const u
 }
 
 __device__ __forceinline__ void store_kv_tile(const KVTileRegs& r, uint16_t* sK, uint16_t* sV, int tid) {
-  // rows tid/16 and tid/16 + 32 share the swizzle (tid / 64) % 4
-  const int o = (tid >> 4) * LDS_ROW_KV + ((tid & 15) ^ ((tid >> 6) & 3)) * 8;
+  const int o = swizzled_store_off(tid);
   constexpr int R32 = 32 * LDS_ROW_KV;
   *reinterpret_cast<uint4*>(sK + o) = r.k0;
   *reinterpret_cast<uint4*>(sK + o + R32) = r.k1;
@@ -423,20 +443,16 @@ void bwd_dq_kernel(BwdArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = uniform(tid >> 6);
   const int l32 = lane & 31, hf = lane >> 5;
-  const int gi = lane >> 4, li = lane & 15;
   const uint16_t* K = static_cast<const uint16_t*>(a.k);
   const uint16_t* V = static_cast<const uint16_t*>(a.v);
   const int GB = a.group * a.block;
   const float c = a.scale_log2;
   const int kv_st = (int)a.kv_st;  // a sequence's K/V span fits 31 bits of bytes (checked on the host)
   const int ld_off = (tid >> 4) * kv_st * 2 + (tid & 15) * 16;
-  // Swizzled element offsets of this lane's K/V tile reads.  Row-major operand
-  // (row 32 mt + l32, chunk 2 ks + hf, swizzle f = (l32 / 4) % 4): chunk
-  // 2 (ks ^ (f / 2)) + (hf ^ f % 2), i.e. kv_row_off[ks % 2] + 16 (ks & ~1).
-  // Transposed K operand (rows key0 = 16 j + 4 hf + li / 4 and key0 + 8, head
-  // dim 32 md + 16 (gi % 2) + 4 (li % 4)): swizzles hf and hf + 2.
+  // swizzled element offsets of this lane's row-major and transposed reads
   int kv_row_off[2], kt_off[2];
   {
+    const int gi = lane >> 4, li = lane & 15;
     const int f = (l32 >> 2) & 3;
 #pragma unroll
     for (int k = 0; k < 2; ++k) kv_row_off[k] = l32 * LDS_ROW_KV + 16 * (k ^ (f >> 1)) + 8 * (hf ^ (f & 1));
