@@ -4,10 +4,11 @@
  *
  * What it computes (pages: "Split-KV: Breaking the Context Parallelism
  * Bottleneck in Diffusion Drafter Training", lede and "Split-KV's Core
- * Mechanism"; arXiv:2611.05926, Abstract):  a short set of draft queries,
- * built by anchor sampling, attends with a block-sparse mask over a much longer
- * context.  The context K/V stays resident in chunks; every chunk yields a
- * query-sized partial result and the partials are merged exactly, so the
+ * Mechanism"; arXiv:2611.05926, Abstract):  the draft tokens, a few blocks
+ * placed at sampled anchor positions, attend to a context many times their
+ * length, each block to a part of it only.  The context K/V stays resident in
+ * chunks; every chunk yields a query-sized partial result and the partials
+ * are merged exactly, so the
  * result equals unsharded attention.  The backward reuses the merged
  * log-sum-exp.  Work items are placed on persistent workgroups by a
  * cost-aware longest-processing-time-first (LPT) planner ("LPT Scheduling").
