@@ -217,8 +217,9 @@ static int check_bwd_args(const skv_problem* p, const skv_plan* plan_kv, const s
   const int64_t tq = p->h_q_off[p->n_seq], tk = p->h_kv_off[p->n_seq];
   if ((tq && (!q || !o || !lse || !dout || !dq)) || (tk && (!k || !v || !dk || !dv)))
     return fail(SKV_EINVAL, "tensor pointer is NULL");
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) || !aligned16(dq))
-    return fail(SKV_ESHAPE, "q, k, v, o, dout and dq must be 16-byte aligned");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) || !aligned16(dq) ||
+      !aligned16(dk) || !aligned16(dv))
+    return fail(SKV_ESHAPE, "q, k, v, o, dout, dq, dk and dv must be 16-byte aligned");
   if (p->mask == SKV_MASK_OWN_BLOCK) {
     if ((rc = check_own_shape(p))) return rc;
     if (!own || (tq && (!own->k || !own->v || !own->dk || !own->dv)))

@@ -362,25 +362,45 @@ void bwd_kv_kernel(BwdArgs a) {
               const uint32_t to = 2u * (kstep * 16 * LDS_ROW_SW + nd * 32);
               const bf16x8 ob = lds_tr_pair(ot0 + to, ot1 + to);
               const bf16x8 qb = lds_tr_pair(qt0 + to, qt1 + to);
-              dv_acc[nd] = mfma32x32x16(pa, ob, dv_acc[nd]);
-              dk_acc[nd] = mfma32x32x16(da, qb, dk_acc[nd]);
+              dv_acc[nd] = mfma32x32x16(ob, pa, dv_acc[nd]);  // dV^T: head dim x keys
+              dk_acc[nd] = mfma32x32x16(qb, da, dk_acc[nd]);  // dK^T
             }
           }
         }
       }
 
       // ---- write dK (scaled) and dV for this wave's keys inside the item ----
+      // The accumulators hold dK^T and dV^T: lane (l32, hf) has key key_w and
+      // head dim nd*32 + 8r + 4hf + j in element 4r + j.  Swapping the 8-byte
+      // runs of r = 2s+1 in the low lane half with those of r = 2s in the high
+      // half gives each lane 16 consecutive bytes, head dim nd*32 + 16s + 8hf
+      // onwards, so every store is 16 bytes.
+      {
+        const int64_t row = (k0 + key_w) * a.kv_st + (int64_t)g * a.kv_sh + 8 * hf;
+        const bool own_key = key_w < kend;
 #pragma unroll
-      for (int nd = 0; nd < 4; ++nd)
+        for (int nd = 0; nd < 4; ++nd)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int key = kw0 + (e >> 2) * 8 + 4 * hf + (e & 3);
-          if (key < kend) {
-            const int64_t off = (k0 + key) * a.kv_st + (int64_t)g * a.kv_sh + nd * 32 + l32;
-            dK[off] = f32_to_bf16_bits(a.sm_scale * dk_acc[nd][e]);
-            dV[off] = f32_to_bf16_bits(dv_acc[nd][e]);
+          for (int s2 = 0; s2 < 2; ++s2) {
+            const f32x16& ka = dk_acc[nd];
+            const f32x16& va = dv_acc[nd];
+            const int e0 = 8 * s2;
+            const float sc = a.sm_scale;
+            uint4 k4 = __builtin_bit_cast(uint4, to_bf16x8(sc * ka[e0], sc * ka[e0 + 1], sc * ka[e0 + 2], sc * ka[e0 + 3],
+                                                         sc * ka[e0 + 4], sc * ka[e0 + 5], sc * ka[e0 + 6],
+                                                         sc * ka[e0 + 7]));
+            uint4 v4 = __builtin_bit_cast(uint4, to_bf16x8(va[e0], va[e0 + 1], va[e0 + 2], va[e0 + 3], va[e0 + 4],
+                                                         va[e0 + 5], va[e0 + 6], va[e0 + 7]));
+            swap_lane_halves(k4.x, k4.z);
+            swap_lane_halves(k4.y, k4.w);
+            swap_lane_halves(v4.x, v4.z);
+            swap_lane_halves(v4.y, v4.w);
+            if (own_key) {
+              *reinterpret_cast<uint4*>(dK + row + nd * 32 + 16 * s2) = k4;
+              *reinterpret_cast<uint4*>(dV + row + nd * 32 + 16 * s2) = v4;
+            }
           }
-        }
+      }
     }
   }
   record_ticks(a.kv_ticks, me, t_start);

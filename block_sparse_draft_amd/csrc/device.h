@@ -112,6 +112,15 @@ __device__ __forceinline__ bf16x8 to_bf16x8(float a0, float a1, float a2, float 
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
+// v_permlane32_swap: lanes 32..63 of `lo` trade places with lanes 0..31 of
+// `hi` (lanes 0..31 of lo and 32..63 of hi keep their values).  Every lane of
+// the wave must execute it.
+__device__ __forceinline__ void swap_lane_halves(uint32_t& lo, uint32_t& hi) {
+  const auto r = __builtin_amdgcn_permlane32_swap(lo, hi, false, false);
+  lo = r[0];
+  hi = r[1];
+}
+
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
   return __builtin_bit_cast(uint16_t, (__bf16)x);
 }

@@ -287,9 +287,8 @@ void fwd_bf16_kernel(FwdArgs a) {
             for (int md = 0; md < 4; ++md) acc_o[md] *= alpha;
           }
         }
-        // ---- scores of tile t+1 (the buffer holds stale keys after the last
-        //      tile: computed and discarded) ----
-        scores((t + 1) % NBUF, snext);
+        // ---- scores of tile t+1, if some row of this wave sees it ----
+        if (kb + KT < wave_hi) scores((t + 1) % NBUF, snext);
         // ---- P = exp2(s*c - m_ref*c), 16 keys at a time right before their
         //      part of O^T += V^T P^T; the row sum in fp32 (bf16-rounded P
         //      would cost the log-sum-exp up to 2^-9 relative on short rows).

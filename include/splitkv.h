@@ -334,7 +334,9 @@ size_t skv_bwd_workspace_bytes(const skv_problem* p);
  * dK_j = sm_scale * sum dS q, summed over the query heads of each KV head.
  * o = merged output (problem dtype, Q layout), lse = merged LSE (float
  * [sum Mq][hq]), dout = dO.  Outputs dq (Q layout), dk and dv (K/V layout)
- * are fully written, dk = dv = 0 for keys no query sees.
+ * are fully written, dk = dv = 0 for keys no query sees.  Every tensor
+ * pointer (q, k, v, o, dout, dq, dk, dv) must be 16-byte aligned
+ * (SKV_ESHAPE otherwise).
  * plan_kv is a BWD plan (key ranges; dK, dV are owned by their item);
  * plan_q is a FWD plan over the forward's items or chunk runs
  * (skv_coarsen_fwd_items): each item writes one dQ partial for all its

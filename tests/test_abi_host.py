@@ -233,6 +233,12 @@ def test_device_calls_reject_bad_arguments_before_touching_the_gpu():
     tq = B.skv_plan(B.SKV_ITEM_FWD, 4, 1, 16, 16, 32, 0, 0, 64)
     rc = B.lib.sparse_attn_bwd(C.byref(pb.c), C.byref(tk), C.byref(tq), *([fake] * 10), need, None, None)
     assert rc == B.SKV_EPLAN and "ticks" in B.last_error()   # shared ticks arrays are rejected
+    kp2 = B.skv_plan(B.SKV_ITEM_BWD, 4, 1, 16, 16, 48)
+    for i in (7, 8):                               # dk, dv written with 16-byte stores
+        args = [fake] * 10
+        args[i] = C.c_void_p(4098)
+        rc = B.lib.sparse_attn_bwd(C.byref(pb.c), C.byref(kp2), C.byref(qplan), *args, need, None, None)
+        assert rc == B.SKV_ESHAPE and "aligned" in B.last_error()
     # the no-allocation backward: the same checks, and problems whose workspace
     # exceeds the static scratch are rejected before any device work
     rc = B.lib.sparse_attn_bwd_noalloc(C.byref(pb.c), C.byref(bplan), C.byref(plan), *([fake] * 9), None, None)
