@@ -310,16 +310,37 @@ void bwd_kv_kernel(BwdArgs a) {
           asm volatile("" : "+v"(qt0), "+v"(qt1), "+v"(ot0), "+v"(ot1));
 
           // ---- S = Q K^T and dP = dO V^T for 32 rows x this wave's 32 keys ----
+          // Two single chains (S, then dP), each with its LDS operands read one
+          // k step ahead; interleaved, the compiler sank the reads back next to
+          // their MFMAs and every step waited out a full LDS round trip.
           f32x16 sacc = f32x16{}, pacc = f32x16{};
+          const uint16_t* kw_ = sK + (wave * 32 + l32) * LDS_ROW + hf * 8;
+          {
+            bf16x8 qa = lds_load_bf16x8(bq + so.row_off[0]);
+            bf16x8 kf = lds_load_bf16x8(kw_);
 #pragma unroll
-          for (int ks = 0; ks < 8; ++ks) {
-            if (ks & 1) asm volatile("" ::: "memory");  // bounds how far the compiler hoists the reads
-            const int ro = so.row_off[ks & 1] + (ks & ~1) * 16;
-            const bf16x8 qa = lds_load_bf16x8(bq + ro);
-            const bf16x8 oa = lds_load_bf16x8(bo + ro);
-            const bf16x8 kf = lds_load_bf16x8(sK + (wave * 32 + l32) * LDS_ROW + ks * 16 + hf * 8);
-            sacc = mfma32x32x16(qa, kf, sacc);
-            pacc = mfma32x32x16(oa, vreg[ks], pacc);
+            for (int ks = 0; ks < 8; ++ks) {
+              bf16x8 qn = qa, kn = kf;
+              if (ks + 1 < 8) {
+                const int ro = so.row_off[(ks + 1) & 1] + ((ks + 1) & ~1) * 16;
+                qn = lds_load_bf16x8(bq + ro);
+                kn = lds_load_bf16x8(kw_ + (ks + 1) * 16);
+              }
+              sacc = mfma32x32x16(qa, kf, sacc);
+              asm volatile("" ::: "memory");
+              qa = qn; kf = kn;
+            }
+          }
+          {
+            bf16x8 oa = lds_load_bf16x8(bo + so.row_off[0]);
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks) {
+              bf16x8 on = oa;
+              if (ks + 1 < 8) on = lds_load_bf16x8(bo + so.row_off[(ks + 1) & 1] + ((ks + 1) & ~1) * 16);
+              pacc = mfma32x32x16(oa, vreg[ks], pacc);
+              asm volatile("" ::: "memory");
+              oa = on;
+            }
           }
           // ---- P = exp2(s*c - LSE2) on visible entries, dS = P (dP - Delta) ----
           // lane holds key key_w, rows 8i + 4hf + j (element 4i + j).  Rows are
@@ -571,13 +592,27 @@ void bwd_dq_kernel(BwdArgs a) {
             const uint16_t* kh = sK + mt * 32 * LDS_ROW_KV;
             const uint16_t* vh = sV + mt * 32 * LDS_ROW_KV;
             f32x16 sacc = f32x16{}, pacc = f32x16{};
+            {  // S^T chain, operands read one k step ahead
+              bf16x8 kf = lds_load_bf16x8(kh + kv_row_off[0]);
 #pragma unroll
-            for (int ks = 0; ks < 8; ++ks) {
-              const int o = kv_row_off[ks & 1] + (ks & ~1) * 16;
-              const bf16x8 kf = lds_load_bf16x8(kh + o);
-              const bf16x8 vf = lds_load_bf16x8(vh + o);
-              sacc = mfma32x32x16(kf, qf[ks], sacc);
-              pacc = mfma32x32x16(vf, of[ks], pacc);
+              for (int ks = 0; ks < 8; ++ks) {
+                bf16x8 kn = kf;
+                if (ks + 1 < 8) kn = lds_load_bf16x8(kh + kv_row_off[(ks + 1) & 1] + ((ks + 1) & ~1) * 16);
+                sacc = mfma32x32x16(kf, qf[ks], sacc);
+                asm volatile("" ::: "memory");
+                kf = kn;
+              }
+            }
+            {  // dP^T chain
+              bf16x8 vf = lds_load_bf16x8(vh + kv_row_off[0]);
+#pragma unroll
+              for (int ks = 0; ks < 8; ++ks) {
+                bf16x8 vn = vf;
+                if (ks + 1 < 8) vn = lds_load_bf16x8(vh + kv_row_off[(ks + 1) & 1] + ((ks + 1) & ~1) * 16);
+                pacc = mfma32x32x16(vf, of[ks], pacc);
+                asm volatile("" ::: "memory");
+                vf = vn;
+              }
             }
             // element e holds key kb + mt*32 + 8*(e/4) + 4*hf + e%4 of this lane's row
 #pragma unroll
@@ -589,17 +624,20 @@ void bwd_dq_kernel(BwdArgs a) {
               }
               sacc[e2] = pe * (pacc[e2] - del);
             }
+            // dQ^T += K^T dS^T, the K^T operand read one step ahead
+            const bf16x8 df0 = to_bf16x8(sacc[0], sacc[1], sacc[2], sacc[3], sacc[4], sacc[5], sacc[6], sacc[7]);
+            const bf16x8 df1 = to_bf16x8(sacc[8], sacc[9], sacc[10], sacc[11], sacc[12], sacc[13], sacc[14], sacc[15]);
+            bf16x8 kt = lds_tr_pair(sK + kt_off[0] + 2 * mt * 16 * LDS_ROW_KV, sK + kt_off[1] + 2 * mt * 16 * LDS_ROW_KV);
 #pragma unroll
-            for (int half = 0; half < 2; ++half) {
-              const int qh = half * 8;
-              const bf16x8 df = to_bf16x8(sacc[qh + 0], sacc[qh + 1], sacc[qh + 2], sacc[qh + 3], sacc[qh + 4],
-                                          sacc[qh + 5], sacc[qh + 6], sacc[qh + 7]);
-#pragma unroll
-              for (int md = 0; md < 4; ++md) {
-                const int o = (2 * mt + half) * 16 * LDS_ROW_KV + md * 32;
-                const bf16x8 kt = lds_tr_pair(sK + kt_off[0] + o, sK + kt_off[1] + o);
-                acc[md] = mfma32x32x16(kt, df, acc[md]);
+            for (int st = 0; st < 8; ++st) {  // st = half * 4 + md
+              bf16x8 ktn = kt;
+              if (st + 1 < 8) {
+                const int o = (2 * mt + ((st + 1) >> 2)) * 16 * LDS_ROW_KV + ((st + 1) & 3) * 32;
+                ktn = lds_tr_pair(sK + kt_off[0] + o, sK + kt_off[1] + o);
               }
+              acc[st & 3] = mfma32x32x16(kt, (st >> 2) ? df1 : df0, acc[st & 3]);
+              asm volatile("" ::: "memory");
+              kt = ktn;
             }
           }
         };
