@@ -22,7 +22,9 @@
 //      those keys (anchors are sorted, so those rows are a suffix of the draft
 //      blocks); the next tile's Q, dO, LSE, Delta load while the current one
 //      is computed.  S = Q K^T, dP = dO V^T (A from LDS), P and dS in
-//      registers, dV += P^T dO and dK += dS^T Q (B read transposed from LDS).
+//      registers, dV^T += dO^T P and dK^T += Q^T dS (A read transposed from
+//      LDS), so each lane ends with runs of consecutive head-dim values of one
+//      key and dK, dV leave as 16-byte stores.
 //   3. query-owner kernel over the forward's items (sequence, KV head, run of
 //      consecutive chunks, draft blocks), structured like the forward: 8
 //      waves (two per SIMD, so one wave's LDS waits and dS arithmetic overlap
@@ -357,7 +359,7 @@ void bwd_kv_kernel(BwdArgs a) {
                 if (key_w >= ends[j]) sacc[4 * i + j] = -INFINITY;
             }
           }
-          // ---- dV += P^T dO, dK += dS^T Q (A from registers, B transposed from LDS) ----
+          // ---- dV^T += dO^T P, dK^T += Q^T dS (A transposed from LDS, B = P, dS from registers) ----
 #pragma unroll
           for (int kstep = 0; kstep < 2; ++kstep) {
             const int qh = kstep * 8;
