@@ -28,10 +28,13 @@
 // exp2 domain with lazy rescaling (the reference maximum only moves when the
 // true maximum exceeds it by 2^8; the output is corrected to the true maximum
 // once per item), O^T += V^T P^T with P^T taken straight from the S^T
-// accumulators.  The scores of tile t+1 are computed before the exponentials
-// and PV products of tile t (software pipeline), every LDS operand is read one
-// MFMA step ahead of its use, and K/V tiles are fetched through buffer
-// descriptors so that the per-tile address work is scalar.
+// accumulators.  Each tile's scores are computed right before its softmax:
+// the wave's own MFMA latency is covered by the other wave of its SIMD, and a
+// cross-tile pipeline (the scores of tile t+1 before the softmax of tile t)
+// measured 4% slower, for its second set of score registers and their copies.
+// Every LDS operand is read one MFMA step ahead of its use, and K/V tiles are
+// fetched through buffer descriptors so that the per-tile address work is
+// scalar.
 #include "device.h"
 #include "launch.h"
 #include "timing.h"
@@ -246,10 +249,7 @@ void fwd_bf16_kernel(FwdArgs a) {
         }
       };
 
-      // Software pipeline: the scores of tile t+1 are issued together with
-      // the softmax and PV products of tile t, so no wave waits on its own
-      // MFMA results inside a tile.
-      f32x16 scur[2], snext[2];
+      f32x16 scur[2];  // this tile's scores S^T
       for (int t = 0; t < ntiles; ++t) {
         const int kb = klo + t * KT;
         if (t + 1 < ntiles) {
@@ -258,7 +258,7 @@ void fwd_bf16_kernel(FwdArgs a) {
         }
         __syncthreads();
         if (kb >= wave_hi) continue;  // no row of this wave sees the tile (nor any later one)
-        if (t == 0) scores(0, scur);
+        scores(t % NBUF, scur);
 
         // ---- mask keys at or past the row's prefix end (partial tiles only) ----
         if (kb + KT > wave_full) {
@@ -287,8 +287,6 @@ void fwd_bf16_kernel(FwdArgs a) {
             for (int md = 0; md < 4; ++md) acc_o[md] *= alpha;
           }
         }
-        // ---- scores of tile t+1, if some row of this wave sees it ----
-        if (kb + KT < wave_hi) scores((t + 1) % NBUF, snext);
         // ---- P = exp2(s*c - m_ref*c), 16 keys at a time right before their
         //      part of O^T += V^T P^T; the row sum in fp32 (bf16-rounded P
         //      would cost the log-sum-exp up to 2^-9 relative on short rows).
@@ -329,8 +327,6 @@ void fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
           for (int md = 0; md < 4; ++md) vc[md] = vn[md];
         }
-        scur[0] = snext[0];
-        scur[1] = snext[1];
       }
 
       // ---- epilogue: unnormalised O_c against the true row max, max and log-sum-exp ----
