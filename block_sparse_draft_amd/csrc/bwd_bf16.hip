@@ -171,7 +171,7 @@ constexpr int QT = 32;                // query rows per tile
 
 struct QTileMeta {
   float lse[QT];    // LSE of each row, log2 units (+inf for padding rows: P = 0)
-  float delta[QT];
+  float delta[QT];  // -Delta of each row
   int end[QT];      // prefix end e_b of the row (keys at or past it are masked)
 };
 
@@ -254,7 +254,7 @@ void bwd_kv_kernel(BwdArgs a) {
         *reinterpret_cast<uint4*>(sdO[buf] + st_off) = r.o;
         if (tid < QT) {
           sMeta[buf].lse[tid] = r.lse;
-          sMeta[buf].delta[tid] = r.delta;
+          sMeta[buf].delta[tid] = -r.delta;  // the dP accumulators start at -Delta
           sMeta[buf].end[tid] = r.end;
         }
       };
@@ -334,6 +334,14 @@ void bwd_kv_kernel(BwdArgs a) {
             }
           }
           {
+            // dP - Delta: the accumulators start at -Delta of their rows
+            // (element 4i + j: row 8i + 4hf + j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const f32x4 nd4 = *reinterpret_cast<const f32x4*>(&M.delta[8 * i + 4 * hf]);
+#pragma unroll
+              for (int j = 0; j < 4; ++j) pacc[4 * i + j] = nd4[j];
+            }
             bf16x8 oa = lds_load_bf16x8(bo + so.row_off[0]);
 #pragma unroll
             for (int ks = 0; ks < 8; ++ks) {
@@ -369,12 +377,11 @@ void bwd_kv_kernel(BwdArgs a) {
               const int i = (qh >> 2) + ii;
               const int r0 = 8 * i + 4 * hf;
               const f32x4 lse4 = *reinterpret_cast<const f32x4*>(&M.lse[r0]);
-              const f32x4 del4 = *reinterpret_cast<const f32x4*>(&M.delta[r0]);
 #pragma unroll
               for (int j = 0; j < 4; ++j) {
                 const float p = fast_exp2(__builtin_fmaf(sacc[4 * i + j], c, -lse4[j]));
                 pv[4 * ii + j] = p;
-                dv8[4 * ii + j] = p * (pacc[4 * i + j] - del4[j]);
+                dv8[4 * ii + j] = p * pacc[4 * i + j];  // pacc holds dP - Delta
               }
             }
             const bf16x8 pa = to_bf16x8(pv[0], pv[1], pv[2], pv[3], pv[4], pv[5], pv[6], pv[7]);
@@ -605,7 +612,9 @@ void bwd_dq_kernel(BwdArgs a) {
                 kf = kn;
               }
             }
-            {  // dP^T chain
+            {  // dP^T - Delta chain: the accumulator starts at -Delta of this lane's row
+#pragma unroll
+              for (int e2 = 0; e2 < 16; ++e2) pacc[e2] = -del;
               bf16x8 vf = lds_load_bf16x8(vh + kv_row_off[0]);
 #pragma unroll
               for (int ks = 0; ks < 8; ++ks) {
@@ -624,7 +633,7 @@ void bwd_dq_kernel(BwdArgs a) {
                 const int key = kb + mt * 32 + (e2 >> 2) * 8 + hf * 4 + (e2 & 3);
                 if (key >= vend) pe = 0.f;
               }
-              sacc[e2] = pe * (pacc[e2] - del);
+              sacc[e2] = pe * pacc[e2];  // pacc holds dP - Delta
             }
             // dQ^T += K^T dS^T, the K^T operand read one step ahead
             const bf16x8 df0 = to_bf16x8(sacc[0], sacc[1], sacc[2], sacc[3], sacc[4], sacc[5], sacc[6], sacc[7]);
