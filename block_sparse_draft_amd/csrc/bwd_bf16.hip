@@ -588,8 +588,20 @@ void bwd_dq_kernel(BwdArgs a) {
         }
         __syncthreads();
         if (kb >= wave_hi) continue;  // no row of this wave sees the tile (nor any later one)
-        const uint16_t* sK = sKV[t % DQ_NBUF][0];
-        const uint16_t* sV = sKV[t % DQ_NBUF][1];
+        // 32-bit LDS addresses of this lane's reads in the tile's buffers; the
+        // empty asm keeps every per-read offset an immediate instead of one
+        // address add per read.
+        uint32_t ka[2], va[2], kt[2];
+        {
+          const uint32_t kb_ = lds_addr(sKV[t % DQ_NBUF][0]), vb_ = lds_addr(sKV[t % DQ_NBUF][1]);
+#pragma unroll
+          for (int k = 0; k < 2; ++k) {
+            ka[k] = kb_ + 2u * kv_row_off[k];
+            va[k] = vb_ + 2u * kv_row_off[k];
+            kt[k] = kb_ + 2u * kt_off[k];
+          }
+          asm volatile("" : "+v"(ka[0]), "+v"(ka[1]), "+v"(va[0]), "+v"(va[1]), "+v"(kt[0]), "+v"(kt[1]));
+        }
 
         // Per 32-key half mt: S^T = K Q^T and dP^T = V dO^T (A from LDS),
         // dS^T = P^T (dP^T - Delta) with P^T = exp2(s*c - LSE2) on visible keys,
@@ -598,15 +610,14 @@ void bwd_dq_kernel(BwdArgs a) {
           constexpr bool MASK = decltype(mask_c)::value;  // partial tile: keys past a row's end are masked
 #pragma unroll
           for (int mt = 0; mt < 2; ++mt) {
-            const uint16_t* kh = sK + mt * 32 * LDS_ROW_KV;
-            const uint16_t* vh = sV + mt * 32 * LDS_ROW_KV;
+            const uint32_t mo = 2u * (mt * 32 * LDS_ROW_KV);  // byte offset of the half's rows
             f32x16 sacc = f32x16{}, pacc = f32x16{};
             {  // S^T chain, operands read one k step ahead
-              bf16x8 kf = lds_load_bf16x8(kh + kv_row_off[0]);
+              bf16x8 kf = lds_read_b128(ka[0] + mo);
 #pragma unroll
               for (int ks = 0; ks < 8; ++ks) {
                 bf16x8 kn = kf;
-                if (ks + 1 < 8) kn = lds_load_bf16x8(kh + kv_row_off[(ks + 1) & 1] + ((ks + 1) & ~1) * 16);
+                if (ks + 1 < 8) kn = lds_read_b128(ka[(ks + 1) & 1] + mo + 2u * (((ks + 1) & ~1) * 16));
                 sacc = mfma32x32x16(kf, qf[ks], sacc);
                 asm volatile("" ::: "memory");
                 kf = kn;
@@ -615,40 +626,38 @@ void bwd_dq_kernel(BwdArgs a) {
             {  // dP^T - Delta chain: the accumulator starts at -Delta of this lane's row
 #pragma unroll
               for (int e2 = 0; e2 < 16; ++e2) pacc[e2] = -del;
-              bf16x8 vf = lds_load_bf16x8(vh + kv_row_off[0]);
+              bf16x8 vf = lds_read_b128(va[0] + mo);
 #pragma unroll
               for (int ks = 0; ks < 8; ++ks) {
                 bf16x8 vn = vf;
-                if (ks + 1 < 8) vn = lds_load_bf16x8(vh + kv_row_off[(ks + 1) & 1] + ((ks + 1) & ~1) * 16);
+                if (ks + 1 < 8) vn = lds_read_b128(va[(ks + 1) & 1] + mo + 2u * (((ks + 1) & ~1) * 16));
                 pacc = mfma32x32x16(vf, of[ks], pacc);
                 asm volatile("" ::: "memory");
                 vf = vn;
               }
             }
             // element e holds key kb + mt*32 + 8*(e/4) + 4*hf + e%4 of this lane's row
+            const int lim = vend - kb - mt * 32 - hf * 4;  // keys at or past the row's end are masked
 #pragma unroll
             for (int e2 = 0; e2 < 16; ++e2) {
               float pe = fast_exp2(__builtin_fmaf(sacc[e2], c, -lse2));
-              if (MASK) {
-                const int key = kb + mt * 32 + (e2 >> 2) * 8 + hf * 4 + (e2 & 3);
-                if (key >= vend) pe = 0.f;
-              }
+              if (MASK && (e2 >> 2) * 8 + (e2 & 3) >= lim) pe = 0.f;
               sacc[e2] = pe * pacc[e2];  // pacc holds dP - Delta
             }
             // dQ^T += K^T dS^T, the K^T operand read one step ahead
             const bf16x8 df0 = to_bf16x8(sacc[0], sacc[1], sacc[2], sacc[3], sacc[4], sacc[5], sacc[6], sacc[7]);
             const bf16x8 df1 = to_bf16x8(sacc[8], sacc[9], sacc[10], sacc[11], sacc[12], sacc[13], sacc[14], sacc[15]);
-            bf16x8 kt = lds_tr_pair(sK + kt_off[0] + 2 * mt * 16 * LDS_ROW_KV, sK + kt_off[1] + 2 * mt * 16 * LDS_ROW_KV);
+            bf16x8 ktc = lds_tr_pair(kt[0] + 2u * (2 * mt * 16 * LDS_ROW_KV), kt[1] + 2u * (2 * mt * 16 * LDS_ROW_KV));
 #pragma unroll
             for (int st = 0; st < 8; ++st) {  // st = half * 4 + md
-              bf16x8 ktn = kt;
+              bf16x8 ktn = ktc;
               if (st + 1 < 8) {
                 const int o = (2 * mt + ((st + 1) >> 2)) * 16 * LDS_ROW_KV + ((st + 1) & 3) * 32;
-                ktn = lds_tr_pair(sK + kt_off[0] + o, sK + kt_off[1] + o);
+                ktn = lds_tr_pair(kt[0] + 2u * o, kt[1] + 2u * o);
               }
-              acc[st & 3] = mfma32x32x16(kt, (st >> 2) ? df1 : df0, acc[st & 3]);
+              acc[st & 3] = mfma32x32x16(ktc, (st >> 2) ? df1 : df0, acc[st & 3]);
               asm volatile("" ::: "memory");
-              kt = ktn;
+              ktc = ktn;
             }
           }
         };
