@@ -121,8 +121,31 @@ __device__ __forceinline__ void swap_lane_halves(uint32_t& lo, uint32_t& hi) {
   hi = r[1];
 }
 
+// max(x, x of lane ^ 32) in every lane, without an LDS permute: after the swap
+// lane l < 32 holds x[l] and x[l + 32] in its two registers, lane l >= 32
+// x[l - 32] and x[l].
+__device__ __forceinline__ float max_lane_halves(float x) {
+  uint32_t a = __float_as_uint(x), b = a;
+  swap_lane_halves(a, b);
+  return fmaxf(__uint_as_float(a), __uint_as_float(b));
+}
+__device__ __forceinline__ float sum_lane_halves(float x) {
+  uint32_t a = __float_as_uint(x), b = a;
+  swap_lane_halves(a, b);
+  return __uint_as_float(a) + __uint_as_float(b);
+}
+
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
   return __builtin_bit_cast(uint16_t, (__bf16)x);
+}
+
+// max(a, b, c) as one v_max3_f32 (the compiler otherwise pairs plain v_max
+// ahead of each v_max3); not volatile, so it schedules like any VALU op.  For
+// kernels built without IEEE mode (no NaN quieting).
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
 }
 
 __device__ __forceinline__ float wave_max(float x) {

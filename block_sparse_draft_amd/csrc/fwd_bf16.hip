@@ -271,10 +271,14 @@ void fwd_bf16_kernel(FwdArgs a) {
               if (mt * 32 + (e2 >> 2) * 8 + (e2 & 3) >= lim) scur[mt][e2] = -INFINITY;
         }
         // ---- row max; lazy rescale when the row's max grew past 2^8 ----
-        float r0 = fmaxf(scur[0][0], scur[1][0]);
+        // two v_max3 chains (one per 32-key half), two new scores per instruction
+        float r0 = fmaxf(scur[0][0], scur[0][1]), r1 = fmaxf(scur[1][0], scur[1][1]);
 #pragma unroll
-        for (int e2 = 1; e2 < 16; ++e2) r0 = fmaxf(r0, fmaxf(scur[0][e2], scur[1][e2]));
-        r0 = fmaxf(r0, __shfl_xor(r0, 32));
+        for (int e2 = 2; e2 < 16; e2 += 2) {
+          r0 = max3f(r0, scur[0][e2], scur[0][e2 + 1]);
+          r1 = max3f(r1, scur[1][e2], scur[1][e2 + 1]);
+        }
+        r0 = max_lane_halves(fmaxf(r0, r1));
         m_true = fmaxf(m_true, r0);
         const bool grow = (m_true - m_ref) * c > LAZY_LOG2;  // false while both are -inf
         if (__any(grow)) {
@@ -330,7 +334,7 @@ void fwd_bf16_kernel(FwdArgs a) {
       }
 
       // ---- epilogue: unnormalised O_c against the true row max, max and log-sum-exp ----
-      float lt = l + __shfl_xor(l, 32);
+      float lt = sum_lane_halves(l);
       if (valid) {
         const bool seen = lt > 0.f;
         const float fix = seen ? fast_exp2((m_ref - m_true) * c) : 1.f;
