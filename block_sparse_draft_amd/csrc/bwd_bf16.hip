@@ -170,7 +170,7 @@ constexpr int KV_KEYS = 32 * KV_WAVES; // keys per workgroup pass: 32 per wave
 constexpr int QT = 32;                // query rows per tile
 
 struct QTileMeta {
-  float lse[QT];    // LSE of each row, log2 units (+inf for padding rows: P = 0)
+  float lse[QT];    // -LSE2 / c of each row (LSE2 in log2 units; -inf for padding rows: P = 0)
   float delta[QT];  // -Delta of each row
   int end[QT];      // prefix end e_b of the row (keys at or past it are masked)
 };
@@ -196,6 +196,7 @@ void bwd_kv_kernel(BwdArgs a) {
   uint16_t* dV = static_cast<uint16_t*>(a.dv);
   const int GB = a.group * a.block;
   const float c = a.scale_log2;
+  const float inv_c = 1.f / c;
 
   const uint64_t t_start = __builtin_amdgcn_s_memrealtime();
   const int me = plan_worker();
@@ -253,7 +254,7 @@ void bwd_kv_kernel(BwdArgs a) {
         *reinterpret_cast<uint4*>(sQ[buf] + st_off) = r.q;
         *reinterpret_cast<uint4*>(sdO[buf] + st_off) = r.o;
         if (tid < QT) {
-          sMeta[buf].lse[tid] = r.lse;
+          sMeta[buf].lse[tid] = -r.lse * inv_c;  // the S accumulators start here
           sMeta[buf].delta[tid] = -r.delta;  // the dP accumulators start at -Delta
           sMeta[buf].end[tid] = r.end;
         }
@@ -315,9 +316,17 @@ void bwd_kv_kernel(BwdArgs a) {
           // Two single chains (S, then dP), each with its LDS operands read one
           // k step ahead; interleaved, the compiler sank the reads back next to
           // their MFMAs and every step waited out a full LDS round trip.
-          f32x16 sacc = f32x16{}, pacc = f32x16{};
+          f32x16 sacc, pacc = f32x16{};
           const uint16_t* kw_ = sK + (wave * 32 + l32) * LDS_ROW + hf * 8;
           {
+            // S - LSE2/c: the accumulators start at -LSE2/c of their rows
+            // (element 4i + j: row 8i + 4hf + j), so P = exp2(c * acc)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const f32x4 nl4 = *reinterpret_cast<const f32x4*>(&M.lse[8 * i + 4 * hf]);
+#pragma unroll
+              for (int j = 0; j < 4; ++j) sacc[4 * i + j] = nl4[j];
+            }
             bf16x8 qa = lds_load_bf16x8(bq + so.row_off[0]);
             bf16x8 kf = lds_load_bf16x8(kw_);
 #pragma unroll
@@ -375,11 +384,9 @@ void bwd_kv_kernel(BwdArgs a) {
 #pragma unroll
             for (int ii = 0; ii < 2; ++ii) {
               const int i = (qh >> 2) + ii;
-              const int r0 = 8 * i + 4 * hf;
-              const f32x4 lse4 = *reinterpret_cast<const f32x4*>(&M.lse[r0]);
 #pragma unroll
               for (int j = 0; j < 4; ++j) {
-                const float p = fast_exp2(__builtin_fmaf(sacc[4 * i + j], c, -lse4[j]));
+                const float p = fast_exp2(sacc[4 * i + j] * c);  // sacc holds s - LSE2/c
                 pv[4 * ii + j] = p;
                 dv8[4 * ii + j] = p * pacc[4 * i + j];  // pacc holds dP - Delta
               }
