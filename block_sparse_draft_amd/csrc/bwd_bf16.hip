@@ -24,7 +24,9 @@
 //      is computed.  S = Q K^T, dP = dO V^T (A from LDS), P and dS in
 //      registers, dV^T += dO^T P and dK^T += Q^T dS (A read transposed from
 //      LDS), so each lane ends with runs of consecutive head-dim values of one
-//      key and dK, dV leave as 16-byte stores.
+//      key and dK, dV leave as 16-byte stores.  The exponentials of P are
+//      taken between the dP products and half of dS between the dV/dK
+//      products, so that this VALU work issues while the matrix core runs.
 //   3. query-owner kernel over the forward's items (sequence, KV head, run of
 //      consecutive chunks, draft blocks), structured like the forward: 8
 //      waves (two per SIMD, so one wave's LDS waits and dS arithmetic overlap
@@ -344,7 +346,9 @@ void bwd_kv_kernel(BwdArgs a) {
           }
           {
             // dP - Delta: the accumulators start at -Delta of their rows
-            // (element 4i + j: row 8i + 4hf + j)
+            // (element 4i + j: row 8i + 4hf + j).  P = exp2(c * acc) is taken
+            // in place in the S accumulators, two entries per dP step, so the
+            // exponentials issue while the dP products run.
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
               const f32x4 nd4 = *reinterpret_cast<const f32x4*>(&M.delta[8 * i + 4 * hf]);
@@ -357,11 +361,13 @@ void bwd_kv_kernel(BwdArgs a) {
               bf16x8 on = oa;
               if (ks + 1 < 8) on = lds_load_bf16x8(bo + so.row_off[(ks + 1) & 1] + ((ks + 1) & ~1) * 16);
               pacc = mfma32x32x16(oa, vreg[ks], pacc);
+              sacc[2 * ks] = fast_exp2(sacc[2 * ks] * c);  // sacc holds s - LSE2/c
+              sacc[2 * ks + 1] = fast_exp2(sacc[2 * ks + 1] * c);
               asm volatile("" ::: "memory");
               oa = on;
             }
           }
-          // ---- P = exp2(s*c - LSE2) on visible entries, dS = P (dP - Delta) ----
+          // ---- P = 0 on masked entries, dS = P (dP - Delta) ----
           // lane holds key key_w, rows 8i + 4hf + j (element 4i + j).  Rows are
           // sorted by prefix end: if the tile's first row sees all of this
           // wave's keys (and no row is padding) no entry needs masking.
@@ -373,34 +379,41 @@ void bwd_kv_kernel(BwdArgs a) {
               const int ends[4] = {end4.x, end4.y, end4.z, end4.w};
 #pragma unroll
               for (int j = 0; j < 4; ++j)
-                if (key_w >= ends[j]) sacc[4 * i + j] = -INFINITY;
+                if (key_w >= ends[j]) sacc[4 * i + j] = 0.f;
             }
           }
           // ---- dV^T += dO^T P, dK^T += Q^T dS (A transposed from LDS, B = P, dS from registers) ----
+          // P and dS of rows 0-15 first; those of rows 16-31 are formed a pair
+          // at a time between the first half's products.  The transposed
+          // operands of each product pair are read one pair ahead.
+          uint32_t pk[2][4], dk2[2][4];
+          auto form = [&](int kstep, int u) {  // entries 8 kstep + 2u, +1
+            const int e = 8 * kstep + 2 * u;
+            pk[kstep][u] = pack_bf16x2(sacc[e], sacc[e + 1]);
+            dk2[kstep][u] = pack_bf16x2(sacc[e] * pacc[e], sacc[e + 1] * pacc[e + 1]);
+          };
+#pragma unroll
+          for (int u = 0; u < 4; ++u) form(0, u);
+          auto trq = [&](int kstep, int nd) { const uint32_t to = 2u * (kstep * 16 * LDS_ROW_SW + nd * 32); return lds_tr_pair(qt0 + to, qt1 + to); };
+          auto tro = [&](int kstep, int nd) { const uint32_t to = 2u * (kstep * 16 * LDS_ROW_SW + nd * 32); return lds_tr_pair(ot0 + to, ot1 + to); };
+          bf16x8 ob = tro(0, 0), qb = trq(0, 0);
 #pragma unroll
           for (int kstep = 0; kstep < 2; ++kstep) {
-            const int qh = kstep * 8;
-            float pv[8], dv8[8];
-#pragma unroll
-            for (int ii = 0; ii < 2; ++ii) {
-              const int i = (qh >> 2) + ii;
-#pragma unroll
-              for (int j = 0; j < 4; ++j) {
-                const float p = fast_exp2(sacc[4 * i + j] * c);  // sacc holds s - LSE2/c
-                pv[4 * ii + j] = p;
-                dv8[4 * ii + j] = p * pacc[4 * i + j];  // pacc holds dP - Delta
-              }
-            }
-            const bf16x8 pa = to_bf16x8(pv[0], pv[1], pv[2], pv[3], pv[4], pv[5], pv[6], pv[7]);
-            const bf16x8 da = to_bf16x8(dv8[0], dv8[1], dv8[2], dv8[3], dv8[4], dv8[5], dv8[6], dv8[7]);
+            const bf16x8 pa = __builtin_bit_cast(bf16x8, uint4{pk[kstep][0], pk[kstep][1], pk[kstep][2], pk[kstep][3]});
+            const bf16x8 da = __builtin_bit_cast(bf16x8, uint4{dk2[kstep][0], dk2[kstep][1], dk2[kstep][2], dk2[kstep][3]});
 #pragma unroll
             for (int nd = 0; nd < 4; ++nd) {
-              asm volatile("" ::: "memory");
-              const uint32_t to = 2u * (kstep * 16 * LDS_ROW_SW + nd * 32);
-              const bf16x8 ob = lds_tr_pair(ot0 + to, ot1 + to);
-              const bf16x8 qb = lds_tr_pair(qt0 + to, qt1 + to);
+              bf16x8 obn = ob, qbn = qb;
+              if (kstep * 4 + nd + 1 < 8) {
+                const int k2 = (kstep * 4 + nd + 1) >> 2, n2 = (nd + 1) & 3;
+                obn = tro(k2, n2);
+                qbn = trq(k2, n2);
+              }
               dv_acc[nd] = mfma32x32x16(ob, pa, dv_acc[nd]);  // dV^T: head dim x keys
               dk_acc[nd] = mfma32x32x16(qb, da, dk_acc[nd]);  // dK^T
+              if (kstep == 0) form(1, nd);
+              asm volatile("" ::: "memory");
+              ob = obn; qb = qbn;
             }
           }
         }

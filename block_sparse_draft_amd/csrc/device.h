@@ -19,6 +19,7 @@ namespace skv {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -108,6 +109,14 @@ __device__ __forceinline__ bf16x8 to_bf16x8(float a0, float a1, float a2, float 
   r[0] = (__bf16)a0; r[1] = (__bf16)a1; r[2] = (__bf16)a2; r[3] = (__bf16)a3;
   r[4] = (__bf16)a4; r[5] = (__bf16)a5; r[6] = (__bf16)a6; r[7] = (__bf16)a7;
   return r;
+}
+
+// Round-to-nearest-even fp32 -> bf16 of two values, packed into one register
+// (one v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  bf16x2 r;
+  r[0] = (__bf16)a; r[1] = (__bf16)b;
+  return __builtin_bit_cast(uint32_t, r);
 }
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }

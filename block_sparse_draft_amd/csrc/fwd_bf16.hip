@@ -291,13 +291,13 @@ void fwd_bf16_kernel(FwdArgs a) {
             for (int md = 0; md < 4; ++md) acc_o[md] *= alpha;
           }
         }
-        // ---- P = exp2(s*c - m_ref*c), 16 keys at a time right before their
-        //      part of O^T += V^T P^T; the row sum in fp32 (bf16-rounded P
-        //      would cost the log-sum-exp up to 2^-9 relative on short rows).
-        //      The V operands of the next 16 keys are read before this step's
-        //      MFMAs, so they arrive while the next exponentials are computed;
-        //      the empty asm ends each step's scheduling region, which bounds
-        //      how many operands the compiler keeps in flight. ----
+        // ---- P = exp2(s*c - m_ref*c), 16 keys per step of O^T += V^T P^T;
+        //      the row sum in fp32 (bf16-rounded P would cost the log-sum-exp
+        //      up to 2^-9 relative on short rows).  The next step's
+        //      exponentials are taken between this step's four MFMAs, so they
+        //      issue while the products run, and its V operands are read
+        //      before them; the empty asm ends each step's scheduling region,
+        //      which bounds how many operands the compiler keeps in flight. ----
         // Row md*32 + l32, key chunk 2 kstep + hf, swizzle f = (l32 / 4) % 8:
         // this lane's chunk pair sits at 32-byte slot kstep ^ (f / 2), its
         // half at 16 (hf ^ f % 2), the same for every md.
@@ -308,25 +308,38 @@ void fwd_bf16_kernel(FwdArgs a) {
         asm volatile("" : "+v"(va[0]), "+v"(va[1]), "+v"(va[2]), "+v"(va[3]));
         auto vaddr = [&](int md, int ks) { return va[ks] + 2u * (md * 32 * LDS_ROW_VT); };
         const float mc = m_ref == -INFINITY ? 0.f : m_ref * c;
+        // P of step kstep: entries 8 (kstep % 2) .. +7 of half kstep / 2, as
+        // four bf16 pairs; the row sum adds them in a fixed tree.
+        uint32_t pk[2][4];
+        float ps[2][4];
+        auto form = [&](int kstep, int u) {
+          const f32x16& sv = scur[kstep >> 1];
+          const int e = (kstep & 1) * 8 + 2 * u;
+          const float p0 = fast_exp2(__builtin_fmaf(sv[e], c, -mc));
+          const float p1 = fast_exp2(__builtin_fmaf(sv[e + 1], c, -mc));
+          pk[kstep & 1][u] = pack_bf16x2(p0, p1);
+          ps[kstep & 1][u] = p0 + p1;
+        };
         bf16x8 vc[4];
 #pragma unroll
         for (int md = 0; md < 4; ++md) vc[md] = lds_read_b128(vaddr(md, 0));
 #pragma unroll
-        for (int kstep = 0; kstep < 4; ++kstep) {
-          const int mt = kstep >> 1, qh = (kstep & 1) * 8;
-          const f32x16& sv = scur[mt];
-          float pe[8];
+        for (int u = 0; u < 4; ++u) form(0, u);
 #pragma unroll
-          for (int u = 0; u < 8; ++u) pe[u] = fast_exp2(__builtin_fmaf(sv[qh + u], c, -mc));
-          const bf16x8 pf = to_bf16x8(pe[0], pe[1], pe[2], pe[3], pe[4], pe[5], pe[6], pe[7]);
-          l += ((pe[0] + pe[1]) + (pe[2] + pe[3])) + ((pe[4] + pe[5]) + (pe[6] + pe[7]));
+        for (int kstep = 0; kstep < 4; ++kstep) {
+          const int b = kstep & 1;
+          const bf16x8 pf = __builtin_bit_cast(bf16x8, uint4{pk[b][0], pk[b][1], pk[b][2], pk[b][3]});
+          l += (ps[b][0] + ps[b][1]) + (ps[b][2] + ps[b][3]);
           bf16x8 vn[4] = {vc[0], vc[1], vc[2], vc[3]};
           if (kstep + 1 < 4) {
 #pragma unroll
             for (int md = 0; md < 4; ++md) vn[md] = lds_read_b128(vaddr(md, kstep + 1));
           }
 #pragma unroll
-          for (int md = 0; md < 4; ++md) acc_o[md] = mfma32x32x16(vc[md], pf, acc_o[md]);
+          for (int md = 0; md < 4; ++md) {
+            acc_o[md] = mfma32x32x16(vc[md], pf, acc_o[md]);
+            if (kstep + 1 < 4) form(kstep + 1, md);
+          }
           asm volatile("" ::: "memory");
 #pragma unroll
           for (int md = 0; md < 4; ++md) vc[md] = vn[md];
