@@ -453,6 +453,12 @@ extern "C" int skv_plan_fwd_runs(const skv_item* items, const int64_t* cost, int
     for (int32_t w = 0; w < n_workers; ++w) mx = std::max(mx, load[w]);
     const double mean = (double)total / (double)n_workers;
     if (rpw >= max_runs_per_worker || mean == 0.0 || (double)mx / mean - 1.0 <= max_imbalance) break;
+    if (*n_out == n) {
+      // Every run is a single chunk: a smaller target merges nothing either,
+      // so each remaining step would return this same plan.
+      rpw = max_runs_per_worker;
+      break;
+    }
     rpw = std::min(2.0 * rpw, max_runs_per_worker);
   }
   *rpw_used = rpw;

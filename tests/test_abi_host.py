@@ -375,6 +375,7 @@ def _oracle_run_search(desc, cost, n_workers, start, stop, tol):
 @pytest.mark.parametrize("cfg,n_workers,start,stop,tol", [
     ("c3", 256, 4, 64, 0.02), ("c5", 256, 4, 64, 0.02), ("c4", 256, 4, 64, 0.02),
     ("c3", 13, 1, 64, 0.0), ("c5", 64, 2, 2, 0.02), ("c3", 256, 4, 64, 1e9), ("c2", 256, 0.5, 0.5, 0.02),
+    ("c2", 256, 4, 64, 0.02),
     ("c5", 100, 3, 40, 0.001)])
 def test_plan_fwd_runs_matches_oracle_search(cfg, n_workers, start, stop, tol):
     """skv_plan_fwd_runs picks the same run length as the search over the
