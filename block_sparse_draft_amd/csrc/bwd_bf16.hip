@@ -166,6 +166,13 @@ struct QTileRegs {
   int end;
 };
 
+// The lane's index, recomputed where it is called (v_mbcnt): values derived
+// from it are then formed in place rather than hoisted and kept in scratch.
+__device__ __forceinline__ int fresh_lane_id() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
 constexpr int KV_WAVES = 8;            // two per SIMD
 constexpr int KV_THREADS = 64 * KV_WAVES;
 constexpr int KV_KEYS = 32 * KV_WAVES; // keys per workgroup pass: 32 per wave
@@ -199,6 +206,7 @@ void bwd_kv_kernel(BwdArgs a) {
   const int GB = a.group * a.block;
   const float c = a.scale_log2;
   const float inv_c = 1.f / c;
+  const int kv_st = (int)a.kv_st;  // a sequence's K/V span fits 31 bits of bytes (checked on the host)
 
   const uint64_t t_start = __builtin_amdgcn_s_memrealtime();
   const int me = plan_worker();
@@ -235,21 +243,29 @@ void bwd_kv_kernel(BwdArgs a) {
       // Query tile loader: rows qt*32 + row of the visible suffix, contiguous
       // in the packed copies; padding rows read the last row and are masked.
       const int64_t vis0 = pbase + (int64_t)b_first * GB;  // packed index of the suffix's first row
+      // Query tile loads through buffer descriptors based at the tile's first
+      // packed row (scalar work), with fixed 32-bit per-lane offsets; rows
+      // past the suffix (padding of the last tile) read as zeros, and their
+      // LSE is set to +inf below, so they are masked.
+      const int tq = wave * 64 + fresh_lane_id();
+      const int qo = (tq >> 4) * (D * 2) + (tq & 15) * 16, mo = (tq & (QT - 1)) * 4;
       auto load_q = [&](int qt) {
         QTileRegs r;
-        const int row = min(tid >> 4, nq - 1 - qt * QT);
-        const int64_t off = (vis0 + qt * QT + row) * D + (tid & 15) * 8;
-        r.q = *reinterpret_cast<const uint4*>(a.qp + off);
-        r.o = *reinterpret_cast<const uint4*>(a.dop + off);
-        r.lse = INFINITY; r.delta = 0.f; r.end = kb;
-        if (tid < QT) {
-          const int p = qt * QT + tid;
-          const int64_t P = vis0 + min(p, nq - 1);
-          const float lse = a.lsep[P];
-          const float del = a.deltap[P];
-          const int e = a.endp[P];
-          if (p < nq) { r.lse = lse; r.delta = del; r.end = e; }
-        }
+        const int rows = min(nq - qt * QT, QT);
+        const int64_t row0 = vis0 + qt * QT;
+        const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.qp + row0 * D, rows * D * 2);
+        const __amdgpu_buffer_rsrc_t ro = make_rsrc(a.dop + row0 * D, rows * D * 2);
+        r.q = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rq, qo, 0, 0));
+        r.o = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ro, qo, 0, 0));
+        // every thread loads a row's LSE, Delta and end (only threads 0..31
+        // store them), so the loads issue with the tile's without a branch
+        const float lse = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(a.lsep + row0, rows * 4), mo, 0, 0));
+        const float del = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(a.deltap + row0, rows * 4), mo, 0, 0));
+        const int e = (int)__builtin_amdgcn_raw_buffer_load_b32(make_rsrc(a.endp + row0, rows * 4), mo, 0, 0);
+        const bool in = (tid & (QT - 1)) < rows;
+        r.lse = in ? lse : INFINITY;
+        r.delta = in ? del : 0.f;
+        r.end = in ? e : kb;
         return r;
       };
       auto store_q = [&](const QTileRegs& r, int buf) {
@@ -266,32 +282,40 @@ void bwd_kv_kernel(BwdArgs a) {
       // context are clamped to its last key and masked.
       const int kw0 = kb + wave * 32;           // first key of this wave
       const int key_w = kw0 + l32;
+      // The first query tile's loads go out first: its addresses need only
+      // b_first, and it is the last thing the pass waits for.
+      QTileRegs R;
+      if (ntq > 0) R = load_q(0);
+      // K and V of the pass's keys through buffer descriptors based at key kb:
+      // 32-bit offsets, and keys past the context read as zeros (their
+      // entries are masked and their dK, dV rows are not written).
+      const int kv_bytes = (n_ctx - kb) * kv_st * 2;
+      const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kseq + (int64_t)kb * a.kv_st, kv_bytes);
+      const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vseq + (int64_t)kb * a.kv_st, kv_bytes);
+      // per-lane offsets formed here and hidden from the compiler, which
+      // otherwise hoists them out of the loop and keeps them in scratch
+      const int tf = wave * 64 + fresh_lane_id();
+      const int vo = (wave * 32 + (tf & 31)) * kv_st * 2 + ((tf >> 5) & 1) * 16;
+      const int ko = (tf >> 4) * kv_st * 2 + (tf & 15) * 16;
       bf16x8 vreg[8];
-      {
-        const int kc = min(key_w, n_ctx - 1);
-        const uint16_t* vp = Vseq + (int64_t)kc * a.kv_st + hf * 8;
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) vreg[ks] = load_bf16x8(vp + ks * 16);
-      }
+      for (int ks = 0; ks < 8; ++ks)
+        vreg[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rv, vo + ks * 32, 0, 0));
+      uint4 kst[8];
+      // 256 keys x 16 chunks of 16 bytes: thread -> key tid/16 + 32 u, chunk tid % 16
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        kst[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, ko + u * 64 * kv_st, 0, 0));
       __syncthreads();  // every wave is done with the previous pass's K
-      {
-        // 256 keys x 16 chunks of 16 bytes: thread -> key tid/2 .. in 8 steps
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int idx = tid + u * KV_THREADS;        // 0 .. 4095
-          const int key = idx >> 4, ch = idx & 15;
-          const int kc = min(kb + key, n_ctx - 1);
-          *reinterpret_cast<uint4*>(sK + key * LDS_ROW + ch * 8) =
-              *reinterpret_cast<const uint4*>(Kseq + (int64_t)kc * a.kv_st + ch * 8);
-        }
-      }
+      for (int u = 0; u < 8; ++u)
+        *reinterpret_cast<uint4*>(sK + ((tid >> 4) + 32 * u) * LDS_ROW + (tid & 15) * 8) = kst[u];
       f32x16 dk_acc[4], dv_acc[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) dk_acc[i] = dv_acc[i] = f32x16{};
       const bool wave_live = kw0 < kend;        // the wave owns at least one key of the item
 
       if (ntq > 0) {
-        QTileRegs R = load_q(0);
         __syncthreads();  // previous users of the query buffers are done
         store_q(R, 0);
         __builtin_amdgcn_s_waitcnt(0);
