@@ -60,8 +60,11 @@ extern "C" int skv_check_problem(const skv_problem* p) {
   if (!p->h_anchor && p->h_q_off[p->n_seq] > 0) return fail(SKV_EINVAL, "host anchor array is NULL");
   // Vector loads move 16 bytes: strides must keep every head row 16-byte aligned.
   const int64_t vec = p->dtype == SKV_BF16 ? 8 : 4;
-  if (p->q_stride_head < p->d || p->kv_stride_head < p->d || p->q_stride_tok < 1 || p->kv_stride_tok < 1)
-    return fail(SKV_ESHAPE, "strides must be positive and head strides >= d");
+  // Token and head strides of at least d keep every (token, head) row of d
+  // elements apart from the others, which the kernels' buffer ranges (one
+  // sequence's rows from its first key) rely on.
+  if (p->q_stride_head < p->d || p->kv_stride_head < p->d || p->q_stride_tok < p->d || p->kv_stride_tok < p->d)
+    return fail(SKV_ESHAPE, "token and head strides must be >= d");
   if (p->q_stride_tok % vec || p->q_stride_head % vec || p->kv_stride_tok % vec || p->kv_stride_head % vec)
     return fail(SKV_ESHAPE, "strides must be multiples of %lld elements (16 bytes)", (long long)vec);
   // Query rows start at row 0: the kernels that walk every row of the batch

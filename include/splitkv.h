@@ -47,8 +47,10 @@
  *    K, V, dK, dV:   [sum_s N_s, hkv, d]   element (j, g, x) at
  *                    j*kv_stride_tok + g*kv_stride_head + x
  *    LSE:            float [sum_s Mq_s, hq], row-major (t*hq + h).
- *    For bf16, one sequence's K/V rows must span at most 2^31 bytes
- *    (N_s * kv_stride_tok * 2); larger sequences are rejected (SKV_ESHAPE).
+ *    Token and head strides are at least d (rows do not overlap) and
+ *    multiples of 16 bytes.  For bf16, one sequence's K/V rows must span at
+ *    most 2^31 bytes (N_s * kv_stride_tok * 2); larger sequences are
+ *    rejected (SKV_ESHAPE).
  *  - Query head h uses KV head h / (hq / hkv).
  *  - Logits are sm_scale * q.k; LSE is in natural-log units.
  */

@@ -152,7 +152,8 @@ def test_problem_validation_codes():
     cases = [({"hq": 3, "hkv": 2}, B.SKV_ESHAPE), ({"chunk": 100}, B.SKV_ESHAPE), ({"chunk": 0}, B.SKV_ESHAPE),
              ({"d": 96}, B.SKV_ESHAPE), ({"dtype": 7}, B.SKV_EDTYPE), ({"block": 0}, B.SKV_EINVAL),
              ({"sm_scale": float("nan")}, B.SKV_EINVAL), ({"h_anchor": None}, B.SKV_EINVAL),
-             ({"q_stride_tok": 3}, B.SKV_ESHAPE), ({"n_seq": -1}, B.SKV_EINVAL)]
+             ({"q_stride_tok": 3}, B.SKV_ESHAPE), ({"n_seq": -1}, B.SKV_EINVAL),
+             ({"q_stride_tok": 32}, B.SKV_ESHAPE), ({"kv_stride_tok": 32}, B.SKV_ESHAPE)]
     for kw, code in cases:
         p = _bad(w, **kw)
         assert B.lib.skv_check_problem(C.byref(p.c)) == code, kw
