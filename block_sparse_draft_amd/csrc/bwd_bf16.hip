@@ -241,12 +241,11 @@ void bwd_kv_kernel(BwdArgs a) {
       const int ntq = (nq + QT - 1) / QT;
 
       // Query tile loader: rows qt*32 + row of the visible suffix, contiguous
-      // in the packed copies; padding rows read the last row and are masked.
+      // in the packed copies, through buffer descriptors based at the tile's
+      // first packed row (scalar work) with fixed 32-bit per-lane offsets.
+      // Rows past the suffix (padding of the last tile) read as zeros, and
+      // their LSE is set to +inf below, so they are masked.
       const int64_t vis0 = pbase + (int64_t)b_first * GB;  // packed index of the suffix's first row
-      // Query tile loads through buffer descriptors based at the tile's first
-      // packed row (scalar work), with fixed 32-bit per-lane offsets; rows
-      // past the suffix (padding of the last tile) read as zeros, and their
-      // LSE is set to +inf below, so they are masked.
       const int tq = wave * 64 + fresh_lane_id();
       const int qo = (tq >> 4) * (D * 2) + (tq & 15) * 16, mo = (tq & (QT - 1)) * 4;
       auto load_q = [&](int qt) {
@@ -278,8 +277,7 @@ void bwd_kv_kernel(BwdArgs a) {
         }
       };
 
-      // This wave's 32 keys as MFMA B operands (k = head dim); keys past the
-      // context are clamped to its last key and masked.
+      // This wave's 32 keys as MFMA B operands (k = head dim).
       const int kw0 = kb + wave * 32;           // first key of this wave
       const int key_w = kw0 + l32;
       // The first query tile's loads go out first: its addresses need only
