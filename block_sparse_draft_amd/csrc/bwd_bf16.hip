@@ -624,11 +624,14 @@ void bwd_dq_kernel(BwdArgs a) {
 
       for (int t = 0; t < ntiles; ++t) {
         const int kb = klo + t * KT2;
+        __syncthreads();  // tile t, stored during tile t-1, is visible
+        // Tile t+1 goes into the buffer tile t-2 used (free since the
+        // previous barrier), after this barrier, so that the barrier does not
+        // wait for these stores; the next one finds them complete.
         if (t + 1 < ntiles) {
           store_kv_tile(R, sKV[(t + 1) % DQ_NBUF][0], sKV[(t + 1) % DQ_NBUF][1], tid);
           if (t + 2 < ntiles) R = load_kv_tile(Kseq, Vseq, kb + 2 * KT2, n_ctx, kv_st, ld_off);
         }
-        __syncthreads();
         if (kb >= wave_hi) continue;  // no row of this wave sees the tile (nor any later one)
         // 32-bit LDS addresses of this lane's reads in the tile's buffers; the
         // empty asm keeps every per-read offset an immediate instead of one
