@@ -308,6 +308,8 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--policy", default="lpt", choices=["lpt", "static"])
     ap.add_argument("--bwd-granule", type=int, default=256)
+    ap.add_argument("--fwd-granule", type=int, default=0,
+                    help="draft blocks per forward item (0: the library's default, 256 packed rows)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-replan", action="store_true", help="plan once outside the timed region")
     ap.add_argument("--no-steal", action="store_true", help="workgroups run only their own plan lists")
@@ -362,6 +364,7 @@ def main():
 
     path = SplitKVAttention(w.q_off, w.kv_off, w.anchors, c.block, c.hq, c.hkv, c.d, c.chunk, w.sm_scale, dt, dev,
                             policy=args.policy, bwd_granule=args.bwd_granule, with_bwd=with_bwd,
+                            fwd_granule=args.fwd_granule or None,
                             steal=not args.no_steal, fwd_runs_per_worker=args.runs_per_worker or None,
                             mask=args.mask, ticks=True)
     K = args.steps
