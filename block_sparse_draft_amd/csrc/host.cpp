@@ -248,8 +248,12 @@ extern "C" int lpt_plan(const int64_t* cost, int64_t n, int32_t n_workers, int32
   const int wb = bit_width((uint64_t)(n_workers - 1));
   const size_t H = (size_t)n_workers;
   if (wb < 62 && total < (INT64_C(1) << (62 - wb))) {
-    std::vector<uint64_t> heap(H);
-    for (size_t w = 0; w < H; ++w) heap[w] = (uint64_t)w;  // already a heap
+    // A 4-ary heap (children of k: 4k+1 .. 4k+4): half the levels of a
+    // binary one.  Slots are distinct, so the top is the same either way.
+    // Missing children read as UINT64_MAX (the array is padded to a
+    // multiple of 4 plus one).
+    std::vector<uint64_t> heap(((H + 2) / 4) * 4 + 1 + 4, UINT64_MAX);
+    for (size_t w = 0; w < H; ++w) heap[w] = (uint64_t)w;  // ascending: already a heap
     const uint64_t wmask = (UINT64_C(1) << wb) - 1;
     for (int64_t i : seq) {
       uint64_t top = heap[0];
@@ -257,16 +261,20 @@ extern "C" int lpt_plan(const int64_t* cost, int64_t n, int32_t n_workers, int32
       top += (uint64_t)cost[i] << wb;
       size_t k = 0;
       for (;;) {
-        size_t c = 2 * k + 1;
+        const size_t c = 4 * k + 1;
         if (c >= H) break;
-        uint64_t cv = heap[c];
-        if (c + 1 < H && heap[c + 1] < cv) cv = heap[++c];
-        if (cv >= top) break;
-        heap[k] = cv;
-        k = c;
+        size_t m = c;
+        uint64_t mv = heap[c];
+        if (heap[c + 1] < mv) { mv = heap[c + 1]; m = c + 1; }
+        if (heap[c + 2] < mv) { mv = heap[c + 2]; m = c + 2; }
+        if (heap[c + 3] < mv) { mv = heap[c + 3]; m = c + 3; }
+        if (mv >= top) break;
+        heap[k] = mv;
+        k = m;
       }
       heap[k] = top;
     }
+    heap.resize(H);
     for (uint64_t sl : heap) final_load[sl & wmask] = (int64_t)(sl >> wb);
   } else {
     struct Slot {
@@ -361,40 +369,76 @@ extern "C" int skv_drop_zero_cost(const int64_t* cost, int64_t n, int32_t n_work
 }
 
 // Runs of consecutive chunks of the same rows become one forward item.
-extern "C" int skv_coarsen_fwd_items(const skv_item* items, const int64_t* cost, int64_t n, int64_t target,
-                                     skv_item* items_out, int64_t* cost_out, int64_t* n_out) {
-  if (n < 0 || target < 1) return fail(SKV_EINVAL, "n = %lld, target = %lld", (long long)n, (long long)target);
-  if (n > 0 && (!items || !cost || !items_out || !cost_out)) return fail(SKV_EINVAL, "NULL array");
-  if (!n_out) return fail(SKV_EINVAL, "n_out is NULL");
-  for (int64_t i = 0; i < n; ++i)
-    if (items[i].n_chunk != 1 || cost[i] < 0)
-      return fail(SKV_EINVAL, "item %lld: n_chunk %d, cost %lld (single-chunk items with cost >= 0 expected)",
-                  (long long)i, items[i].n_chunk, (long long)cost[i]);
-  // group order: (seq, kv_head, lo, hi, chunk), ties by input index: stable
-  // radix passes from the last field to the first
+// Checks of a coarsening input: single-chunk items, costs >= 0, no negative field.
+static int check_coarsen_input(const skv_item* items, const int64_t* cost, int64_t n) {
   for (int64_t i = 0; i < n; ++i) {
     const skv_item& t = items[i];
+    if (t.n_chunk != 1 || cost[i] < 0)
+      return fail(SKV_EINVAL, "item %lld: n_chunk %d, cost %lld (single-chunk items with cost >= 0 expected)",
+                  (long long)i, t.n_chunk, (long long)cost[i]);
     if (t.seq < 0 || t.kv_head < 0 || t.lo < 0 || t.hi < 0 || t.chunk < 0)
       return fail(SKV_EINVAL, "item %lld has a negative field", (long long)i);
   }
-  std::vector<int64_t> idx(n);
+  return SKV_OK;
+}
+
+// Item indices in group order (seq, kv_head, lo, hi, chunk), ties by index:
+// one stable LSD radix sort, 8 bits per pass, over a composite key whose
+// fields take the bit widths of their maxima (field by field when the widths
+// add up to more than 64 bits).
+static void group_order(const skv_item* items, int64_t n, std::vector<int64_t>& idx) {
+  idx.resize(n);
   for (int64_t i = 0; i < n; ++i) idx[i] = i;
-  std::vector<uint32_t> field(n);
-  auto by = [&](int32_t skv_item::*f) {
-    uint64_t mx = 0;
-    for (int64_t i = 0; i < n; ++i) {
-      field[i] = (uint32_t)(items[i].*f);
-      mx = std::max<uint64_t>(mx, field[i]);
+  int32_t skv_item::*const fields[5] = {&skv_item::seq, &skv_item::kv_head, &skv_item::lo, &skv_item::hi,
+                                        &skv_item::chunk};
+  int width[5], total = 0;
+  for (int f = 0; f < 5; ++f) {
+    uint32_t mx = 0;
+    for (int64_t i = 0; i < n; ++i) mx = std::max(mx, (uint32_t)(items[i].*fields[f]));
+    width[f] = bit_width(mx);
+    total += width[f];
+  }
+  if (total > 64) {
+    std::vector<uint32_t> field(n);
+    for (int f = 4; f >= 0; --f) {  // last field first
+      uint64_t mx = 0;
+      for (int64_t i = 0; i < n; ++i) {
+        field[i] = (uint32_t)(items[i].*fields[f]);
+        mx = std::max<uint64_t>(mx, field[i]);
+      }
+      radix_sort_by(idx, mx, [&](int64_t i) { return (uint64_t)field[i]; });
     }
-    radix_sort_by(idx, mx, [&](int64_t i) { return (uint64_t)field[i]; });
-  };
-  by(&skv_item::chunk);
-  by(&skv_item::hi);
-  by(&skv_item::lo);
-  by(&skv_item::kv_head);
-  by(&skv_item::seq);
+    return;
+  }
+  std::vector<uint64_t> key(n), key2(n);
+  for (int64_t i = 0; i < n; ++i) {
+    uint64_t kk = 0;
+    for (int f = 0; f < 5; ++f) kk = (kk << width[f]) | (uint64_t)(uint32_t)(items[i].*fields[f]);
+    key[i] = kk;
+  }
+  std::vector<int64_t> idx2(n);
+  for (int shift = 0; shift < total; shift += 8) {
+    int64_t cnt[257] = {0};
+    for (int64_t i = 0; i < n; ++i) ++cnt[((key[i] >> shift) & 255) + 1];
+    for (int d = 0; d < 256; ++d) cnt[d + 1] += cnt[d];
+    for (int64_t i = 0; i < n; ++i) {
+      const int64_t pos = cnt[(key[i] >> shift) & 255]++;
+      key2[pos] = key[i];
+      idx2[pos] = idx[i];
+    }
+    key.swap(key2);
+    idx.swap(idx2);
+  }
+}
+
+// Runs over items in group order `idx`: consecutive chunks of the same rows
+// join a run while its cost is below `target`; a zero-cost item stands alone.
+// Output in order of each run's first item.
+static void build_runs(const skv_item* items, const int64_t* cost, int64_t n, const std::vector<int64_t>& idx,
+                       int64_t target, skv_item* items_out, int64_t* cost_out, int64_t* n_out) {
   struct Run { int64_t first; int32_t len; int64_t cost; };
   std::vector<Run> runs;
+  runs.reserve(n);
   bool open = false;
   for (int64_t j = 0; j < n; ++j) {
     const int64_t i = idx[j];
@@ -426,6 +470,18 @@ extern "C" int skv_coarsen_fwd_items(const skv_item* items, const int64_t* cost,
     ++k;
   }
   *n_out = k;
+}
+
+extern "C" int skv_coarsen_fwd_items(const skv_item* items, const int64_t* cost, int64_t n, int64_t target,
+                                     skv_item* items_out, int64_t* cost_out, int64_t* n_out) {
+  if (n < 0 || target < 1) return fail(SKV_EINVAL, "n = %lld, target = %lld", (long long)n, (long long)target);
+  if (n > 0 && (!items || !cost || !items_out || !cost_out)) return fail(SKV_EINVAL, "NULL array");
+  if (!n_out) return fail(SKV_EINVAL, "n_out is NULL");
+  int rc = check_coarsen_input(items, cost, n);
+  if (rc) return rc;
+  std::vector<int64_t> idx;
+  group_order(items, n, idx);
+  build_runs(items, cost, n, idx, target, items_out, cost_out, n_out);
   return SKV_OK;
 }
 
@@ -445,12 +501,15 @@ extern "C" int skv_plan_fwd_runs(const skv_item* items, const int64_t* cost, int
     if (cost[i] > INT64_MAX - total) return fail(SKV_EINVAL, "total cost overflows");
     total += cost[i];
   }
+  int rc = check_coarsen_input(items, cost, n);
+  if (rc) return rc;
+  std::vector<int64_t> idx;  // group order: the same for every target
+  group_order(items, n, idx);
   double rpw = runs_per_worker;
   for (;;) {
     const double t = std::ceil((double)total / ((double)n_workers * rpw));
     const int64_t target = t < 1.0 ? 1 : (t >= 9.2e18 ? INT64_MAX : (int64_t)t);
-    int rc = skv_coarsen_fwd_items(items, cost, n, target, items_out, cost_out, n_out);
-    if (rc) return rc;
+    build_runs(items, cost, n, idx, target, items_out, cost_out, n_out);
     if ((rc = lpt_plan(cost_out, *n_out, n_workers, nullptr, order, worker_off, load))) return rc;
     int64_t mx = 0;
     for (int32_t w = 0; w < n_workers; ++w) mx = std::max(mx, load[w]);
