@@ -358,6 +358,31 @@ def test_coarsen_fwd_items_any_input_order(seed):
     assert (length > 1).any()
 
 
+@pytest.mark.parametrize("wide", [False, True])
+def test_coarsen_fwd_items_wide_fields(wide):
+    """Grouping keys of every width: the same constant added to a field of
+    every item changes neither the groups nor chunk adjacency, so the runs stay
+    the oracle's.  Wide offsets make the fields need 113 bits together (the
+    grouping sort then goes field by field); narrow ones 31 bits (four
+    passes of the composite-key sort, one more than without the offset)."""
+    w = _meta_only("c3", {})
+    p = _problem_from(w)
+    items, cost, _, _ = p.item_table(B.SKV_ITEM_FWD, 4)
+    desc, ocost, _, _ = _oracle_table(w, "fwd", 4)
+    perm = np.random.default_rng(5).permutation(len(cost))
+    items, cost, desc, ocost = items[perm].copy(), cost[perm], desc[perm], ocost[perm]
+    shift = {"seq": 20, "kv_head": 21, "lo": 22, "hi": 22, "chunk": 23} if wide else {"chunk": 12}
+    for f, b in shift.items():
+        items[f] += np.int32(1 << b)
+    target = int(cost.sum() // 700) + 1
+    it2, c2 = B.skv_coarsen_fwd_items(items, cost, target)
+    first, length, rcost = oracle.coarsen_runs(desc, ocost, target)
+    assert np.array_equal(c2, rcost) and np.array_equal(it2["n_chunk"], length)
+    for f in ("seq", "kv_head", "chunk", "range", "part_base", "lo", "hi"):
+        assert np.array_equal(it2[f], items[first][f]), f
+    assert (length > 1).any()
+
+
 def _oracle_run_search(desc, cost, n_workers, start, stop, tol):
     """The run-length search restated on the oracle: double the runs per worker
     until LPT over the oracle's runs balances them to within tol."""
