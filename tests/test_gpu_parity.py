@@ -257,10 +257,12 @@ def test_bf16_backward_edge_anchors():
     assert np.abs(dk[:716]).max() > 0
 
 
-@pytest.mark.parametrize("cfg,kv_heads,seqs", [("c3", [3], [1]), ("c3", [6], [2]), ("c4", [2], None), ("c5", [9], None)])
+@pytest.mark.parametrize("cfg,kv_heads,seqs", [("c3", [3], [1]), ("c3", [6], [2]), ("c3", [0], [0]), ("c3", [7], [3]),
+                                               ("c4", [2], None), ("c5", [9], None)])
 def test_full_size_fwd_bwd_sampled(cfg, kv_heads, seqs):
     """Full configuration on the GPU, compared with the oracle on one KV head
-    (and one sequence for the 4-sequence config)."""
+    (and one sequence for the 4-sequence config: every c3 sequence is sampled
+    once, each on another KV head)."""
     w = make(cfg, seed=0)
     path = make_path(w, DEV, fwd_runs_per_worker=4)  # the driver's default plan (chunk runs)
     q, k, v = _upload(w)
